@@ -1,0 +1,388 @@
+"""Pins for the CPU oracle: closed forms, brute force, invariants, worked examples.
+
+Each test pins the oracle to something other than itself: the pages' 2x2
+Givens matrix, a dense-matrix construction of T taken literally from the
+notes' formula, a signed Walsh-Hadamard closed form, exact-arithmetic round
+trips of the quantizer, and hand-worked examples under tests/golden/.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from oracle import metrics
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def dense_stage(d, pairs_t, theta_t):
+    """Dense d x d matrix of one stage, from the 2x2 matrix [[c, -s], [s, c]]
+    acting on (v_i, v_j) (CSDN article, section 2.2)."""
+    R = np.eye(d)
+    for (i, j), th in zip(pairs_t, theta_t.astype(np.float64)):
+        c, s = np.cos(th), np.sin(th)
+        R[i, i], R[i, j], R[j, i], R[j, j] = c, -s, s, c
+    return R
+
+
+def dense_T(pairs, theta, alpha):
+    """T = R_K ... R_1 diag(alpha), stage 0 applied first (the notes' final transform)."""
+    d = alpha.shape[0]
+    T = np.diag(alpha.astype(np.float64))
+    for t in range(pairs.shape[0]):
+        T = dense_stage(d, pairs[t], theta[t]) @ T
+    return T
+
+
+def small_case(seed, M=5, d=32, G=8, K=3, N=6):
+    rng = synthetic.rng_for(99, seed)
+    x = synthetic.draw_x(rng, M, d, 2, 20.0)
+    w = synthetic.draw_w(rng, N, d, 0.02)
+    pairs, theta, alpha = synthetic.draw_rotation(rng, d, G, K)
+    return x, w, pairs, theta, alpha
+
+
+# ----------------------------------------------------------------------------
+# P1-P7: the rotation
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_p4_bruteforce_dense_T(seed):
+    """Structured oracle == dense T built literally from the pages' definition."""
+    x, w, pairs, theta, alpha = small_case(seed)
+    T = dense_T(pairs, theta, alpha)
+    # weight side: T * W_math, W_math = w^T; our layout returns (T W_math)^T
+    tw = oracle.transform_weights_f64(w, pairs, theta, alpha)
+    np.testing.assert_allclose(tw, (T @ w.astype(np.float64).T).T, rtol=0, atol=1e-13)
+    # activation side: X T^-1 by a linear solve of the dense matrix
+    xr = oracle.rotate_activations(x, pairs, theta, alpha)
+    ref = np.linalg.solve(T.T, x.astype(np.float64).T).T
+    np.testing.assert_allclose(xr, ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+    # with alpha = 1, T is orthogonal
+    T1 = dense_T(pairs, theta, np.ones_like(alpha))
+    np.testing.assert_allclose(T1.T @ T1, np.eye(T1.shape[0]), atol=1e-13)
+
+
+def test_p1_norm_preserved_per_group():
+    x, w, pairs, theta, alpha = small_case(7, M=9, d=64, G=16, K=8)
+    ones = np.ones_like(alpha)
+    xr = oracle.rotate_activations(x, pairs, theta, ones)
+    x64 = x.astype(np.float64)
+    n0 = np.linalg.norm(x64.reshape(9, 4, 16), axis=2)
+    n1 = np.linalg.norm(xr.reshape(9, 4, 16), axis=2)
+    np.testing.assert_allclose(n1, n0, rtol=1e-14 * 8)
+    # and each stage alone is orthogonal
+    for t in range(8):
+        R = dense_stage(64, pairs[t], theta[t])
+        np.testing.assert_allclose(R.T @ R, np.eye(64), atol=1e-15)
+
+
+def test_p2_inverse_returns_input():
+    """Applying stages K-1..0 with -theta and then multiplying by alpha undoes X T^-1."""
+    x, w, pairs, theta, alpha = small_case(3, K=8)
+    xr = oracle.rotate_activations(x, pairs, theta, alpha)
+    back = oracle.rotate_activations(xr, pairs[::-1].copy(), -theta[::-1].copy(),
+                                     np.ones_like(alpha)) * alpha.astype(np.float64)
+    np.testing.assert_allclose(back, x.astype(np.float64), rtol=0,
+                               atol=1e-13 * np.abs(x.astype(np.float64)).max())
+
+
+def test_p3_invariance_xw():
+    """(X T^-1)(T W) = X W before quantization (CSDN article, section 2.1)."""
+    x, w, pairs, theta, alpha = small_case(4, M=7, d=64, G=16, K=8, N=10)
+    lhs = oracle.rotate_activations(x, pairs, theta, alpha) @ \
+        oracle.transform_weights_f64(w, pairs, theta, alpha).T
+    rhs = x.astype(np.float64) @ w.astype(np.float64).T
+    np.testing.assert_allclose(lhs, rhs, rtol=0, atol=1e-12 * np.abs(rhs).max())
+
+
+def test_p5_walsh_hadamard_closed_form():
+    """G = 2^k, stage t pairs (a, a + 2^t), theta = pi/4: T = signed Walsh-Hadamard / sqrt(G)."""
+    k = 5
+    G = 1 << k
+    d = 2 * G  # two groups: the second gets the same structure shifted by G
+    pairs = np.zeros((k, d // 2, 2), np.int32)
+    for t in range(k):
+        lo = [a for a in range(G) if not (a >> t) & 1]
+        for g in range(2):
+            for p, a in enumerate(lo):
+                pairs[t, g * (G // 2) + p] = (g * G + a, g * G + a + (1 << t))
+    theta = np.full((k, d // 2), np.float32(np.pi / 4), np.float32)
+    # the fp32 angle is not exactly pi/4: use its own cos/sin in the closed form
+    th = np.float64(np.float32(np.pi / 4))
+    c, s = np.cos(th), np.sin(th)
+    alpha = np.ones(d, np.float32)
+    Tg = np.empty((G, G))
+    for a in range(G):
+        for b in range(G):
+            v = 1.0
+            for t in range(k):
+                ab, bb = (a >> t) & 1, (b >> t) & 1
+                v *= {(0, 0): c, (0, 1): -s, (1, 0): s, (1, 1): c}[(ab, bb)]
+            Tg[a, b] = v
+    # the exact pi/4 case is the popcount sign pattern
+    sign = np.array([[(-1) ** bin(~a & b & (G - 1)).count("1") for b in range(G)] for a in range(G)])
+    np.testing.assert_allclose(Tg, sign / np.sqrt(G), atol=1e-6)
+    eye = np.eye(d, dtype=np.float16)
+    # activation side with X = I: X' = T^-1 = T^T
+    xr = oracle.rotate_activations(eye, pairs, theta, alpha)
+    for g in range(2):
+        blk = xr[g * G:(g + 1) * G, g * G:(g + 1) * G]
+        np.testing.assert_allclose(blk, Tg.T, rtol=0, atol=1e-13)
+    # weight side with W = I: the [N][d] result is (T W_math)^T = T^T
+    tw = oracle.transform_weights_f64(eye, pairs, theta, alpha)
+    np.testing.assert_allclose(tw[:G, :G], Tg.T, rtol=0, atol=1e-13)
+    assert np.all(xr[:G, G:] == 0) and np.all(xr[G:, :G] == 0)
+
+
+def test_hadamard_golden_g4():
+    rows = [list(map(float, ln.split())) for ln in open(os.path.join(GOLDEN, "hadamard_g4.txt"))
+            if ln.strip() and not ln.startswith("#")]
+    T = np.array(rows) / 2.0
+    pairs = np.array([[[0, 1], [2, 3]], [[0, 2], [1, 3]]], np.int32)
+    theta = np.full((2, 2), np.pi / 4, np.float32)
+    alpha = np.ones(4, np.float32)
+    xr = oracle.rotate_activations(np.eye(4, dtype=np.float16), pairs, theta, alpha)
+    np.testing.assert_allclose(xr, T.T, atol=1e-7)
+    tw = oracle.transform_weights_f64(np.eye(4, dtype=np.float16), pairs, theta, alpha)
+    np.testing.assert_allclose(tw, T.T, atol=1e-7)
+    # canonical fp32 path agrees to fp32 precision
+    tw32 = oracle.transform_weights_f32(np.eye(4, dtype=np.float16), pairs, theta, alpha)
+    np.testing.assert_allclose(tw32, T.T, atol=1e-6)
+
+
+def test_p6_sign_convention_quarter_turn():
+    """One pair (i, j) = (1, 3), theta = pi/2: e_i -> e_j and e_j -> -e_i."""
+    d = 4
+    pairs = np.array([[[1, 3], [0, 2]]], np.int32)
+    theta = np.array([[np.pi / 2, 0.0]], np.float32)
+    alpha = np.ones(d, np.float32)
+    xr = oracle.rotate_activations(np.eye(d, dtype=np.float16), pairs, theta, alpha)
+    np.testing.assert_allclose(xr[1], [0, 0, 0, 1], atol=1e-7)
+    np.testing.assert_allclose(xr[3], [0, -1, 0, 0], atol=1e-7)
+    np.testing.assert_allclose(xr[0], [1, 0, 0, 0], atol=0)
+    # swapping the stored order of a pair is the same as negating its angle
+    pairs2 = pairs.copy()
+    pairs2[0, 0] = [3, 1]
+    theta2 = theta.copy()
+    theta2[0, 0] = -theta[0, 0]
+    x = synthetic.draw_x(synthetic.rng_for(99, 50), 3, d, 0)
+    np.testing.assert_allclose(oracle.rotate_activations(x, pairs2, theta2, alpha),
+                               oracle.rotate_activations(x, pairs, theta, alpha), atol=1e-15)
+
+
+def test_p7_k0_is_channel_scaling():
+    x, w, pairs, theta, alpha = small_case(5)
+    p0 = pairs[:0]
+    t0 = theta[:0]
+    np.testing.assert_array_equal(oracle.rotate_activations(x, p0, t0, alpha),
+                                  x.astype(np.float64) / alpha.astype(np.float64))
+    np.testing.assert_array_equal(oracle.transform_weights_f32(w, p0, t0, alpha),
+                                  w.astype(np.float32) * alpha)
+
+
+def test_fp32_transform_matches_scalar_loop_and_f64():
+    """Canonical fp32 transform: vectorised == scalar loop bit for bit; close to fp64."""
+    x, w, pairs, theta, alpha = small_case(6, d=16, G=8, K=4, N=3)
+    got = oracle.transform_weights_f32(w, pairs, theta, alpha)
+    f32 = np.float32
+    ref = np.empty_like(got)
+    for n in range(w.shape[0]):
+        u = [f32(w[n, k]) * f32(alpha[k]) for k in range(16)]
+        for t in range(4):
+            for (i, j), th in zip(pairs[t], theta[t]):
+                c = f32(np.cos(np.float64(th)))
+                s = f32(np.sin(np.float64(th)))
+                a, b = u[i], u[j]
+                u[i] = f32(f32(c * a) - f32(s * b))
+                u[j] = f32(f32(s * a) + f32(c * b))
+        ref[n] = u
+    np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+    f64 = oracle.transform_weights_f64(w, pairs, theta, alpha)
+    np.testing.assert_allclose(got, f64, rtol=0, atol=1e-6 * np.abs(f64).max())
+
+
+def test_param_validation():
+    d, G = 16, 8
+    pairs, theta, alpha = synthetic.draw_rotation(synthetic.rng_for(99, 9), d, G, 2)
+    oracle.check_rotation_params(pairs, theta, alpha, G)
+    bad = pairs.copy()
+    bad[0, 0, 1] = bad[0, 1, 0]  # duplicate channel
+    with pytest.raises(ValueError):
+        oracle.check_rotation_params(bad, theta, alpha, G)
+    cross = pairs.copy()
+    # swap one member between the two groups -> crosses a group
+    a = cross[1, 0, 0]
+    b = cross[1, G // 2, 0]
+    cross[1, 0, 0], cross[1, G // 2, 0] = b, a
+    with pytest.raises(ValueError):
+        oracle.check_rotation_params(cross, theta, alpha, G)
+    with pytest.raises(ValueError):
+        oracle.check_rotation_params(pairs, theta, -alpha, G)
+
+
+# ----------------------------------------------------------------------------
+# R1-R6: the quantizer
+# ----------------------------------------------------------------------------
+
+def read_quant_golden():
+    cases = []
+    for ln in open(os.path.join(GOLDEN, "quantize_worked.txt")):
+        if not ln.strip() or ln.startswith("#"):
+            continue
+        u, sz, q, packed = [p.split() for p in ln.split("|")]
+        cases.append((np.array(u, np.float32), int(sz[0], 16), int(sz[1]),
+                      np.array(q, np.uint8), bytes(int(b, 16) for b in packed)))
+    return cases
+
+
+def test_quantize_worked_examples():
+    cases = read_quant_golden()
+    assert len(cases) == 6
+    for u, s_bits, z, q, packed in cases:
+        codes, s16, zeros = oracle.quantize_groups(u[None, :], 4)
+        assert int(s16.view(np.uint16)[0, 0]) == s_bits
+        assert int(zeros[0, 0]) == z
+        np.testing.assert_array_equal(codes[0], q)
+        assert oracle.pack_codes(codes)[0].tobytes() == packed
+    # all six as one row of six groups
+    row = np.concatenate([c[0] for c in cases])[None, :]
+    codes, s16, zeros = oracle.quantize_groups(row, 4)
+    assert oracle.pack_codes(codes)[0].tobytes() == b"".join(c[4] for c in cases)
+
+
+def test_r1_r2_r3_on_random_groups():
+    rng = synthetic.rng_for(99, 11)
+    w = synthetic.draw_w(rng, 64, 512, 0.02, n_outlier_cols=5, factor=10.0)
+    pairs, theta, alpha = synthetic.draw_rotation(rng, 512, 128, 8)
+    u = oracle.transform_weights_f32(w, pairs, theta, alpha)
+    codes, s16, z = oracle.quantize_groups(u, 128)
+    sq = s16.astype(np.float64)
+    assert codes.max() <= 15 and z.max() <= 15
+    ug = u.reshape(64, 4, 128).astype(np.float64)
+    qg = codes.reshape(64, 4, 128).astype(np.float64)
+    # R1: the minimum maps to code 0 when negative; otherwise the maximum is 15
+    neg = ug.min(axis=2) < 0
+    assert np.all(np.where(neg, qg.min(axis=2) == 0, qg.max(axis=2) == 15))
+    # R2: reconstruction error <= (0.5 + 15 * 2^-11) * s
+    rec = (qg - z[:, :, None]) * sq[:, :, None]
+    bound = (0.5 + 15 * 2.0 ** -11) * sq[:, :, None] * (1 + 1e-6)
+    assert np.all(np.abs(ug - rec) <= bound)
+    # R3: each code is the nearest of the 16 grid points (up to the fp32 quotient's rounding)
+    grid = (np.arange(16)[None, None, None, :] - z[:, :, None, None]) * sq[:, :, None, None]
+    dist = np.abs(ug[..., None] - grid)
+    mine = np.take_along_axis(dist, qg.astype(np.int64)[..., None], axis=3)[..., 0]
+    assert np.all(mine <= dist.min(axis=3) + np.abs(ug) * 2.0 ** -22 + 1e-30)
+
+
+def test_r4_grid_aligned_round_trip():
+    rng = synthetic.rng_for(99, 12)
+    N, d, G = 40, 256, 128
+    s16 = np.abs(rng.standard_normal((N, d // G)) * 0.01).astype(np.float16)
+    s16 = np.where(s16 < np.float16(1e-3), np.float16(1e-3), s16).astype(np.float16)
+    z = rng.integers(0, 16, size=(N, d // G)).astype(np.uint8)
+    q = rng.integers(0, 16, size=(N, d // G, G)).astype(np.uint8)
+    q[:, :, 0] = 0
+    q[:, :, 1] = 15
+    u = ((q.astype(np.float32) - z[:, :, None].astype(np.float32)) *
+         s16[:, :, None].astype(np.float32)).reshape(N, d)
+    codes, s_out, z_out = oracle.quantize_groups(u, G)
+    np.testing.assert_array_equal(s_out.view(np.uint16), s16.view(np.uint16))
+    np.testing.assert_array_equal(z_out, z)
+    np.testing.assert_array_equal(codes, q.reshape(N, d))
+
+
+def test_r5_packing_and_one_hot_linear():
+    rng = synthetic.rng_for(99, 13)
+    codes = rng.integers(0, 16, size=(7, 32)).astype(np.uint8)
+    packed = oracle.pack_codes(codes)
+    np.testing.assert_array_equal(oracle.unpack_codes(packed), codes)
+    # nibble order: channel 0 -> low nibble
+    assert oracle.pack_codes(np.array([[1, 2]], np.uint8))[0, 0] == 0x21
+    # one-hot activations read out single dequantized weights plus the bias
+    scales = (rng.random((7, 2)) * 0.1 + 0.01).astype(np.float16)
+    zeros = rng.integers(0, 16, size=(7, 2)).astype(np.uint8)
+    bias = rng.standard_normal(7).astype(np.float16)
+    y = oracle.linear(np.eye(32), packed, scales, zeros, 16, bias)
+    for k in range(32):
+        for n in range(7):
+            g = k // 16
+            want = (int(codes[n, k]) - int(zeros[n, g])) * float(scales[n, g]) + float(bias[n])
+            assert y[k, n] == want
+
+
+def test_r6_zero_angles_equal_k0_codes():
+    rng = synthetic.rng_for(99, 14)
+    w = synthetic.draw_w(rng, 16, 256, 0.02)
+    pairs, theta, alpha = synthetic.draw_rotation(rng, 256, 128, 8)
+    zero = np.zeros_like(theta)
+    a = oracle.quantize_weights(w, 128, pairs, zero, alpha)
+    b = oracle.quantize_weights(w, 128, pairs[:0], theta[:0], alpha)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x.view(np.uint8), y.view(np.uint8))
+    c, s = oracle.cos_sin_f32(zero)
+    assert np.all(c == 1) and np.all(s == 0)
+
+
+def test_quantizer_degenerate_and_overflow():
+    codes, s16, z = oracle.quantize_groups(np.zeros((2, 8), np.float32), 4)
+    assert np.all(codes == 0) and np.all(z == 0) and np.all(s16 == 1.0)
+    with pytest.raises(oracle.QuantizeError):
+        oracle.quantize_groups(np.array([[1e6, -1e6, 0, 0]], np.float32), 4)
+    with pytest.raises(oracle.QuantizeError):
+        oracle.quantize_groups(np.array([[np.inf, 0, 0, 0]], np.float32), 4)
+
+
+# ----------------------------------------------------------------------------
+# L1-L2: the linear
+# ----------------------------------------------------------------------------
+
+def test_l1_linear_against_python_loops():
+    rng = synthetic.rng_for(99, 15)
+    M, N, d, G = 3, 5, 32, 16
+    x = rng.standard_normal((M, d))
+    codes = rng.integers(0, 16, size=(N, d)).astype(np.uint8)
+    qweight = oracle.pack_codes(codes)
+    scales = (rng.random((N, 2)) * 0.1 + 0.01).astype(np.float16)
+    zeros = rng.integers(0, 16, size=(N, 2)).astype(np.uint8)
+    bias = rng.standard_normal(N).astype(np.float16)
+    y = oracle.linear(x, qweight, scales, zeros, G, bias)
+    for m in range(M):
+        for n in range(N):
+            acc = 0.0
+            for k in range(d):
+                acc += x[m, k] * (int(codes[n, k]) - int(zeros[n, k // G])) * float(scales[n, k // G])
+            assert abs(y[m, n] - (acc + float(bias[n]))) <= 1e-12 * (1 + abs(acc))
+
+
+def test_l2_codes_equal_zero_give_bias():
+    N, d, G = 4, 256, 128
+    zeros = np.arange(N * 2, dtype=np.uint8).reshape(N, 2) % 16
+    codes = np.repeat(zeros, G, axis=1)
+    qweight = oracle.pack_codes(codes)
+    scales = np.full((N, 2), 0.37, np.float16)
+    bias = np.array([1.5, -2.0, 0.25, 3.0], np.float16)
+    x = synthetic.draw_x(synthetic.rng_for(99, 16), 3, d, 2)
+    y = oracle.linear(x.astype(np.float64), qweight, scales, zeros, G, bias)
+    np.testing.assert_array_equal(y, np.broadcast_to(bias.astype(np.float64), (3, N)))
+
+
+def test_tiny_end_to_end_is_close_to_unquantized():
+    """Sanity: the quantized rotated layer approximates X W^T (not a pin)."""
+    x, layer = synthetic.tiny()
+    qw, s, z = oracle.quantize_weights(layer.w, 128, layer.pairs, layer.theta, layer.alpha)
+    y = oracle.rotated_w4_linear(x, qw, s, z, 128, layer.pairs, layer.theta, layer.alpha)
+    ref = x.astype(np.float64) @ layer.w.astype(np.float64).T
+    fro, _ = metrics.linear_error(y, ref)
+    # random (untrained) angles spread the x10 outlier columns over whole groups,
+    # so int4 error is large; this only guards against gross breakage
+    assert fro < 0.5
+
+
+def test_metrics_floor():
+    ref = np.array([[1.0, 1e-9, -2.0, 0.5]])
+    got = ref + np.array([[1e-4, 1e-6, 0, 0]])
+    fl, raw, n = metrics.rotated_error(got, ref, 4)
+    assert raw > 1 and fl < 2e-3
