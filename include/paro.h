@@ -1,0 +1,207 @@
+/*
+ * paro.h - C ABI of the MI355X (gfx950) rotated W4G128 linear library.
+ *
+ * The library implements the inference hot path of ParoQuant (pairwise
+ * rotation quantization, arXiv 2511.10645):
+ *
+ *   Y = X W + b = (X T^-1)(T W) + b                     (CSDN article, section 2.1)
+ *   T = (prod_{t=1..K} R(P_t, Theta_t)) diag(alpha)     (paper notes, "关键设计")
+ *
+ * R(P_t, Theta_t) is one stage of independent Givens rotations: every channel
+ * of a quantization group belongs to exactly one pair (i, j) of the stage, and
+ * the pair is rotated by its own angle theta with the 2x2 matrix
+ * [[cos, -sin], [sin, cos]] acting on (v_i, v_j) (CSDN article, section 2.2):
+ *
+ *   v_i <- cos(theta) v_i - sin(theta) v_j,   v_j <- sin(theta) v_i + cos(theta) v_j
+ *
+ * Conventions fixed by this library (the pages leave them open):
+ *   - stage 0 of the arrays is applied first;
+ *   - activations are divided by alpha and then go through the SAME stages in
+ *     the SAME order with the SAME update (this equals x T^-1 for a row x);
+ *     weights are multiplied by alpha and then go through the stages;
+ *   - W4G128 quantization (paper notes, "主实验"; per-group s and z:
+ *     "损失函数 / 训练策略") is asymmetric min/max round-to-nearest-even over
+ *     15 steps with the range widened to include 0, an fp16 scale and an
+ *     integer zero in [0, 15].
+ *
+ * Types: fp16 tensors are passed as uint16_t* (IEEE binary16 bit patterns).
+ * Every tensor is row-major and contiguous. Device pointers are HIP device
+ * memory (for example torch.Tensor.data_ptr() of a ROCm tensor); host
+ * pointers are ordinary memory. The caller owns every tensor; a rotation
+ * handle owns only the device tables it allocates in paro_rotation_create and
+ * frees in paro_rotation_destroy.
+ *
+ * Errors: every int-returning function returns PARO_OK (0) or a negative
+ * paro_status and never throws or aborts. Argument checks run on the host
+ * before anything is enqueued, so a failed check enqueues nothing. A failed
+ * kernel launch returns PARO_ERR_HIP. Asynchronous device faults surface at
+ * the caller's next synchronisation, as with any HIP library.
+ * paro_last_error() returns a thread-local message for the last failure.
+ *
+ * Threads and streams: hot calls (paro_rotate, paro_w4_linear) allocate
+ * nothing, do not synchronise and keep no mutable global state; a handle may
+ * be used from several threads and streams at once.
+ */
+#ifndef PARO_H
+#define PARO_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PARO_OK = 0,
+  PARO_ERR_NULL = -1,        /* a required pointer is NULL */
+  PARO_ERR_SHAPE = -2,       /* sizes inconsistent (d % group, N % 16, negative sizes, ...) */
+  PARO_ERR_PAIRING = -3,     /* a stage is not a perfect pairing inside every group */
+  PARO_ERR_VALUE = -4,       /* alpha <= 0 or non-finite, theta non-finite, non-finite weights */
+  PARO_ERR_ALIGN = -5,       /* a tensor pointer is not 16-byte aligned */
+  PARO_ERR_UNSUPPORTED = -6, /* a valid request this build does not implement */
+  PARO_ERR_WORKSPACE = -7,   /* workspace missing or too small */
+  PARO_ERR_HIP = -8          /* a HIP runtime call failed */
+} paro_status;
+
+/* Static string naming a status code. Never NULL. */
+const char* paro_status_string(int status);
+
+/* Thread-local detail message of the last failing call on this thread ("" if none). */
+const char* paro_last_error(void);
+
+/* Opaque rotation plan: the K stages of pairs/angles plus alpha for one layer,
+ * validated and turned into device tables. Immutable after creation. */
+typedef struct paro_rotation paro_rotation;
+
+/*
+ * Create a rotation plan on the current HIP device (synchronous).
+ *
+ *   d      number of input channels; d % group == 0; d % 128 == 0.
+ *   group  rotation group size: 64, 128 or 256 (pairs never leave a group,
+ *          paper notes "关键设计").
+ *   K      number of stages, 0 <= K <= 32 (the pages' default is 8).
+ *   pairs  host int32 [K][d/2][2], global channel ids. In every stage each
+ *          channel appears exactly once and i / group == j / group. The
+ *          order of pairs inside a stage is free; the order (i, j) inside a
+ *          pair selects the sign as in the update above (swapping i and j is
+ *          the same as negating theta). Partial pairings are expressed with
+ *          theta = 0, which is an exact identity.
+ *   theta  host float [K][d/2], radians, finite. The library evaluates
+ *          c = (float)cos((double)theta), s = (float)sin((double)theta) on the
+ *          host.
+ *   alpha  host float [d], finite and > 0.
+ *   out    receives the handle.
+ *
+ * Errors: PARO_ERR_NULL, PARO_ERR_SHAPE, PARO_ERR_PAIRING, PARO_ERR_VALUE,
+ * PARO_ERR_UNSUPPORTED (group not in {64,128,256}, K > 32, d % 128 != 0),
+ * PARO_ERR_HIP (device allocation or copy failed). The host arrays are only
+ * read during the call.
+ */
+int paro_rotation_create(int64_t d, int32_t group, int32_t K, const int32_t* pairs,
+                         const float* theta, const float* alpha, paro_rotation** out);
+
+/* Free the plan's device tables (synchronous). NULL is a no-op. The caller
+ * must make sure no enqueued work still uses the handle. */
+void paro_rotation_destroy(paro_rotation* r);
+
+/* Read back plan properties (host only; any pointer may be NULL). */
+int paro_rotation_info(const paro_rotation* r, int64_t* d, int32_t* group, int32_t* K);
+
+/*
+ * Online activation transform X' = X T^-1, row by row
+ * (paper notes, "关键设计" and "亮点与洞察": one fused launch for all stages).
+ *
+ *   x, y   device fp16 [M][d], 16-byte aligned. y == x (in place) is allowed;
+ *          any other overlap is undefined.
+ *   M      number of token rows, >= 0; M == 0 is a no-op.
+ *   stream HIP stream the kernel is enqueued on (0 = the null stream).
+ *
+ * Arithmetic: fp32 inside, one fp16 round-to-nearest-even per output.
+ * Errors: PARO_ERR_NULL, PARO_ERR_SHAPE (M < 0), PARO_ERR_ALIGN, PARO_ERR_HIP.
+ */
+int paro_rotate(const paro_rotation* r, const uint16_t* x, uint16_t* y, int64_t M,
+                hipStream_t stream);
+
+/*
+ * Offline weight transform and int4 group quantization: Q(T W) (r != NULL)
+ * or Q(W) (r == NULL, plain W4).
+ *
+ *   w        device fp16 [N][d] (the nn.Linear [out][in] layout, i.e. the
+ *            transpose of the math W whose rows are input channels).
+ *   group    quantization group along d: 64, 128 or 256; with r != NULL it
+ *            must equal the plan's group.
+ *   qweight  device uint8 [N][d/2]: byte b of a row = code(2b) | code(2b+1) << 4.
+ *   scales   device fp16 [N][d/group].
+ *   zeros    device uint8 [N][d/group], values 0..15.
+ *
+ * The result is bit-exact with this arithmetic, in fp32 with every operation
+ * rounded on its own (no fused multiply-add):
+ *   u_k = w_k * alpha_k; for each stage and pair: a = u_i, b = u_j,
+ *   u_i = c*a - s*b, u_j = s*a + c*b (c, s as in paro_rotation_create);
+ *   per group: mn = min(0, min u), mx = max(0, max u), s32 = (mx - mn) / 15,
+ *   s16 = fp16(s32) (round to nearest even; 0 becomes 1.0),
+ *   z = clamp(rint(-mn / s16), 0, 15), q = clamp(rint(u / s16) + z, 0, 15).
+ * Synchronises the stream to read a device error flag and returns
+ * PARO_ERR_VALUE if some transformed weight or some scale is not finite
+ * (the outputs are then unspecified). Allocates a 4-byte flag per call.
+ * Errors: also PARO_ERR_NULL, PARO_ERR_SHAPE, PARO_ERR_ALIGN,
+ * PARO_ERR_UNSUPPORTED, PARO_ERR_HIP.
+ */
+int paro_quantize_weights(const paro_rotation* r, const uint16_t* w, int64_t N, int64_t d,
+                          int32_t group, uint8_t* qweight, uint16_t* scales, uint8_t* zeros,
+                          hipStream_t stream);
+
+/* Bytes of device workspace paro_w4_linear needs for this plan and M (0 when
+ * r == NULL). */
+size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t d);
+
+/*
+ * The W4G128 linear layer on rotated activations:
+ *   Y[m][n] = sum_k X'[m][k] * (q[n][k] - z[n][k/128]) * s[n][k/128] + bias[n]
+ * with X' = X T^-1 when r != NULL (rotated inside the call) and X' = X when
+ * r == NULL (plain W4, or activations the caller rotated already).
+ *
+ *   x        device fp16 [M][d]; qweight/scales/zeros as produced by
+ *            paro_quantize_weights with group 128; bias device fp16 [N] or NULL;
+ *   y        device fp16 [M][N] (must not overlap x).
+ *   group    must be 128 (W4G128); other values return PARO_ERR_UNSUPPORTED.
+ *   N % 16 == 0, d % 128 == 0, M >= 0 (M == 0 is a no-op).
+ *   workspace, workspace_bytes: device memory of at least
+ *            paro_w4_linear_workspace_size(r, M, d) bytes, 16-byte aligned
+ *            (may be NULL when that size is 0). Its contents are scratch.
+ *
+ * Arithmetic: fp32 accumulation of exact fp16 products against the fp16
+ * rounding of each dequantized weight (q - z) * s; fp16 output.
+ * Errors: PARO_ERR_NULL, PARO_ERR_SHAPE, PARO_ERR_ALIGN, PARO_ERR_UNSUPPORTED,
+ * PARO_ERR_WORKSPACE, PARO_ERR_HIP.
+ */
+int paro_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qweight,
+                   const uint16_t* scales, const uint8_t* zeros, const uint16_t* bias,
+                   uint16_t* y, int64_t M, int64_t N, int64_t d, int32_t group,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Host-only view of the per-segment rotation schedule that
+ * paro_rotation_create uploads (for testing the plan logic without a GPU).
+ * Fills `out` (host memory of out_bytes) with the exact table image and writes
+ * the image size to *needed (out may be NULL to query the size), and the
+ * layout descriptor to *layout (may be NULL):
+ *   layout[0] = channels per segment (128 or 256),
+ *   layout[1] = pairs per lane (1 or 2),
+ *   layout[2] = 32-bit words per lane per segment,
+ *   layout[3] = 1 if the factored two-FMA stage form is used, 0 for the
+ *               general 2x2 form.
+ * Runs the same validation as paro_rotation_create and returns its errors;
+ * PARO_ERR_WORKSPACE when out is non-NULL and out_bytes is too small.
+ */
+int paro_rotation_plan_host(int64_t d, int32_t group, int32_t K, const int32_t* pairs,
+                            const float* theta, const float* alpha, void* out, size_t out_bytes,
+                            size_t* needed, int32_t layout[4]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PARO_H */

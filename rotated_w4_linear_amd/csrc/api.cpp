@@ -1,0 +1,269 @@
+// C ABI of the rotated W4G128 linear library (declarations and argument
+// contracts in include/paro.h).
+#include <cstring>
+#include <string>
+
+#include "paro_internal.h"
+
+namespace paro {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int hip_fail(hipError_t e, const char* what) {
+  set_error(std::string(what) + ": " + hipGetErrorString(e));
+  return PARO_ERR_HIP;
+}
+
+template <typename T>
+int upload(T** dst, const std::vector<T>& src) {
+  *dst = nullptr;
+  if (src.empty()) return PARO_OK;
+  hipError_t e = hipMalloc((void**)dst, src.size() * sizeof(T));
+  if (e != hipSuccess) {
+    *dst = nullptr;
+    return hip_fail(e, "hipMalloc");
+  }
+  e = hipMemcpy(*dst, src.data(), src.size() * sizeof(T), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy");
+  return PARO_OK;
+}
+
+void free_rotation(paro_rotation* r) {
+  if (!r) return;
+  if (r->d_table) (void)hipFree(r->d_table);
+  if (r->d_wt_pairs) (void)hipFree(r->d_wt_pairs);
+  if (r->d_wt_c) (void)hipFree(r->d_wt_c);
+  if (r->d_wt_s) (void)hipFree(r->d_wt_s);
+  if (r->d_alpha) (void)hipFree(r->d_alpha);
+  delete r;
+}
+
+}  // namespace
+}  // namespace paro
+
+using namespace paro;
+
+extern "C" {
+
+const char* paro_status_string(int status) {
+  switch (status) {
+    case PARO_OK: return "PARO_OK";
+    case PARO_ERR_NULL: return "PARO_ERR_NULL";
+    case PARO_ERR_SHAPE: return "PARO_ERR_SHAPE";
+    case PARO_ERR_PAIRING: return "PARO_ERR_PAIRING";
+    case PARO_ERR_VALUE: return "PARO_ERR_VALUE";
+    case PARO_ERR_ALIGN: return "PARO_ERR_ALIGN";
+    case PARO_ERR_UNSUPPORTED: return "PARO_ERR_UNSUPPORTED";
+    case PARO_ERR_WORKSPACE: return "PARO_ERR_WORKSPACE";
+    case PARO_ERR_HIP: return "PARO_ERR_HIP";
+    default: return "PARO_ERR_UNKNOWN";
+  }
+}
+
+const char* paro_last_error(void) { return g_last_error.c_str(); }
+
+int paro_rotation_plan_host(int64_t d, int32_t group, int32_t K, const int32_t* pairs,
+                            const float* theta, const float* alpha, void* out, size_t out_bytes,
+                            size_t* needed, int32_t layout[4]) {
+  RotPlanHost plan;
+  int st = build_rotation_plan(d, group, K, pairs, theta, alpha, &plan);
+  if (st != PARO_OK) return st;
+  const size_t bytes = plan.table.size() * sizeof(uint32_t);
+  if (needed) *needed = bytes;
+  if (layout) {
+    layout[0] = plan.lay.seg_ch;
+    layout[1] = plan.lay.ppl;
+    layout[2] = plan.lay.words;
+    layout[3] = plan.lay.fast ? 1 : 0;
+  }
+  if (out) {
+    if (out_bytes < bytes) {
+      set_error("output buffer too small for the plan image");
+      return PARO_ERR_WORKSPACE;
+    }
+    std::memcpy(out, plan.table.data(), bytes);
+  }
+  return PARO_OK;
+}
+
+int paro_rotation_create(int64_t d, int32_t group, int32_t K, const int32_t* pairs,
+                         const float* theta, const float* alpha, paro_rotation** out) {
+  if (!out) {
+    set_error("out is NULL");
+    return PARO_ERR_NULL;
+  }
+  *out = nullptr;
+  RotPlanHost plan;
+  int st = build_rotation_plan(d, group, K, pairs, theta, alpha, &plan);
+  if (st != PARO_OK) return st;
+  paro_rotation* r = new paro_rotation();
+  std::memset(r, 0, sizeof(*r));
+  r->d = d;
+  r->group = group;
+  r->K = K;
+  r->lay = plan.lay;
+  hipError_t e = hipGetDevice(&r->device);
+  if (e != hipSuccess) {
+    free_rotation(r);
+    return hip_fail(e, "hipGetDevice");
+  }
+  if ((st = upload(&r->d_table, plan.table)) != PARO_OK ||
+      (st = upload(&r->d_wt_pairs, plan.wt_pairs)) != PARO_OK ||
+      (st = upload(&r->d_wt_c, plan.wt_c)) != PARO_OK ||
+      (st = upload(&r->d_wt_s, plan.wt_s)) != PARO_OK ||
+      (st = upload(&r->d_alpha, plan.alpha)) != PARO_OK) {
+    free_rotation(r);
+    return st;
+  }
+  *out = r;
+  return PARO_OK;
+}
+
+void paro_rotation_destroy(paro_rotation* r) { free_rotation(r); }
+
+int paro_rotation_info(const paro_rotation* r, int64_t* d, int32_t* group, int32_t* K) {
+  if (!r) {
+    set_error("rotation handle is NULL");
+    return PARO_ERR_NULL;
+  }
+  if (d) *d = r->d;
+  if (group) *group = r->group;
+  if (K) *K = r->K;
+  return PARO_OK;
+}
+
+int paro_rotate(const paro_rotation* r, const uint16_t* x, uint16_t* y, int64_t M,
+                hipStream_t stream) {
+  if (!r) {
+    set_error("paro_rotate: NULL handle");
+    return PARO_ERR_NULL;
+  }
+  if (M < 0) {
+    set_error("paro_rotate: M < 0");
+    return PARO_ERR_SHAPE;
+  }
+  if (M == 0) return PARO_OK;
+  if (!x || !y) {
+    set_error("paro_rotate: NULL tensor");
+    return PARO_ERR_NULL;
+  }
+  if (!aligned16(x) || !aligned16(y)) {
+    set_error("paro_rotate: x and y must be 16-byte aligned");
+    return PARO_ERR_ALIGN;
+  }
+  hipError_t e = launch_rotate(r, x, y, M, stream);
+  if (e != hipSuccess) return hip_fail(e, "paro_rotate launch");
+  return PARO_OK;
+}
+
+int paro_quantize_weights(const paro_rotation* r, const uint16_t* w, int64_t N, int64_t d,
+                          int32_t group, uint8_t* qweight, uint16_t* scales, uint8_t* zeros,
+                          hipStream_t stream) {
+  if (!w || !qweight || !scales || !zeros) {
+    set_error("paro_quantize_weights: NULL tensor");
+    return PARO_ERR_NULL;
+  }
+  if (N < 0 || d <= 0 || group <= 0) {
+    set_error("paro_quantize_weights: bad sizes");
+    return PARO_ERR_SHAPE;
+  }
+  if (group != 64 && group != 128 && group != 256) {
+    set_error("paro_quantize_weights: group must be 64, 128 or 256");
+    return PARO_ERR_UNSUPPORTED;
+  }
+  if (d % group) {
+    set_error("paro_quantize_weights: d must be a multiple of group");
+    return PARO_ERR_SHAPE;
+  }
+  if (r && (r->d != d || r->group != group)) {
+    set_error("paro_quantize_weights: d/group differ from the rotation plan");
+    return PARO_ERR_SHAPE;
+  }
+  if (!aligned16(w)) {
+    set_error("paro_quantize_weights: w must be 16-byte aligned");
+    return PARO_ERR_ALIGN;
+  }
+  if (N == 0) return PARO_OK;
+  int* flag = nullptr;
+  hipError_t e = hipMalloc((void**)&flag, sizeof(int));
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc(flag)");
+  e = hipMemsetAsync(flag, 0, sizeof(int), stream);
+  if (e == hipSuccess) e = launch_quantize(r, w, N, d, group, qweight, scales, zeros, flag, stream);
+  int hflag = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&hflag, flag, sizeof(int), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  (void)hipFree(flag);
+  if (e != hipSuccess) return hip_fail(e, "paro_quantize_weights");
+  if (hflag) {
+    set_error("paro_quantize_weights: non-finite transformed weight or group scale");
+    return PARO_ERR_VALUE;
+  }
+  return PARO_OK;
+}
+
+size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t d) {
+  if (!r || M <= 0 || d <= 0) return 0;
+  size_t bytes = (size_t)M * (size_t)d * 2;
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int paro_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qweight,
+                   const uint16_t* scales, const uint8_t* zeros, const uint16_t* bias,
+                   uint16_t* y, int64_t M, int64_t N, int64_t d, int32_t group,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (M < 0 || N <= 0 || d <= 0) {
+    set_error("paro_w4_linear: bad sizes");
+    return PARO_ERR_SHAPE;
+  }
+  if (group != 128) {
+    set_error("paro_w4_linear: only group 128 (W4G128) is implemented");
+    return PARO_ERR_UNSUPPORTED;
+  }
+  if (N % 16 || d % 128) {
+    set_error("paro_w4_linear: N must be a multiple of 16 and d of 128");
+    return PARO_ERR_SHAPE;
+  }
+  if (N > (int64_t(1) << 30) || d > (int64_t(1) << 30) || M > (int64_t(1) << 31) / 2) {
+    set_error("paro_w4_linear: sizes too large");
+    return PARO_ERR_UNSUPPORTED;
+  }
+  if (r && r->d != d) {
+    set_error("paro_w4_linear: d differs from the rotation plan");
+    return PARO_ERR_SHAPE;
+  }
+  if (M == 0) return PARO_OK;
+  if (!x || !qweight || !scales || !zeros || !y) {
+    set_error("paro_w4_linear: NULL tensor");
+    return PARO_ERR_NULL;
+  }
+  if (!aligned16(x) || !aligned16(qweight) || !aligned16(y) || (bias && ((uintptr_t)bias & 7))) {
+    set_error("paro_w4_linear: x, qweight, y must be 16-byte aligned (bias 8-byte)");
+    return PARO_ERR_ALIGN;
+  }
+  const uint16_t* xin = x;
+  if (r) {
+    const size_t need = paro_w4_linear_workspace_size(r, M, d);
+    if (!workspace || workspace_bytes < need) {
+      set_error("paro_w4_linear: workspace missing or smaller than paro_w4_linear_workspace_size");
+      return PARO_ERR_WORKSPACE;
+    }
+    if (!aligned16(workspace)) {
+      set_error("paro_w4_linear: workspace must be 16-byte aligned");
+      return PARO_ERR_ALIGN;
+    }
+    hipError_t e = launch_rotate(r, x, (uint16_t*)workspace, M, stream);
+    if (e != hipSuccess) return hip_fail(e, "paro_w4_linear rotate launch");
+    xin = (const uint16_t*)workspace;
+  }
+  hipError_t e = launch_w4_linear(xin, qweight, scales, zeros, bias, y, M, N, d, stream);
+  if (e != hipSuccess) return hip_fail(e, "paro_w4_linear launch");
+  return PARO_OK;
+}
+
+}  // extern "C"

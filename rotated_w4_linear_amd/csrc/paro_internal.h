@@ -1,0 +1,94 @@
+// Internal declarations shared by the host library and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/paro.h"
+
+namespace paro {
+
+// ---------------------------------------------------------------------------
+// Rotation schedule for the activation kernel.
+//
+// The d channels are cut into segments of 128 channels (groups of 64 or 128:
+// one or two groups per segment) or 256 channels (group 256). One wavefront
+// processes one segment of a token: "virtual lane" v (0 .. SEG/2-1) holds two
+// channels, in registers X and Y; with 256-channel segments a hardware lane
+// holds two virtual lanes (v = lane and v = lane + 64).
+//
+// Between two consecutive pairings (the natural pairing {2v, 2v+1} before
+// stage 0 and after stage K-1, and the K stages in between) every virtual
+// lane keeps one of its two channels (in X) and fetches the other member of
+// its next pair from the Y register of another virtual lane, through a
+// per-wave LDS tile. The two pairings together form disjoint even cycles, so
+// a "keep one, fetch one" assignment always exists.
+//
+// Table image per segment: NW fields, each field NV words (one per virtual
+// lane), field-major: tab[seg][field][v]. Field order:
+//   0                 load selector (v_perm byte selector putting the kept
+//                     channel of the natural pair in the low half)
+//   1 + 2*tau         LDS byte offset the lane writes its Y to, tau = 0..K
+//   2 + 2*tau         LDS byte offset the lane reads its fetched value from
+//   3 + 2*K + c*t + e stage t coefficient e (c = 2 for the factored form,
+//                     4 for the general 2x2 form)
+//   then              final scale of X, final scale of the fetched value,
+//                     store byte offset of the natural pair, store selector.
+// ---------------------------------------------------------------------------
+struct RotPlanLayout {
+  int seg_ch = 128;      // channels per segment
+  int ppl = 1;           // virtual lanes per hardware lane
+  int nv = 64;           // virtual lanes per segment
+  int coef = 2;          // coefficients per stage (2 factored, 4 general)
+  int words = 0;         // fields per virtual lane
+  bool fast = true;      // factored two-FMA stage form
+};
+
+inline int rot_field_count(int K, int coef) { return 1 + 2 * (K + 1) + coef * K + 4; }
+
+struct RotPlanHost {
+  RotPlanLayout lay;
+  std::vector<uint32_t> table;  // [segs][words][nv]
+  // canonical fp32 tables for the weight transform, per group, stage, pair:
+  // local (i | j << 16), c bits, s bits
+  std::vector<uint32_t> wt_pairs;  // [groups][K][G/2]
+  std::vector<float> wt_c, wt_s;   // [groups][K][G/2]
+  std::vector<float> alpha;        // [d]
+};
+
+// Validates arguments and builds the schedule. Returns a paro_status.
+int build_rotation_plan(int64_t d, int32_t group, int32_t K, const int32_t* pairs,
+                        const float* theta, const float* alpha, RotPlanHost* out);
+
+void set_error(const std::string& msg);
+
+}  // namespace paro
+
+struct paro_rotation {
+  int64_t d;
+  int32_t group;
+  int32_t K;
+  int device;
+  paro::RotPlanLayout lay;
+  uint32_t* d_table;    // device copy of RotPlanHost::table
+  uint32_t* d_wt_pairs; // device canonical weight-transform tables
+  float* d_wt_c;
+  float* d_wt_s;
+  float* d_alpha;
+};
+
+namespace paro {
+// Kernel launchers (defined in the .hip files). Return hipError_t of the launch.
+hipError_t launch_rotate(const paro_rotation* r, const uint16_t* x, uint16_t* y, int64_t M,
+                         hipStream_t stream);
+hipError_t launch_quantize(const paro_rotation* r, const uint16_t* w, int64_t N, int64_t d,
+                           int group, uint8_t* qweight, uint16_t* scales, uint8_t* zeros,
+                           int* d_flag, hipStream_t stream);
+hipError_t launch_w4_linear(const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
+                            const uint8_t* zeros, const uint16_t* bias, uint16_t* y, int64_t M,
+                            int64_t N, int64_t d, hipStream_t stream);
+}  // namespace paro

@@ -1,0 +1,366 @@
+// Host-side validation of the rotation parameters and construction of the
+// per-segment schedule that the gfx950 rotation kernel executes.
+//
+// What is computed follows the ParoQuant paper notes, section "关键设计":
+// K stages of independent Givens rotations on disjoint channel pairs inside
+// each quantization group, preceded by the channel scaling diag(alpha); the
+// 2x2 update is the CSDN article's section 2.2 matrix [[c, -s], [s, c]] on
+// (v_i, v_j). On the activation side the scaling is 1/alpha and the stages run
+// in the same order with the same update (x T^-1 for a row x).
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+
+#include "paro_internal.h"
+
+namespace paro {
+namespace {
+
+constexpr int kMaxK = 32;
+
+uint32_t fbits(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return u;
+}
+
+// v_perm_b32 byte selectors (result byte k <- byte sel[k] of {src0:src1}).
+constexpr uint32_t kSelLoadKeep = 0x03020100u;  // kept channel is the low half
+constexpr uint32_t kSelLoadSwap = 0x01000302u;  // kept channel is the high half
+constexpr uint32_t kSelStoreX = 0x05040100u;    // X (src1) low, fetched (src0) high
+constexpr uint32_t kSelStoreB = 0x01000504u;    // fetched low, X high
+
+// One segment's sequence of pairings: index 0 is the natural pairing before
+// stage 0, 1..K are the stages, K+1 is the natural pairing after the last
+// stage. partner[tt][ch] is the other member of ch's pair; first[tt][ch] is
+// 1 when ch is the pair's first member (the "i" of (i, j)); cs[tt][ch] holds
+// the pair's fp64 cos and sin.
+struct SegPairings {
+  int C = 0;
+  std::vector<std::vector<int>> partner;
+  std::vector<std::vector<uint8_t>> first;
+  std::vector<std::vector<double>> c, s;
+};
+
+// Kuhn augmenting path on a bipartite multigraph given as edge lists.
+bool augment(int u, const std::vector<std::vector<std::pair<int, int>>>& adj,
+             std::vector<int>& match_r, std::vector<int>& match_edge_r, std::vector<char>& seen,
+             const std::vector<char>& edge_used) {
+  for (auto [v, e] : adj[u]) {
+    if (edge_used[e] || seen[v]) continue;
+    seen[v] = 1;
+    if (match_r[v] < 0 || augment(match_r[v], adj, match_r, match_edge_r, seen, edge_used)) {
+      match_r[v] = u;
+      match_edge_r[v] = e;
+      return true;
+    }
+  }
+  return false;
+}
+
+// Colour the virtual lanes with 8 colours so that every block of 8 writers and
+// every block of 8 readers of one LDS instruction hits 8 different 16-byte bank
+// groups. src[v] is the lane whose Y the lane v reads. Returns slot[v].
+std::vector<int> plan_lds_slots(const std::vector<int>& src) {
+  const int nv = (int)src.size();
+  const int nb = nv / 8;
+  std::vector<int> src_inv(nv);
+  for (int v = 0; v < nv; ++v) src_inv[src[v]] = v;
+  // edge u: writer block u/8 -- reader block src_inv[u]/8
+  std::vector<std::vector<std::pair<int, int>>> adj(nb);
+  for (int u = 0; u < nv; ++u) adj[u / 8].push_back({src_inv[u] / 8, u});
+  std::vector<char> used(nv, 0);
+  std::vector<int> colour(nv, -1);
+  for (int col = 0; col < 8; ++col) {
+    std::vector<int> match_r(nb, -1), match_e(nb, -1);
+    for (int u = 0; u < nb; ++u) {
+      std::vector<char> seen(nb, 0);
+      augment(u, adj, match_r, match_e, seen, used);
+    }
+    for (int v = 0; v < nb; ++v) {
+      if (match_e[v] < 0) return {};  // cannot happen for a regular bipartite multigraph
+      used[match_e[v]] = 1;
+      colour[match_e[v]] = col;
+    }
+  }
+  std::vector<int> slot(nv), next(8, 0);
+  for (int u = 0; u < nv; ++u) slot[u] = colour[u] + 8 * next[colour[u]]++;
+  return slot;
+}
+
+struct LaneState {
+  std::vector<std::vector<int>> kept, fetched, src;  // [tau][v]
+};
+
+}  // namespace
+
+int build_rotation_plan(int64_t d, int32_t group, int32_t K, const int32_t* pairs,
+                        const float* theta, const float* alpha, RotPlanHost* out) {
+  if (!out || !alpha || (K > 0 && (!pairs || !theta))) {
+    set_error("null pointer argument");
+    return PARO_ERR_NULL;
+  }
+  if (d <= 0 || group <= 0 || K < 0) {
+    set_error("d, group must be positive and K non-negative");
+    return PARO_ERR_SHAPE;
+  }
+  if (group != 64 && group != 128 && group != 256) {
+    set_error("group must be 64, 128 or 256");
+    return PARO_ERR_UNSUPPORTED;
+  }
+  if (d % group) {
+    set_error("d must be a multiple of group");
+    return PARO_ERR_SHAPE;
+  }
+  if (d % 128) {
+    set_error("d must be a multiple of 128");
+    return PARO_ERR_UNSUPPORTED;
+  }
+  if (K > kMaxK) {
+    set_error("K > 32 is not supported");
+    return PARO_ERR_UNSUPPORTED;
+  }
+  if (d > (int64_t(1) << 30)) {
+    set_error("d too large");
+    return PARO_ERR_UNSUPPORTED;
+  }
+  for (int64_t k = 0; k < d; ++k) {
+    if (!std::isfinite(alpha[k]) || !(alpha[k] > 0.0f)) {
+      set_error("alpha must be finite and > 0 (channel " + std::to_string(k) + ")");
+      return PARO_ERR_VALUE;
+    }
+  }
+  const int64_t half = d / 2;
+  for (int64_t e = 0; e < (int64_t)K * half; ++e) {
+    if (!std::isfinite(theta[e])) {
+      set_error("theta must be finite");
+      return PARO_ERR_VALUE;
+    }
+  }
+  // pairings: a perfect pairing inside every group, per stage
+  {
+    std::vector<int> seen(d);
+    for (int t = 0; t < K; ++t) {
+      std::fill(seen.begin(), seen.end(), 0);
+      for (int64_t p = 0; p < half; ++p) {
+        int64_t i = pairs[(t * half + p) * 2], j = pairs[(t * half + p) * 2 + 1];
+        if (i < 0 || j < 0 || i >= d || j >= d || i == j) {
+          set_error("stage " + std::to_string(t) + ": channel index out of range or i == j");
+          return PARO_ERR_PAIRING;
+        }
+        if (i / group != j / group) {
+          set_error("stage " + std::to_string(t) + ": pair crosses a group boundary");
+          return PARO_ERR_PAIRING;
+        }
+        if (seen[i]++ || seen[j]++) {
+          set_error("stage " + std::to_string(t) + ": channel appears twice");
+          return PARO_ERR_PAIRING;
+        }
+      }
+    }
+  }
+
+  RotPlanHost& P = *out;
+  P.alpha.assign(alpha, alpha + d);
+  const int seg_ch = group == 256 ? 256 : 128;
+  const int nv = seg_ch / 2;
+  const int segs = (int)(d / seg_ch);
+
+  // ---- canonical fp32 tables for the weight transform -------------------------
+  const int64_t groups = d / group;
+  const int gp = group / 2;
+  P.wt_pairs.assign((size_t)groups * K * gp, 0);
+  P.wt_c.assign((size_t)groups * K * gp, 0.f);
+  P.wt_s.assign((size_t)groups * K * gp, 0.f);
+  {
+    std::vector<int> fill(groups);
+    for (int t = 0; t < K; ++t) {
+      std::fill(fill.begin(), fill.end(), 0);
+      for (int64_t p = 0; p < half; ++p) {
+        int64_t i = pairs[(t * half + p) * 2], j = pairs[(t * half + p) * 2 + 1];
+        int64_t g = i / group;
+        size_t at = ((size_t)g * K + t) * gp + fill[g]++;
+        P.wt_pairs[at] = (uint32_t)(i - g * group) | ((uint32_t)(j - g * group) << 16);
+        double th = (double)theta[t * half + p];
+        P.wt_c[at] = (float)std::cos(th);
+        P.wt_s[at] = (float)std::sin(th);
+      }
+    }
+  }
+
+  // ---- activation schedule ------------------------------------------------------
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    const bool fast = attempt == 0;
+    RotPlanLayout lay;
+    lay.seg_ch = seg_ch;
+    lay.ppl = seg_ch / 128;
+    lay.nv = nv;
+    lay.fast = fast;
+    lay.coef = fast ? 2 : 4;
+    lay.words = rot_field_count(K, lay.coef);
+    std::vector<uint32_t> table((size_t)segs * lay.words * nv, 0);
+    bool ok = true;
+
+    for (int sg = 0; sg < segs && ok; ++sg) {
+      const int64_t base = (int64_t)sg * seg_ch;
+      SegPairings S;
+      S.C = seg_ch;
+      S.partner.assign(K + 2, std::vector<int>(seg_ch));
+      S.first.assign(K + 2, std::vector<uint8_t>(seg_ch, 0));
+      S.c.assign(K + 2, std::vector<double>(seg_ch, 1.0));
+      S.s.assign(K + 2, std::vector<double>(seg_ch, 0.0));
+      for (int ch = 0; ch < seg_ch; ++ch) {
+        S.partner[0][ch] = S.partner[K + 1][ch] = ch ^ 1;
+        S.first[0][ch] = S.first[K + 1][ch] = (ch & 1) == 0;
+      }
+      for (int t = 0; t < K; ++t) {
+        for (int64_t p = 0; p < half; ++p) {
+          int64_t i = pairs[(t * half + p) * 2], j = pairs[(t * half + p) * 2 + 1];
+          if (i < base || i >= base + seg_ch) continue;
+          int li = (int)(i - base), lj = (int)(j - base);
+          double th = (double)theta[t * half + p];
+          S.partner[t + 1][li] = lj;
+          S.partner[t + 1][lj] = li;
+          S.first[t + 1][li] = 1;
+          S.first[t + 1][lj] = 0;
+          S.c[t + 1][li] = S.c[t + 1][lj] = std::cos(th);
+          S.s[t + 1][li] = S.s[t + 1][lj] = std::sin(th);
+        }
+      }
+
+      // mu(out <- in) of the pairing tt's 2x2 update, for two members of one pair
+      auto mu = [&](int tt, int out_ch, int in_ch) -> double {
+        bool oi = S.first[tt][out_ch], ii = S.first[tt][in_ch];
+        double c = S.c[tt][out_ch], s = S.s[tt][out_ch];
+        if (oi) return ii ? c : -s;
+        return ii ? s : c;
+      };
+
+      LaneState L;
+      L.kept.assign(K + 1, std::vector<int>(nv));
+      L.fetched.assign(K + 1, std::vector<int>(nv));
+      L.src.assign(K + 1, std::vector<int>(nv));
+      std::vector<int> ch_a(nv), ch_b(nv), lane_of(seg_ch);
+      for (int v = 0; v < nv; ++v) {
+        ch_a[v] = 2 * v;
+        ch_b[v] = 2 * v + 1;
+      }
+
+      for (int tau = 0; tau <= K; ++tau) {
+        for (int v = 0; v < nv; ++v) lane_of[ch_a[v]] = lane_of[ch_b[v]] = v;
+        const std::vector<int>& nxt = S.partner[tau + 1];
+        std::vector<char> done(nv, 0);
+        for (int L0 = 0; L0 < nv; ++L0) {
+          if (done[L0]) continue;
+          struct Rec { int lane, keep, fetch, from; };
+          std::vector<Rec> orient[2];
+          double score[2] = {1.0, 1.0};
+          for (int o = 0; o < 2; ++o) {
+            int lane = L0;
+            int keep = o == 0 ? ch_a[L0] : ch_b[L0];
+            for (int guard = 0; guard <= nv; ++guard) {
+              int fetch = nxt[keep];
+              int from = lane_of[fetch];
+              orient[o].push_back({lane, keep, fetch, from});
+              if (fast && tau >= 1) {
+                // stage tau-1 at `lane` had inputs kept[tau-1] (A) and fetched[tau-1] (B)
+                int a = L.kept[tau - 1][lane];
+                int b = L.fetched[tau - 1][lane];
+                double m = (keep == a) ? std::fabs(mu(tau, a, a)) : std::fabs(mu(tau, b, a));
+                (void)b;
+                score[o] = std::min(score[o], m);
+              }
+              if (from == L0) break;
+              lane = from;
+              keep = (ch_a[from] == fetch) ? ch_b[from] : ch_a[from];
+            }
+          }
+          int o = score[1] > score[0] ? 1 : 0;
+          for (const auto& rc : orient[o]) {
+            L.kept[tau][rc.lane] = rc.keep;
+            L.fetched[tau][rc.lane] = rc.fetch;
+            L.src[tau][rc.lane] = rc.from;
+            done[rc.lane] = 1;
+          }
+        }
+        for (int v = 0; v < nv; ++v) {
+          ch_a[v] = L.kept[tau][v];
+          ch_b[v] = L.fetched[tau][v];
+        }
+      }
+
+      // ---- coefficients with deferred per-channel scales -------------------
+      std::vector<double> lam(seg_ch);
+      for (int ch = 0; ch < seg_ch; ++ch) lam[ch] = 1.0 / (double)alpha[base + ch];
+      uint32_t* T = &table[(size_t)sg * lay.words * nv];
+      auto put = [&](int field, int v, uint32_t w) { T[(size_t)field * nv + v] = w; };
+      const double lo = std::ldexp(1.0, -60), hi = std::ldexp(1.0, 60), tiny = std::ldexp(1.0, -20);
+      auto in_range = [&](double x) { double a = std::fabs(x); return a >= lo && a <= hi; };
+      for (int t = 0; t < K && ok; ++t) {
+        const int tt = t + 1;
+        std::vector<double> new_lam = lam;
+        for (int v = 0; v < nv; ++v) {
+          int a = L.kept[t][v], b = L.fetched[t][v];
+          int p = L.kept[t + 1][v];
+          int q = (p == a) ? b : a;
+          double mpa = mu(tt, p, a), mpb = mu(tt, p, b), mqa = mu(tt, q, a), mqb = mu(tt, q, b);
+          const int f0 = 3 + 2 * K + lay.coef * t;
+          if (fast) {
+            if (std::fabs(mpa) < tiny || std::fabs(mqb) < tiny) { ok = false; break; }
+            double lp = mpa * lam[a], lq = mqb * lam[b];
+            double k1 = mpb * lam[b] / lp, k2 = mqa * lam[a] / lq;
+            if (!in_range(lp) || !in_range(lq) || std::fabs(k1) > hi || std::fabs(k2) > hi) {
+              ok = false;
+              break;
+            }
+            new_lam[p] = lp;
+            new_lam[q] = lq;
+            put(f0 + 0, v, fbits((float)k1));
+            put(f0 + 1, v, fbits((float)k2));
+          } else {
+            put(f0 + 0, v, fbits((float)(mpa * lam[a])));
+            put(f0 + 1, v, fbits((float)(mpb * lam[b])));
+            put(f0 + 2, v, fbits((float)(mqa * lam[a])));
+            put(f0 + 3, v, fbits((float)(mqb * lam[b])));
+            new_lam[p] = 1.0;
+            new_lam[q] = 1.0;
+          }
+        }
+        lam.swap(new_lam);
+      }
+      if (!ok) break;
+
+      // ---- load / store / LDS fields -----------------------------------------
+      for (int v = 0; v < nv; ++v) {
+        put(0, v, L.kept[0][v] == 2 * v ? kSelLoadKeep : kSelLoadSwap);
+      }
+      for (int tau = 0; tau <= K; ++tau) {
+        std::vector<int> slot = plan_lds_slots(L.src[tau]);
+        if (slot.empty()) { ok = false; break; }
+        for (int v = 0; v < nv; ++v) {
+          put(1 + 2 * tau, v, (uint32_t)slot[v] * 16u);
+          put(2 + 2 * tau, v, (uint32_t)slot[L.src[tau][v]] * 16u);
+        }
+      }
+      if (!ok) break;
+      const int ff = 3 + 2 * K + lay.coef * K;
+      for (int v = 0; v < nv; ++v) {
+        int kx = L.kept[K][v], kb = L.fetched[K][v];
+        int q = kx / 2;  // natural pair index the lane stores
+        put(ff + 0, v, fbits((float)lam[kx]));
+        put(ff + 1, v, fbits((float)lam[kb]));
+        put(ff + 2, v, (uint32_t)q * 4u);
+        put(ff + 3, v, (kx & 1) == 0 ? kSelStoreX : kSelStoreB);
+      }
+    }
+    if (ok) {
+      P.lay = lay;
+      P.table.swap(table);
+      return PARO_OK;
+    }
+  }
+  set_error("internal: could not build the rotation schedule");
+  return PARO_ERR_HIP;
+}
+
+}  // namespace paro

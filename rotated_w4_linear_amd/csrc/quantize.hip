@@ -1,0 +1,122 @@
+// gfx950 kernel for the offline weight transform T W and W4 group quantization.
+//
+// Method: ParoQuant paper notes, section "关键设计" (W scaled by alpha, then the
+// K independent-rotation stages) and "损失函数 / 训练策略" / "主实验" (int4
+// weights with a per-group scale s and zero z, group 128). The quantizer
+// formula is not on the pages; this library uses asymmetric min/max
+// round-to-nearest over 15 steps with the range widened to include zero, an
+// fp16 scale and an integer zero, in a fixed fp32 order of operations so that
+// codes, scales and zeros are reproducible bit for bit:
+//   u_k = fl(w_k alpha_k); per pair u_i = fl(fl(c a) - fl(s b)), u_j = fl(fl(s a) + fl(c b));
+//   s32 = fl(fl(max(0,max u) - min(0,min u)) / 15); s16 = fp16_rne(s32) (0 -> 1.0);
+//   z = clamp(rint(fl(-mn / s16)), 0, 15); q = clamp(rint(fl(u / s16)) + z, 0, 15).
+// The file is compiled without floating-point contraction.
+//
+// One wavefront owns one (output row, group): the group lives in a
+// wave-private LDS slice, each lane updates its own pairs per stage, and
+// min/max are wave reductions (exact in any order).
+#include <cmath>
+
+#include "paro_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace paro {
+namespace {
+
+__global__ __launch_bounds__(256) void quantize_kernel(
+    const uint16_t* __restrict__ w, int64_t N, int64_t d, int G, int K,
+    const uint32_t* __restrict__ wt_pairs, const float* __restrict__ wt_c,
+    const float* __restrict__ wt_s, const float* __restrict__ alpha, uint8_t* __restrict__ qweight,
+    uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros, int* __restrict__ flag) {
+  __shared__ float buf[4][256];
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int64_t groups = d / G;
+  const int64_t total = N * groups;
+  float* u = buf[wid];
+  const int half = G / 2;
+  for (int64_t item = (int64_t)blockIdx.x * 4 + wid; item < total; item += (int64_t)gridDim.x * 4) {
+    const int64_t n = item / groups;
+    const int64_t g = item - n * groups;
+    const uint16_t* wr = w + n * d + g * G;
+    for (int k = lane; k < G; k += 64) {
+      float v = (float)__builtin_bit_cast(_Float16, wr[k]);
+      if (alpha) v = v * alpha[g * G + k];
+      u[k] = v;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int t = 0; t < K; ++t) {
+      const size_t base = ((size_t)g * K + t) * half;
+      for (int p = lane; p < half; p += 64) {
+        const uint32_t ij = wt_pairs[base + p];
+        const int i = (int)(ij & 0xffffu), j = (int)(ij >> 16);
+        const float c = wt_c[base + p], s = wt_s[base + p];
+        const float a = u[i], b = u[j];
+        const float ca = c * a, sb = s * b, sa = s * a, cb = c * b;
+        u[i] = ca - sb;
+        u[j] = sa + cb;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    float mn = 0.0f, mx = 0.0f;
+    int bad = 0;
+    for (int k = lane; k < G; k += 64) {
+      const float v = u[k];
+      bad |= !__builtin_isfinite(v);
+      mn = fminf(mn, v);
+      mx = fmaxf(mx, v);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      mn = fminf(mn, __shfl_xor(mn, off, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+      bad |= __shfl_xor(bad, off, 64);
+    }
+    const float range = mx - mn;
+    const float s32 = range / 15.0f;
+    _Float16 s16 = (_Float16)s32;
+    float sq = (float)s16;
+    if (bad || !__builtin_isfinite(sq)) {
+      if (lane == 0) atomicOr(flag, 1);
+    }
+    if (sq == 0.0f) {
+      s16 = (_Float16)1.0f;
+      sq = 1.0f;
+    }
+    const float negmn = -mn;
+    const float zf = fminf(fmaxf(rintf(negmn / sq), 0.0f), 15.0f);
+    for (int b = lane; b < half; b += 64) {
+      const float q0f = fminf(fmaxf(rintf(u[2 * b] / sq) + zf, 0.0f), 15.0f);
+      const float q1f = fminf(fmaxf(rintf(u[2 * b + 1] / sq) + zf, 0.0f), 15.0f);
+      const uint32_t q0 = (uint32_t)q0f, q1 = (uint32_t)q1f;
+      qweight[n * (d / 2) + g * half + b] = (uint8_t)(q0 | (q1 << 4));
+    }
+    if (lane == 0) {
+      scales[n * groups + g] = __builtin_bit_cast(uint16_t, s16);
+      zeros[n * groups + g] = (uint8_t)zf;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const paro_rotation* r, const uint16_t* w, int64_t N, int64_t d,
+                           int group, uint8_t* qweight, uint16_t* scales, uint8_t* zeros,
+                           int* d_flag, hipStream_t stream) {
+  const int64_t total = N * (d / group);
+  if (total == 0) return hipSuccess;
+  int64_t blocks = (total + 3) / 4;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w, N, d, group,
+                     r ? r->K : 0, r ? r->d_wt_pairs : nullptr, r ? r->d_wt_c : nullptr,
+                     r ? r->d_wt_s : nullptr, r ? r->d_alpha : nullptr, qweight, scales, zeros,
+                     d_flag);
+  return hipGetLastError();
+}
+
+}  // namespace paro

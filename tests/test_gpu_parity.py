@@ -1,0 +1,302 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+* rotation: X' within the floored max relative error 2e-3 of the fp64 oracle;
+* quantization: qweight, scales and zeros byte-for-byte equal to the oracle's
+  canonical fp32 quantizer;
+* linear: ||Y - Y_ref||_F / ||Y_ref||_F <= 1e-2 and max|Y - Y_ref| <= 5e-2 max|Y_ref|
+  against the fp64 oracle on the same codes.
+
+Full-size workloads are checked on sampled token rows / weight rows (every row
+is independent, so the oracle computes them one by one) in the same launch
+configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from oracle import metrics
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def paro():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rotated_w4_linear_amd as p
+    p.load_library()
+    return p
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# rotation
+# ----------------------------------------------------------------------------
+
+def check_rotation(paro, x, layer, rows=None, inplace=False):
+    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, layer.group)
+    xd = dev(x)
+    if inplace:
+        yd = paro.paro_rotate(r, xd, xd)
+    else:
+        yd = paro.paro_rotate(r, xd)
+    got = host(yd)
+    idx = np.arange(x.shape[0]) if rows is None else rows
+    ref = oracle.rotate_activations(x[idx], layer.pairs, layer.theta, layer.alpha)
+    err = metrics.assert_rotated_close(got[idx], ref, layer.group)
+    r.close()
+    return err, got
+
+
+def test_rotate_tiny(paro):
+    x, layer = synthetic.tiny()
+    log("rotate tiny 4x256 G128 K8")
+    check_rotation(paro, x, layer)
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_rotate_decode(paro, M):
+    layer = synthetic.decode_layer()
+    log(f"rotate decode M={M}")
+    check_rotation(paro, synthetic.decode_x(M), layer)
+
+
+@pytest.mark.parametrize("G,K,d,M", [(64, 8, 512, 37), (256, 8, 512, 37), (128, 1, 384, 9),
+                                     (128, 0, 256, 5), (256, 0, 512, 3), (64, 0, 256, 2),
+                                     (128, 3, 1024, 100), (256, 5, 768, 19), (128, 16, 256, 7),
+                                     (64, 32, 256, 5), (256, 12, 512, 6), (128, 2, 128, 1)])
+def test_rotate_shapes(paro, G, K, d, M):
+    log(f"rotate G={G} K={K} d={d} M={M}")
+    x, layer = synthetic.rotation_case(seed=G + K * 7 + d + M, M=M, d=d, group=G, K=K)
+    check_rotation(paro, x, layer)
+
+
+def test_rotate_general_form_and_identity_angles(paro):
+    log("rotate with theta=0 pairs (general 2x2 form)")
+    x, layer = synthetic.rotation_case(seed=11, M=33, d=512, group=128, K=8)
+    layer.theta[:, ::3] = 0.0
+    img, lay = paro.paro_rotation_plan_host(layer.pairs, layer.theta, layer.alpha, 128)
+    assert not lay["fast"]
+    check_rotation(paro, x, layer)
+    # all angles zero: X' = X / alpha exactly up to the fp16 rounding
+    layer.theta[:] = 0.0
+    _, got = check_rotation(paro, x, layer)
+    want = (x.astype(np.float64) / layer.alpha.astype(np.float64)).astype(np.float16)
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
+def test_rotate_inplace_and_empty(paro):
+    log("rotate in place / M=0")
+    x, layer = synthetic.rotation_case(seed=3, M=21, d=512, group=128, K=8)
+    check_rotation(paro, x, layer, inplace=True)
+    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, 128)
+    empty = torch.empty((0, 512), dtype=torch.float16, device="cuda")
+    out = paro.paro_rotate(r, empty)
+    assert out.shape == (0, 512)
+
+
+def test_rotate_deterministic(paro):
+    x, layer = synthetic.rotation_case(seed=4, M=333, d=1024, group=128, K=8)
+    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, 128)
+    xd = dev(x)
+    a = host(paro.paro_rotate(r, xd))
+    b = host(paro.paro_rotate(r, xd))
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+@pytest.mark.parametrize("point", list(range(27)))
+def test_rotate_sweep_full_size(paro, point):
+    """The 27 sweep points at M = 8192 (the benchmark's launch), 96 sampled rows checked."""
+    x, layer = synthetic.sweep(point)
+    d, K, G = synthetic.sweep_points()[point]
+    log(f"rotate sweep point {point}: d={d} K={K} G={G}")
+    rows = np.sort(synthetic.rng_for(3000, point).choice(x.shape[0], 96, replace=False))
+    rows[-1] = x.shape[0] - 1
+    check_rotation(paro, x, layer, rows=rows)
+
+
+# ----------------------------------------------------------------------------
+# quantization
+# ----------------------------------------------------------------------------
+
+def check_quantize(paro, layer, rotated=True, rows=None, group=None):
+    group = group or layer.group
+    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, layer.group) if rotated else None
+    qw, s, z = paro.paro_quantize_weights(r, dev(layer.w), group)
+    qw, s, z = host(qw), host(s), host(z)
+    idx = np.arange(layer.w.shape[0]) if rows is None else rows
+    if rotated:
+        rq, rs, rz = oracle.quantize_weights(layer.w[idx], group, layer.pairs, layer.theta, layer.alpha)
+    else:
+        rq, rs, rz = oracle.quantize_weights(layer.w[idx], group)
+    for name, g, w in (("qweight", qw[idx], rq), ("scales", s[idx].view(np.uint16), rs.view(np.uint16)),
+                       ("zeros", z[idx], rz)):
+        bad = np.argwhere(g != w)
+        assert bad.size == 0, f"{name}: {len(bad)} mismatches, first at {bad[0]}: {g[tuple(bad[0])]} vs {w[tuple(bad[0])]}"
+    return qw, s, z
+
+
+def test_quantize_tiny(paro):
+    log("quantize tiny")
+    _, layer = synthetic.tiny()
+    check_quantize(paro, layer)
+    check_quantize(paro, layer, rotated=False)
+
+
+def test_quantize_decode_layer_full(paro):
+    log("quantize decode layer 4096x4096 (all rows)")
+    check_quantize(paro, synthetic.decode_layer())
+
+
+@pytest.mark.parametrize("which", ["mlp", "down"])
+def test_quantize_prefill_layers_sampled(paro, which):
+    _, layer = synthetic.prefill_mlp() if which == "mlp" else synthetic.prefill_down()
+    rows = np.sort(synthetic.rng_for(3100, 0 if which == "mlp" else 1).choice(layer.w.shape[0], 384, replace=False))
+    log(f"quantize {which} {layer.w.shape} on {len(rows)} sampled rows")
+    check_quantize(paro, layer, rows=rows)
+    check_quantize(paro, layer, rotated=False, rows=rows[:64])
+
+
+@pytest.mark.parametrize("G", [64, 256])
+def test_quantize_other_groups(paro, G):
+    log(f"quantize group {G}")
+    rng = synthetic.rng_for(3200, G)
+    w = synthetic.draw_w(rng, 40, 512, 0.02, n_outlier_cols=3)
+    pairs, theta, alpha = synthetic.draw_rotation(rng, 512, G, 5)
+    check_quantize(paro, synthetic.Layer(w, pairs, theta, alpha, G))
+
+
+def test_quantize_zero_angles_equal_plain_scaled(paro):
+    """theta = 0: codes equal the K = 0 (scale-only) codes bit for bit."""
+    rng = synthetic.rng_for(3300, 0)
+    w = synthetic.draw_w(rng, 32, 256, 0.02)
+    pairs, theta, alpha = synthetic.draw_rotation(rng, 256, 128, 8)
+    a = paro.paro_quantize_weights(paro.Rotation(pairs, np.zeros_like(theta), alpha, 128), dev(w), 128)
+    b = paro.paro_quantize_weights(paro.Rotation(pairs[:0], theta[:0], alpha, 128), dev(w), 128)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+def test_quantize_nonfinite_weight_is_an_error(paro):
+    w = synthetic.draw_w(synthetic.rng_for(3400, 0), 8, 256, 0.02)
+    w[3, 17] = np.float16(np.inf)
+    with pytest.raises(paro.ParoError) as e:
+        paro.paro_quantize_weights(None, dev(w), 128)
+    assert e.value.status == -4
+    big = np.full((4, 256), 60000, np.float16)
+    big[:, ::2] = -60000
+    with pytest.raises(paro.ParoError):
+        # range 120000 / 15 = 8000 fits; scaled by alpha = 16 it overflows fp16
+        pairs, theta, _ = synthetic.draw_rotation(synthetic.rng_for(3400, 1), 256, 128, 1)
+        paro.paro_quantize_weights(paro.Rotation(pairs, theta, np.full(256, 16.0, np.float32), 128),
+                                   dev(big), 128)
+
+
+# ----------------------------------------------------------------------------
+# the linear layer
+# ----------------------------------------------------------------------------
+
+def check_linear(paro, x, layer, bias=None, rotated=True, rows=None):
+    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, layer.group) if rotated else None
+    qw, s, z = paro.paro_quantize_weights(r, dev(layer.w), 128)
+    y = host(paro.paro_w4_linear(r, dev(x), qw, s, z, dev(bias) if bias is not None else None))
+    qw, s, z = host(qw), host(s), host(z)
+    idx = np.arange(x.shape[0]) if rows is None else rows
+    if rotated:
+        ref = oracle.rotated_w4_linear(x[idx], qw, s, z, 128, layer.pairs, layer.theta, layer.alpha, bias)
+    else:
+        ref = oracle.rotated_w4_linear(x[idx], qw, s, z, 128, bias=bias)
+    assert np.all(np.isfinite(y[idx].astype(np.float32)))
+    return metrics.assert_linear_close(y[idx], ref)
+
+
+def test_linear_tiny(paro):
+    log("linear tiny (GEMV)")
+    x, layer = synthetic.tiny()
+    check_linear(paro, x, layer)
+    check_linear(paro, x, layer, rotated=False)
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_linear_decode(paro, M):
+    log(f"linear decode M={M}")
+    layer = synthetic.decode_layer()
+    check_linear(paro, synthetic.decode_x(M), layer)
+    check_linear(paro, synthetic.decode_x(M), layer, rotated=False)
+
+
+@pytest.mark.parametrize("M,d,N", [(17, 256, 64), (130, 512, 272), (300, 384, 128), (256, 1024, 512),
+                                   (3, 512, 48), (9, 1152, 1040)])
+def test_linear_shapes_with_bias(paro, M, d, N):
+    log(f"linear M={M} d={d} N={N}")
+    x, layer, b = synthetic.linear_case(seed=M + d + N, M=M, d=d, N=N)
+    check_linear(paro, x, layer, bias=b)
+
+
+def test_linear_gemv_vs_gemm_same_rows(paro):
+    """Rows 0..15 through the GEMV (M = 16) and the GEMM (M = 40) agree."""
+    x, layer, b = synthetic.linear_case(seed=5, M=40, d=1024, N=256)
+    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, 128)
+    qw, s, z = paro.paro_quantize_weights(r, dev(layer.w), 128)
+    xd = dev(x)
+    y_gemm = host(paro.paro_w4_linear(r, xd, qw, s, z, dev(b)))
+    y_gemv = host(paro.paro_w4_linear(r, xd[:16].contiguous(), qw, s, z, dev(b)))
+    fro, mx = metrics.linear_error(y_gemv, y_gemm[:16])
+    assert fro < 1e-3 and mx < 5e-3
+
+
+def test_linear_one_hot_reads_weights(paro):
+    """X = e_k (no rotation) reads out dequantized weight columns plus the bias (GEMV and GEMM)."""
+    d, N = 256, 64
+    x, layer, b = synthetic.linear_case(seed=6, M=1, d=d, N=N)
+    qw, s, z = paro.paro_quantize_weights(None, dev(layer.w), 128)
+    w_hat = oracle.dequantize(host(qw), host(s), host(z), 128)
+    for rows in (np.arange(0, 16), np.arange(0, d)):
+        eye = np.zeros((len(rows), d), np.float16)
+        eye[np.arange(len(rows)), rows] = 1
+        y = host(paro.paro_w4_linear(None, dev(eye), qw, s, z, dev(b))).astype(np.float64)
+        want = (w_hat[:, rows].T + b.astype(np.float64)[None, :]).astype(np.float16).astype(np.float64)
+        # fp16 rounding of (q - z) * s in the kernel, then of the sum with the bias
+        assert np.max(np.abs(y - want)) <= 2 * 2.0 ** -10 * (np.abs(want).max() + 1)
+
+
+def test_linear_workspace_errors(paro):
+    x, layer, b = synthetic.linear_case(seed=7, M=8, d=256, N=32)
+    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, 128)
+    qw, s, z = paro.paro_quantize_weights(r, dev(layer.w), 128)
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(paro.ParoError) as e:
+        paro.paro_w4_linear(r, dev(x), qw, s, z, workspace=small)
+    assert e.value.status == -7
+    assert paro.paro_w4_linear_workspace_size(r, 8, 256) >= 8 * 256 * 2
+
+
+def test_linear_prefill_mlp_sampled(paro):
+    log("linear prefill MLP 8192x4096 -> 14336 (sampled rows)")
+    x, layer = synthetic.prefill_mlp()
+    rows = np.sort(synthetic.rng_for(3500, 0).choice(x.shape[0], 48, replace=False))
+    rows[-1] = x.shape[0] - 1
+    check_linear(paro, x, layer, rows=rows)
+
+
+def test_linear_prefill_down_sampled(paro):
+    log("linear prefill down 2048x14336 -> 4096 (sampled rows)")
+    x, layer = synthetic.prefill_down()
+    rows = np.sort(synthetic.rng_for(3500, 1).choice(x.shape[0], 48, replace=False))
+    rows[-1] = x.shape[0] - 1
+    check_linear(paro, x, layer, rows=rows)

@@ -1,0 +1,243 @@
+"""CPU tests of the C-ABI library: exports, argument validation, rotation schedule.
+
+No kernel is launched here. The schedule test emulates, in numpy, exactly what
+the rotation kernel executes from the table image that paro_rotation_create
+uploads (load selector, keep/fetch exchanges through LDS slots, two-FMA or 2x2
+stage updates, deferred scales, store selector) and compares the result with
+the oracle.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from oracle import metrics
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def paro():
+    import rotated_w4_linear_amd as p
+    if not os.path.exists(p.LIB_PATH):
+        pytest.skip("libparo.so not built")
+    p.load_library()
+    return p
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "paro.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(paro_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol(paro):
+    names = header_functions()
+    assert "paro_rotate" in names and "paro_w4_linear" in names and "paro_quantize_weights" in names
+    lib = ctypes.CDLL(paro.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/paro.h but not exported"
+
+
+def test_status_strings(paro):
+    lib = paro.load_library()
+    for code, name in paro.STATUS.items():
+        assert lib.paro_status_string(code).decode() == name
+    assert lib.paro_status_string(123).decode() == "PARO_ERR_UNKNOWN"
+
+
+def _create(paro, d, group, K, pairs, theta, alpha):
+    lib = paro.load_library()
+    h = ctypes.c_void_p()
+    pairs = np.ascontiguousarray(pairs, np.int32)
+    theta = np.ascontiguousarray(theta, np.float32)
+    alpha = np.ascontiguousarray(alpha, np.float32)
+    st = lib.paro_rotation_create(d, group, K, paro._ptr(pairs), paro._ptr(theta),
+                                  paro._ptr(alpha), ctypes.byref(h))
+    return st, h
+
+
+def test_create_validation_errors(paro):
+    d, G, K = 256, 128, 3
+    pairs, theta, alpha = synthetic.draw_rotation(synthetic.rng_for(77, 1), d, G, K)
+    cases = []
+    dup = pairs.copy(); dup[1, 0, 1] = dup[1, 1, 0]
+    cases.append(("duplicate channel", (d, G, K, dup, theta, alpha), -3))
+    cross = pairs.copy(); a, b = cross[0, 0, 0], cross[0, 64, 0]
+    cross[0, 0, 0], cross[0, 64, 0] = b, a
+    cases.append(("pair crosses group", (d, G, K, cross, theta, alpha), -3))
+    oob = pairs.copy(); oob[2, 5, 0] = d
+    cases.append(("index out of range", (d, G, K, oob, theta, alpha), -3))
+    same = pairs.copy(); same[0, 3, 1] = same[0, 3, 0]
+    cases.append(("i == j", (d, G, K, same, theta, alpha), -3))
+    bad_a = alpha.copy(); bad_a[7] = 0.0
+    cases.append(("alpha zero", (d, G, K, pairs, theta, bad_a), -4))
+    bad_a2 = alpha.copy(); bad_a2[9] = np.nan
+    cases.append(("alpha nan", (d, G, K, pairs, theta, bad_a2), -4))
+    bad_t = theta.copy(); bad_t[1, 2] = np.inf
+    cases.append(("theta inf", (d, G, K, pairs, bad_t, alpha), -4))
+    cases.append(("group 96", (d, 96, K, pairs, theta, alpha), -6))
+    cases.append(("d not multiple of group", (d + 64, G, K, pairs, theta, alpha), -2))
+    cases.append(("K too large", (d, G, 33, np.zeros((33, d // 2, 2), np.int32),
+                                  np.zeros((33, d // 2), np.float32), alpha), -6))
+    for name, args, want in cases:
+        st, h = _create(paro, *args)
+        assert st == want, f"{name}: got {st}, want {want}"
+        assert not h.value
+    lib = paro.load_library()
+    assert lib.paro_rotation_create(d, G, K, None, None, None, None) == -1
+    assert "NULL" in lib.paro_last_error().decode() or lib.paro_last_error()
+
+
+def test_hot_calls_validate_before_any_launch(paro):
+    lib = paro.load_library()
+    assert lib.paro_rotate(None, None, None, 4, None) == -1
+    assert lib.paro_rotate(None, None, None, 0, None) == -1  # handle still required
+    dummy = ctypes.c_void_p(16 * 1024)
+    bad = ctypes.c_void_p(16 * 1024 + 2)
+    # null handle
+    assert lib.paro_rotate(None, dummy, dummy, 4, None) == -1
+    # w4_linear: group other than 128 is unsupported; N % 16, d % 128 are shape errors
+    args = [None, dummy, dummy, dummy, dummy, None, dummy]
+    assert lib.paro_w4_linear(*args, 4, 64, 256, 64, None, 0, None) == -6
+    assert lib.paro_w4_linear(*args, 4, 60, 256, 128, None, 0, None) == -2
+    assert lib.paro_w4_linear(*args, 4, 64, 200, 128, None, 0, None) == -2
+    assert lib.paro_w4_linear(*args, -1, 64, 256, 128, None, 0, None) == -2
+    assert lib.paro_w4_linear(None, bad, dummy, dummy, dummy, None, dummy, 4, 64, 256, 128,
+                              None, 0, None) == -5
+    assert lib.paro_w4_linear(None, None, dummy, dummy, dummy, None, dummy, 4, 64, 256, 128,
+                              None, 0, None) == -1
+    # M == 0 is a successful no-op, even without a GPU
+    assert lib.paro_w4_linear(*args, 0, 64, 256, 128, None, 0, None) == 0
+    # quantize: unsupported group, shape mismatch
+    assert lib.paro_quantize_weights(None, dummy, 8, 256, 96, dummy, dummy, dummy, None) == -6
+    assert lib.paro_quantize_weights(None, dummy, 8, 200, 128, dummy, dummy, dummy, None) == -2
+    assert lib.paro_quantize_weights(None, None, 8, 256, 128, dummy, dummy, dummy, None) == -1
+    assert lib.paro_w4_linear_workspace_size(None, 16, 4096) == 0
+    lib.paro_rotation_destroy(None)  # no-op
+
+
+# ----------------------------------------------------------------------------
+# schedule emulation
+# ----------------------------------------------------------------------------
+
+SEL_LOAD_KEEP, SEL_LOAD_SWAP = 0x03020100, 0x01000302
+SEL_STORE_X, SEL_STORE_B = 0x05040100, 0x01000504
+
+
+def f32(a):
+    return np.asarray(a, dtype=np.float32)
+
+
+def fma32(a, b, c):
+    """fp32 fused multiply-add (exact product in fp64, one final rounding)."""
+    return (a.astype(np.float64) * b.astype(np.float64) + c.astype(np.float64)).astype(np.float32)
+
+
+def emulate_rotate(img, lay, x, K, d):
+    nv = lay["seg_ch"] // 2
+    W = lay["words"]
+    C = 2 if lay["fast"] else 4
+    segs = d // lay["seg_ch"]
+    tab = img.reshape(segs, W, nv)
+    M = x.shape[0]
+    out = np.zeros((M, d), np.float16)
+    for s in range(segs):
+        t = tab[s]
+        seg = x[:, s * lay["seg_ch"]:(s + 1) * lay["seg_ch"]].astype(np.float32)
+        lo, hi = seg[:, 0::2], seg[:, 1::2]          # [M][nv]
+        keep = t[0] == SEL_LOAD_KEEP
+        assert np.all((t[0] == SEL_LOAD_KEEP) | (t[0] == SEL_LOAD_SWAP))
+        X = np.where(keep, lo, hi)
+        B = np.where(keep, hi, lo)
+
+        def exchange(tau, B):
+            wr = t[1 + 2 * tau] // 16
+            rd = t[2 + 2 * tau] // 16
+            lds = np.zeros((M, nv), np.float32)
+            lds[:, wr] = B
+            return lds[:, rd]
+        if K > 0:
+            B = exchange(0, B)
+            for st in range(K):
+                cf = [f32(t[3 + 2 * K + C * st + e].view(np.float32)) for e in range(C)]
+                a, b = X, B
+                if C == 2:
+                    X, B = fma32(cf[0], b, a), fma32(cf[1], a, b)
+                else:
+                    X = fma32(cf[1], b, (cf[0] * a).astype(np.float32))
+                    B = fma32(cf[2], a, (cf[3] * b).astype(np.float32))
+                B = exchange(st + 1, B)
+        ff = 3 + 2 * K + C * K
+        lamX = t[ff].view(np.float32)
+        lamB = t[ff + 1].view(np.float32)
+        q = t[ff + 2] // 4
+        sel = t[ff + 3]
+        ox = (X * lamX).astype(np.float16)
+        ob = (B * lamB).astype(np.float16)
+        first = np.where(sel == SEL_STORE_X, ox, ob)
+        second = np.where(sel == SEL_STORE_X, ob, ox)
+        assert np.all((sel == SEL_STORE_X) | (sel == SEL_STORE_B))
+        assert sorted(q.tolist()) == list(range(nv))
+        o = out[:, s * lay["seg_ch"]:(s + 1) * lay["seg_ch"]]
+        o[:, 2 * q] = first
+        o[:, 2 * q + 1] = second
+    return out
+
+
+def check_slots_conflict_free(img, lay, K, d):
+    nv = lay["seg_ch"] // 2
+    tab = img.reshape(d // lay["seg_ch"], lay["words"], nv)
+    for s in range(tab.shape[0]):
+        for tau in range(K + 1):
+            wr = tab[s, 1 + 2 * tau] // 16
+            rd = tab[s, 2 + 2 * tau] // 16
+            assert sorted(wr.tolist()) == list(range(nv))
+            assert sorted(rd.tolist()) == list(range(nv))
+            for blk in range(nv // 8):
+                assert len(set((wr[8 * blk:8 * blk + 8] % 8).tolist())) == 8
+                assert len(set((rd[8 * blk:8 * blk + 8] % 8).tolist())) == 8
+
+
+@pytest.mark.parametrize("G,K,d,M", [(128, 8, 256, 5), (128, 1, 256, 3), (64, 8, 256, 4),
+                                     (256, 8, 512, 3), (256, 2, 256, 2), (128, 0, 256, 3),
+                                     (64, 3, 384, 2), (128, 4, 512, 2)])
+def test_schedule_emulation_matches_oracle(paro, G, K, d, M):
+    x, layer = synthetic.rotation_case(seed=G * 100 + K * 10 + M, M=M, d=d, group=G, K=K)
+    img, lay = paro.paro_rotation_plan_host(layer.pairs, layer.theta, layer.alpha, G)
+    assert lay["seg_ch"] == (256 if G == 256 else 128)
+    if K:
+        check_slots_conflict_free(img, lay, K, d)
+    got = emulate_rotate(img, lay, x, K, d)
+    ref = oracle.rotate_activations(x, layer.pairs, layer.theta, layer.alpha)
+    metrics.assert_rotated_close(got, ref, G)
+
+
+def test_schedule_general_form_with_identity_pairs(paro):
+    """theta = 0 (exact identities) defeat the factored form; the general 2x2 form is used."""
+    d, G, K, M = 256, 128, 6, 4
+    x, layer = synthetic.rotation_case(seed=5, M=M, d=d, group=G, K=K)
+    theta = layer.theta.copy()
+    theta[:, ::3] = 0.0
+    img, lay = paro.paro_rotation_plan_host(layer.pairs, theta, layer.alpha, G)
+    assert not lay["fast"]
+    check_slots_conflict_free(img, lay, K, d)
+    got = emulate_rotate(img, lay, x, K, d)
+    ref = oracle.rotate_activations(x, layer.pairs, theta, layer.alpha)
+    metrics.assert_rotated_close(got, ref, G)
+
+
+def test_schedule_full_decode_layer(paro):
+    """The 4096-channel, K = 8 decode layer: factored form, exact on a few tokens."""
+    layer = synthetic.decode_layer()
+    x = synthetic.decode_x(4)
+    img, lay = paro.paro_rotation_plan_host(layer.pairs, layer.theta, layer.alpha, 128)
+    assert lay["fast"]
+    check_slots_conflict_free(img, lay, 8, 4096)
+    got = emulate_rotate(img, lay, x, 8, 4096)
+    ref = oracle.rotate_activations(x, layer.pairs, layer.theta, layer.alpha)
+    metrics.assert_rotated_close(got, ref, 128)
