@@ -1,0 +1,405 @@
+"""Benchmark of the rotated W4G128 linear layer on one MI355X.
+
+Default workload: the prefill MLP up/gate layer, 8192 tokens x 4096 -> 14336,
+group 128, K = 8 rotation stages. One step is one forward pass of the layer's
+hot path: the online rotation X' = X T^-1 (paro_rotate) followed by the W4G128
+linear on X' (paro_w4_linear), i.e. exactly the two launches that
+paro_w4_linear performs with a rotation handle. The plain W4 layer (same
+kernel on the unrotated X and Q(W)) is timed the same way to give the
+rotation's overhead.
+
+Inputs are synthetic (seeded), resident in HBM before timing; distinct copies
+of X and of the quantized weights are cycled so that caches (incl. the 256 MB
+Infinity Cache) do not serve them from a previous step. Kernel durations are
+measured with HIP events recorded on the launch stream around every launch in
+the timed region.
+
+Other workloads (``--workload``): prefill_down (2048 x 14336 -> 4096),
+decode (M = 1, 4, 16 tokens, 4096 -> 4096; weight streaming), sweep (the 27
+rotation-only points, 8192 x d), copy (a plain device copy, for calibrating
+HBM byte counters).
+
+Prints one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
+METRIC = "rotated-W4G128 linear TFLOP/s + rotation HBM GB/s; % overhead vs plain W4"
+KERNEL_SOURCES = ["rotated_w4_linear_amd/csrc/rotate.hip", "rotated_w4_linear_amd/csrc/w4_linear.hip",
+                  "rotated_w4_linear_amd/csrc/plan.cpp"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_sha(path):
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        ent = data[kernel_key]
+        if ent.get("source_sha") != source_sha(ent["source"]):
+            return None
+        return ent["bytes_per_launch"]
+    except Exception:
+        return None
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+class Timer:
+    """HIP events on the current stream around each launch."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def event(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+
+def setup_layer(paro, torch, x, layer, ring):
+    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, layer.group)
+    w = torch.from_numpy(layer.w).cuda()
+    q_rot = paro.paro_quantize_weights(r, w, 128)
+    q_plain = paro.paro_quantize_weights(None, w, 128)
+    del w
+    xs = [torch.from_numpy(x).cuda()]
+    for _ in range(ring - 1):
+        xs.append(xs[0].clone())
+    qr = [q_rot] + [tuple(t.clone() for t in q_rot) for _ in range(ring - 1)]
+    qp = [q_plain] + [tuple(t.clone() for t in q_plain) for _ in range(ring - 1)]
+    torch.cuda.synchronize()
+    return r, xs, qr, qp
+
+
+def time_layer(paro, torch, r, xs, qr, qp, steps, warmup, M, N, d):
+    """Return per-step and per-kernel timings (ms) of the rotated and plain layer."""
+    ring = len(xs)
+    xr = torch.empty((M, d), dtype=torch.float16, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    T = Timer(torch)
+
+    def rotated_step(i):
+        k = i % ring
+        paro.paro_rotate(r, xs[k], xr)
+        e1 = T.event()
+        paro.paro_w4_linear(None, xr, *qr[k], y=y)
+        return e1
+
+    for i in range(warmup):
+        rotated_step(i)
+    torch.cuda.synchronize()
+    ev = []
+    start = T.event()
+    prev = start
+    for i in range(steps):
+        mid = rotated_step(i)
+        end = T.event()
+        ev.append((prev, mid, end))
+        prev = end
+    torch.cuda.synchronize()
+    total = start.elapsed_time(prev)
+    rot = [a.elapsed_time(b) for a, b, _ in ev]
+    lin = [b.elapsed_time(c) for _, b, c in ev]
+
+    # the fused entry point (rotation handle passed to paro_w4_linear) on the same data
+    ws = torch.empty(paro.paro_w4_linear_workspace_size(r, M, d), dtype=torch.uint8, device="cuda")
+    for i in range(2):
+        paro.paro_w4_linear(r, xs[i % ring], *qr[i % ring], y=y, workspace=ws)
+    torch.cuda.synchronize()
+    s = T.event()
+    for i in range(steps):
+        paro.paro_w4_linear(r, xs[i % ring], *qr[i % ring], y=y, workspace=ws)
+    e = T.event()
+    torch.cuda.synchronize()
+    fused = s.elapsed_time(e) / steps
+
+    # plain W4 (no rotation) on the unrotated activations
+    for i in range(warmup):
+        paro.paro_w4_linear(None, xs[i % ring], *qp[i % ring], y=y)
+    torch.cuda.synchronize()
+    plain = []
+    for i in range(steps):
+        a = T.event()
+        paro.paro_w4_linear(None, xs[i % ring], *qp[i % ring], y=y)
+        b = T.event()
+        plain.append((a, b))
+    torch.cuda.synchronize()
+    plain_ms = [a.elapsed_time(b) for a, b in plain]
+    return {
+        "step_ms": total / steps,
+        "rot_ms": float(np.mean(rot)),
+        "lin_ms": float(np.mean(lin)),
+        "fused_call_ms": fused,
+        "plain_ms": float(np.mean(plain_ms)),
+    }
+
+
+def cpu_baseline(x, layer, paro_q, N, d, target_s=12.0):
+    """Time the oracle (rotation + fp64 linear) on a bounded sample of token rows."""
+    import oracle
+    qw, s, z = paro_q
+    m = 16
+    t_used = 0.0
+    while True:
+        t0 = time.perf_counter()
+        xr = oracle.rotate_activations(x[:m], layer.pairs, layer.theta, layer.alpha)
+        oracle.linear(xr, qw, s, z, 128)
+        t_used = time.perf_counter() - t0
+        if t_used > target_s / 4 or m >= x.shape[0]:
+            break
+        m = min(x.shape[0], m * 4)
+    flops = 2.0 * m * N * d
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"{m} of {x.shape[0]} token rows: fp64 rotation + dequantize + fp64 matmul "
+                      f"({t_used:.1f} s)"}
+
+
+def bench_layer(args, paro, torch, name, x, layer):
+    M, d = x.shape
+    N = layer.w.shape[0]
+    ring = args.ring or 4
+    log(f"[bench] {name}: M={M} d={d} N={N} ring={ring}")
+    r, xs, qr, qp = setup_layer(paro, torch, x, layer, ring)
+    tm = time_layer(paro, torch, r, xs, qr, qp, args.steps, args.warmup, M, N, d)
+    flops = 2.0 * M * N * d
+    rot_bytes = 4.0 * M * d
+    lin_tflops = flops / (tm["lin_ms"] * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(flops / (tm["step_ms"] * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(tm["step_ms"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": name, "tokens": M, "in_features": d, "out_features": N,
+                   "group": 128, "stages_K": layer.K},
+        "rotation_gbps": round(rot_bytes / (tm["rot_ms"] * 1e-3) / 1e9, 1),
+        "rotation_ms": round(tm["rot_ms"], 4),
+        "linear_ms": round(tm["lin_ms"], 4),
+        "plain_w4_ms": round(tm["plain_ms"], 4),
+        "plain_w4_tflops": round(flops / (tm["plain_ms"] * 1e-3) / 1e12, 3),
+        "fused_entry_ms": round(tm["fused_call_ms"], 4),
+        "overhead_vs_plain_pct": round(100.0 * (tm["step_ms"] - tm["plain_ms"]) / tm["plain_ms"], 2),
+        "rotation_share_pct": round(100.0 * tm["rot_ms"] / tm["step_ms"], 2),
+        "roofline": {"bound": "mfma", "achieved": round(lin_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(lin_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": traffic_for(f"w4_gemm:{name}")},
+        "roofline_rotation": {"bound": "hbm", "achieved": round(rot_bytes / (tm["rot_ms"] * 1e-3) / 1e9, 1),
+                              "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                              "frac": round(rot_bytes / (tm["rot_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                              "traffic": traffic_for(f"rotate:{name}")},
+    }
+    if args.cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        q = tuple(t.cpu().numpy() for t in qr[0])
+        out["cpu_baseline"] = cpu_baseline(x, layer, q, N, d)
+    return out
+
+
+def bench_decode(args, paro, torch):
+    import synthetic
+    layer = synthetic.decode_layer()
+    d, N = 4096, 4096
+    ring = args.ring or 128   # 128 copies of the 8.8 MB packed layer: about 1.1 GB
+    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, 128)
+    w = torch.from_numpy(layer.w).cuda()
+    q0 = paro.paro_quantize_weights(r, w, 128)
+    p0 = paro.paro_quantize_weights(None, w, 128)
+    qs = [q0] + [tuple(t.clone() for t in q0) for _ in range(ring - 1)]
+    ps = [p0] + [tuple(t.clone() for t in p0) for _ in range(min(ring, 128) - 1)]
+    T = Timer(torch)
+    res = {}
+    total_ms = 0.0
+    total_flops = 0.0
+    for M in (1, 4, 16):
+        x = torch.from_numpy(synthetic.decode_x(M)).cuda()
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        ws = torch.empty(paro.paro_w4_linear_workspace_size(r, M, d), dtype=torch.uint8, device="cuda")
+        xr = torch.empty_like(x)
+
+        def run(kind, i):
+            if kind == "rot":
+                paro.paro_w4_linear(r, x, *qs[i % ring], y=y, workspace=ws)
+            elif kind == "plain":
+                paro.paro_w4_linear(None, x, *ps[i % len(ps)], y=y)
+            elif kind == "rotate_only":
+                paro.paro_rotate(r, x, xr)
+            else:
+                paro.paro_w4_linear(None, xr, *qs[i % ring], y=y)
+
+        timing = {}
+        for kind in ("rot", "plain", "rotate_only", "linear_only"):
+            for i in range(args.warmup + 3):
+                run(kind, i)
+            torch.cuda.synchronize()
+            n = max(args.steps, 100)
+            s = T.event()
+            for i in range(n):
+                run(kind, i)
+            e = T.event()
+            torch.cuda.synchronize()
+            timing[kind] = s.elapsed_time(e) / n
+        wbytes = N * d / 2 + 3 * N * d / 128 + 2 * M * d + 2 * M * N
+        res[f"M{M}"] = {
+            "rotated_us": round(1e3 * timing["rot"], 2), "plain_us": round(1e3 * timing["plain"], 2),
+            "rotate_kernel_us": round(1e3 * timing["rotate_only"], 2),
+            "linear_kernel_us": round(1e3 * timing["linear_only"], 2),
+            "linear_gbps": round(wbytes / (timing["linear_only"] * 1e-3) / 1e9, 1),
+            "overhead_vs_plain_pct": round(100 * (timing["rot"] - timing["plain"]) / timing["plain"], 1),
+        }
+        total_ms += timing["rot"]
+        total_flops += 2.0 * M * N * d
+    lin16 = res["M16"]["linear_gbps"]
+    return {
+        "metric": METRIC, "value": round(total_flops / (total_ms * 1e-3) / 1e12, 4), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(total_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "decode_q_proj_4096x4096_M1_4_16", "group": 128, "stages_K": 8},
+        "decode": res,
+        "roofline": {"bound": "hbm", "achieved": lin16, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(lin16 / HBM_PEAK_GBPS, 4), "traffic": traffic_for("w4_gemv:decode")},
+    }
+
+
+def bench_sweep(args, paro, torch):
+    import synthetic
+    T = Timer(torch)
+    pts = []
+    ring = args.ring or 6
+    for p, (d, K, G) in enumerate(synthetic.sweep_points()):
+        x, layer = synthetic.sweep(p)
+        r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, G)
+        xs = [torch.from_numpy(x).cuda()]
+        for _ in range(ring - 1):
+            xs.append(xs[0].clone())
+        ys = [torch.empty_like(xs[0]) for _ in range(ring)]
+        for i in range(args.warmup + 2):
+            paro.paro_rotate(r, xs[i % ring], ys[i % ring])
+        torch.cuda.synchronize()
+        n = max(args.steps, 30)
+        s = T.event()
+        for i in range(n):
+            paro.paro_rotate(r, xs[i % ring], ys[i % ring])
+        e = T.event()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / n
+        gbps = 4.0 * x.shape[0] * d / (ms * 1e-3) / 1e9
+        pts.append({"d": d, "K": K, "G": G, "us": round(ms * 1e3, 2), "gbps": round(gbps, 1),
+                    "frac": round(gbps / HBM_PEAK_GBPS, 4)})
+        log(f"[sweep] d={d} K={K} G={G}: {ms*1e3:.1f} us, {gbps:.0f} GB/s")
+        del xs, ys
+    g = [q["gbps"] for q in pts]
+    k8 = [q for q in pts if q["K"] == 8 and q["G"] == 128 and q["d"] == 4096][0]
+    return {
+        "metric": "rotation HBM GB/s (paro_rotate, 8192 tokens)", "value": round(float(np.mean(g)), 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(sum(q["us"] for q in pts) / 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "rotation_sweep_8192xd_27pts"}, "points": pts,
+        "roofline": {"bound": "hbm", "achieved": k8["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": k8["frac"], "traffic": traffic_for("rotate:sweep_d4096_K8_G128")},
+    }
+
+
+def bench_copy(args, torch):
+    """A plain device copy of known size (for calibrating HBM byte counters)."""
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    T = Timer(torch)
+    s = T.event()
+    for _ in range(args.steps):
+        b.copy_(a)
+    e = T.event()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / args.steps
+    return {"metric": "device copy GB/s (read + write)", "value": round(2 * n / (ms * 1e-3) / 1e9, 1),
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": 3, "ms_per_step": round(ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8",
+            "data": "synthetic", "config": {"workload": "copy_256MiB"}}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_mlp",
+                    choices=["prefill_mlp", "prefill_down", "decode", "sweep", "tiny", "copy"])
+    ap.add_argument("--ring", type=int, default=0, help="distinct input copies cycled (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the rotated W4G128 layer is built and measured on a "
+              "single MI355X (multi-GPU sharding is described in DESIGN.md, not run).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import rotated_w4_linear_amd as paro
+    import synthetic
+    paro.load_library()
+    torch.cuda.set_device(0)
+
+    if args.workload == "prefill_mlp":
+        x, layer = synthetic.prefill_mlp()
+        out = bench_layer(args, paro, torch, "prefill_mlp_8192x4096to14336", x, layer)
+    elif args.workload == "prefill_down":
+        x, layer = synthetic.prefill_down()
+        out = bench_layer(args, paro, torch, "prefill_down_2048x14336to4096", x, layer)
+    elif args.workload == "tiny":
+        x, layer = synthetic.tiny()
+        out = bench_layer(args, paro, torch, "tiny_4x256to256", x, layer)
+    elif args.workload == "decode":
+        out = bench_decode(args, paro, torch)
+    elif args.workload == "sweep":
+        out = bench_sweep(args, paro, torch)
+    else:
+        out = bench_copy(args, torch)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
