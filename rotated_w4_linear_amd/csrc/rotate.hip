@@ -18,6 +18,7 @@
 // host). HBM traffic is one coalesced dword load and one dword store per lane
 // and token; the schedule tables are read once per wavefront.
 #include <cstring>
+#include <type_traits>
 
 #include "paro_internal.h"
 
@@ -38,20 +39,23 @@ __device__ __forceinline__ uint32_t half_bits(float f) {
 __device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
 
 // PPL: pairs per lane (1: 128-channel segments, 2: 256-channel segments).
-// KMAX: compile-time bound on the number of stages (runtime K <= KMAX).
+// KMAX: compile-time number of stages; with KEXACT the runtime K equals KMAX
+//   (straight-line code), otherwise K <= KMAX and stages past K are skipped.
 // FAST: factored two-FMA stage form (else the general 2x2 form).
-template <int PPL, int KMAX, bool FAST>
-__global__ __launch_bounds__(256) void rotate_kernel(const uint32_t* x, uint32_t* y,
+// T: tokens per batch (a multiple of 4: one LDS quad holds 4 tokens).
+template <int PPL, int KMAX, bool KEXACT, bool FAST, int T>
+__global__ __launch_bounds__(256) void rotate_kernel(const uint16_t* x, uint16_t* y,
                                                      const uint32_t* __restrict__ tab, int64_t M,
-                                                     int64_t row_dw, int segs, int K, int tpw) {
+                                                     int64_t row, int segs, int K, int tpw) {
   constexpr int NV = 64 * PPL;             // virtual lanes (pairs) per segment
-  constexpr int T = PPL == 1 ? 8 : 4;      // tokens per batch
+  constexpr int SEG = 2 * NV;              // channels per segment
   constexpr int NQ = T / 4;                // 4-token LDS quads per batch
   constexpr int C = FAST ? 2 : 4;          // coefficients per stage
   constexpr bool TREG = KMAX <= 8;         // keep the whole schedule in VGPRs
   constexpr int KR = TREG ? KMAX : 0;
-  __shared__ f4 lds_all[4][NQ * NV > 0 ? NQ * NV : 1];
+  __shared__ f4 lds_all[4][NQ * NV];
 
+  if constexpr (KEXACT) K = KMAX;
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int64_t gw = (int64_t)blockIdx.x * 4 + wid;
@@ -78,14 +82,14 @@ __global__ __launch_bounds__(256) void rotate_kernel(const uint32_t* x, uint32_t
     if constexpr (TREG) {
 #pragma unroll
       for (int tau = 0; tau <= KR; ++tau) {
-        if (tau <= K) {
+        if (KEXACT || tau <= K) {
           wr[tau][h] = tb[(size_t)(1 + 2 * tau) * NV + 64 * h];
           rd[tau][h] = tb[(size_t)(2 + 2 * tau) * NV + 64 * h];
         }
       }
 #pragma unroll
       for (int t = 0; t < KR; ++t) {
-        if (t < K) {
+        if (KEXACT || t < K) {
 #pragma unroll
           for (int e = 0; e < C; ++e) cf[t][e][h] = as_f(tb[(size_t)(3 + 2 * K + C * t + e) * NV + 64 * h]);
         }
@@ -106,65 +110,70 @@ __global__ __launch_bounds__(256) void rotate_kernel(const uint32_t* x, uint32_t
     else return as_f(tb[(size_t)(3 + 2 * K + C * t + e) * NV + 64 * h]);
   };
 
-  const int64_t seg_dw = (int64_t)seg * NV;
-  float X[PPL][T], B[PPL][T];
+  const uint16_t* xseg = x + (int64_t)seg * SEG;
+  uint16_t* yseg = y + (int64_t)seg * SEG;
 
-  auto exchange = [&](int tau) {
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-#pragma unroll
-      for (int h = 0; h < PPL; ++h) {
-        f4 v = {B[h][4 * q], B[h][4 * q + 1], B[h][4 * q + 2], B[h][4 * q + 3]};
-        *(f4*)(lds + q * NV * 16 + wr_off(tau, h)) = v;
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-#pragma unroll
-      for (int h = 0; h < PPL; ++h) {
-        f4 v = *(const f4*)(lds + q * NV * 16 + rd_off(tau, h));
-        B[h][4 * q] = v.x;
-        B[h][4 * q + 1] = v.y;
-        B[h][4 * q + 2] = v.z;
-        B[h][4 * q + 3] = v.w;
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  };
+  auto process = [&](int64_t t0, auto guarded_tag) {
+    constexpr bool GUARD = decltype(guarded_tag)::value;
+    float X[PPL][T], B[PPL][T];
 
-  for (int64_t t0 = tok0; t0 < tok1; t0 += T) {
-    // ---- load (natural channel pairs), keep one member in X --------------------
+    auto exchange = [&](int tau) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+        for (int h = 0; h < PPL; ++h) {
+          f4 v = {B[h][4 * q], B[h][4 * q + 1], B[h][4 * q + 2], B[h][4 * q + 3]};
+          *(f4*)(lds + q * NV * 16 + wr_off(tau, h)) = v;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+        for (int h = 0; h < PPL; ++h) {
+          f4 v = *(const f4*)(lds + q * NV * 16 + rd_off(tau, h));
+          B[h][4 * q] = v.x;
+          B[h][4 * q + 1] = v.y;
+          B[h][4 * q + 2] = v.z;
+          B[h][4 * q + 3] = v.w;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    // ---- load ---------------------------------------------------------------
 #pragma unroll
     for (int i = 0; i < T; ++i) {
       const int64_t tok = t0 + i;
+      const bool ok = !GUARD || tok < tok1;
+      const char* rowp = (const char*)(xseg + tok * row);
 #pragma unroll
       for (int h = 0; h < PPL; ++h) {
-        uint32_t v = 0;
-        if (tok < tok1) v = x[tok * row_dw + seg_dw + 64 * h + lane];
+        uint32_t v = ok ? ((const uint32_t*)rowp)[64 * h + lane] : 0u;
         v = __builtin_amdgcn_perm(v, v, ldsel[h]);
         X[h][i] = half_lo(v);
         B[h][i] = half_hi(v);
       }
     }
+    // ---- stages and exchanges -------------------------------------------------
     if constexpr (KMAX > 0) {
       exchange(0);
 #pragma unroll
       for (int t = 0; t < KMAX; ++t) {
-        if (t < K) {
+        if (KEXACT || t < K) {
 #pragma unroll
           for (int h = 0; h < PPL; ++h) {
 #pragma unroll
             for (int i = 0; i < T; ++i) {
               const float a = X[h][i], b = B[h][i];
               if constexpr (FAST) {
-                X[h][i] = __builtin_fmaf(coef(t, 0, h), b, a);
                 B[h][i] = __builtin_fmaf(coef(t, 1, h), a, b);
+                X[h][i] = __builtin_fmaf(coef(t, 0, h), b, a);
               } else {
-                X[h][i] = __builtin_fmaf(coef(t, 1, h), b, coef(t, 0, h) * a);
                 B[h][i] = __builtin_fmaf(coef(t, 2, h), a, coef(t, 3, h) * b);
+                X[h][i] = __builtin_fmaf(coef(t, 1, h), b, coef(t, 0, h) * a);
               }
             }
           }
@@ -172,52 +181,77 @@ __global__ __launch_bounds__(256) void rotate_kernel(const uint32_t* x, uint32_t
         }
       }
     }
-    // ---- apply the deferred scales, round to fp16, store the natural pair -------
+    // ---- deferred scales, fp16 rounding, store --------------------------------
 #pragma unroll
     for (int i = 0; i < T; ++i) {
       const int64_t tok = t0 + i;
-      if (tok < tok1) {
-        char* row = (char*)(y + tok * row_dw + seg_dw);
+      if (!GUARD || tok < tok1) {
+        char* rowp = (char*)(yseg + tok * row);
 #pragma unroll
         for (int h = 0; h < PPL; ++h) {
           const uint32_t ux = half_bits(X[h][i] * lamX[h]);
           const uint32_t ub = half_bits(B[h][i] * lamB[h]);
-          *(uint32_t*)(row + stoff[h]) = __builtin_amdgcn_perm(ub, ux, stsel[h]);
+          *(uint32_t*)(rowp + stoff[h]) = __builtin_amdgcn_perm(ub, ux, stsel[h]);
         }
       }
     }
-  }
+  };
+
+  const int64_t nfull = ((tok1 - tok0) / T) * T;
+  for (int64_t t0 = tok0; t0 < tok0 + nfull; t0 += T) process(t0, std::false_type{});
+  if (nfull < tok1 - tok0) process(tok0 + nfull, std::true_type{});
 }
 
-template <int PPL, int KMAX, bool FAST>
-hipError_t launch_t(const paro_rotation* r, const uint16_t* x, uint16_t* y, int64_t M,
-                    hipStream_t stream) {
-  const int segs = (int)(r->d / r->lay.seg_ch);
-  constexpr int T = PPL == 1 ? 8 : 4;
-  // about 4096 wavefronts in flight over the 256 CUs; tokens per wave a multiple of T
-  int64_t per = (M * segs + 4095) / 4096;
+// Tokens per wavefront: enough wavefronts to fill the chip (target_waves), a
+// multiple of the batch size T.
+inline int64_t tokens_per_wave(int64_t M, int segs, int T, int64_t target_waves) {
+  int64_t per = (M * segs + target_waves - 1) / target_waves;
   int64_t tpw = ((per + T - 1) / T) * T;
-  if (tpw < T) tpw = T;
+  return tpw < T ? T : tpw;
+}
+
+template <int PPL, int KMAX, bool KEXACT, bool FAST, int T>
+hipError_t launch_t(const paro_rotation* r, const uint16_t* x, uint16_t* y, int64_t M,
+                    hipStream_t stream, int64_t target_waves) {
+  const int segs = (int)(r->d / r->lay.seg_ch);
+  const int64_t tpw = tokens_per_wave(M, segs, T, target_waves);
   const int64_t chunks = (M + tpw - 1) / tpw;
   const int64_t waves = chunks * segs;
   const int64_t blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL((rotate_kernel<PPL, KMAX, FAST>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                     (const uint32_t*)x, (uint32_t*)y, r->d_table, M, r->d / 2, segs, r->K,
-                     (int)tpw);
+  hipLaunchKernelGGL((rotate_kernel<PPL, KMAX, KEXACT, FAST, T>), dim3((unsigned)blocks),
+                     dim3(256), 0, stream, x, y, r->d_table, M, r->d, segs, r->K, (int)tpw);
   return hipGetLastError();
 }
 
-template <int PPL, bool FAST>
-hipError_t launch_k(const paro_rotation* r, const uint16_t* x, uint16_t* y, int64_t M,
-                    hipStream_t stream) {
+// About 8192 wavefronts per launch (32 per CU) measured best on MI355X for
+// the 8192-token workloads.
+constexpr int64_t kTargetWaves = 8192;
+
+template <int PPL>
+hipError_t launch_ppl(const paro_rotation* r, const uint16_t* x, uint16_t* y, int64_t M,
+                      hipStream_t stream) {
+  constexpr int T = PPL == 1 ? 8 : 4;
   const int K = r->K;
-  if (K == 0) return launch_t<PPL, 0, true>(r, x, y, M, stream);
-  if (K <= 1) return launch_t<PPL, 1, FAST>(r, x, y, M, stream);
-  if (K <= 2) return launch_t<PPL, 2, FAST>(r, x, y, M, stream);
-  if (K <= 4) return launch_t<PPL, 4, FAST>(r, x, y, M, stream);
-  if (K <= 8) return launch_t<PPL, 8, FAST>(r, x, y, M, stream);
-  if (K <= 16) return launch_t<PPL, 16, FAST>(r, x, y, M, stream);
-  return launch_t<PPL, 32, FAST>(r, x, y, M, stream);
+  const int64_t tw = kTargetWaves;
+  if (K == 0) return launch_t<PPL, 0, true, true, T>(r, x, y, M, stream, tw);
+  if (r->lay.fast) {
+    switch (K) {
+      case 1: return launch_t<PPL, 1, true, true, T>(r, x, y, M, stream, tw);
+      case 2: return launch_t<PPL, 2, true, true, T>(r, x, y, M, stream, tw);
+      case 3: return launch_t<PPL, 3, true, true, T>(r, x, y, M, stream, tw);
+      case 4: return launch_t<PPL, 4, true, true, T>(r, x, y, M, stream, tw);
+      case 5: return launch_t<PPL, 5, true, true, T>(r, x, y, M, stream, tw);
+      case 6: return launch_t<PPL, 6, true, true, T>(r, x, y, M, stream, tw);
+      case 7: return launch_t<PPL, 7, true, true, T>(r, x, y, M, stream, tw);
+      case 8: return launch_t<PPL, 8, true, true, T>(r, x, y, M, stream, tw);
+      default: break;
+    }
+    if (K <= 16) return launch_t<PPL, 16, false, true, T>(r, x, y, M, stream, tw);
+    return launch_t<PPL, 32, false, true, T>(r, x, y, M, stream, tw);
+  }
+  if (K <= 8) return launch_t<PPL, 8, false, false, T>(r, x, y, M, stream, tw);
+  if (K <= 16) return launch_t<PPL, 16, false, false, T>(r, x, y, M, stream, tw);
+  return launch_t<PPL, 32, false, false, T>(r, x, y, M, stream, tw);
 }
 
 }  // namespace
@@ -225,10 +259,7 @@ hipError_t launch_k(const paro_rotation* r, const uint16_t* x, uint16_t* y, int6
 hipError_t launch_rotate(const paro_rotation* r, const uint16_t* x, uint16_t* y, int64_t M,
                          hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  if (r->lay.ppl == 1) {
-    return r->lay.fast ? launch_k<1, true>(r, x, y, M, stream) : launch_k<1, false>(r, x, y, M, stream);
-  }
-  return r->lay.fast ? launch_k<2, true>(r, x, y, M, stream) : launch_k<2, false>(r, x, y, M, stream);
+  return r->lay.ppl == 1 ? launch_ppl<1>(r, x, y, M, stream) : launch_ppl<2>(r, x, y, M, stream);
 }
 
 }  // namespace paro

@@ -149,6 +149,7 @@ def emulate_rotate(img, lay, x, K, d):
     for s in range(segs):
         t = tab[s]
         seg = x[:, s * lay["seg_ch"]:(s + 1) * lay["seg_ch"]].astype(np.float32)
+        ff = 3 + 2 * K + C * K
         lo, hi = seg[:, 0::2], seg[:, 1::2]          # [M][nv]
         keep = t[0] == SEL_LOAD_KEEP
         assert np.all((t[0] == SEL_LOAD_KEEP) | (t[0] == SEL_LOAD_SWAP))
@@ -172,7 +173,7 @@ def emulate_rotate(img, lay, x, K, d):
                     X = fma32(cf[1], b, (cf[0] * a).astype(np.float32))
                     B = fma32(cf[2], a, (cf[3] * b).astype(np.float32))
                 B = exchange(st + 1, B)
-        ff = 3 + 2 * K + C * K
+        o = out[:, s * lay["seg_ch"]:(s + 1) * lay["seg_ch"]]
         lamX = t[ff].view(np.float32)
         lamB = t[ff + 1].view(np.float32)
         q = t[ff + 2] // 4
@@ -183,7 +184,6 @@ def emulate_rotate(img, lay, x, K, d):
         second = np.where(sel == SEL_STORE_X, ob, ox)
         assert np.all((sel == SEL_STORE_X) | (sel == SEL_STORE_B))
         assert sorted(q.tolist()) == list(range(nv))
-        o = out[:, s * lay["seg_ch"]:(s + 1) * lay["seg_ch"]]
         o[:, 2 * q] = first
         o[:, 2 * q + 1] = second
     return out
@@ -212,9 +212,8 @@ def test_schedule_emulation_matches_oracle(paro, G, K, d, M):
     assert lay["seg_ch"] == (256 if G == 256 else 128)
     if K:
         check_slots_conflict_free(img, lay, K, d)
-    got = emulate_rotate(img, lay, x, K, d)
     ref = oracle.rotate_activations(x, layer.pairs, layer.theta, layer.alpha)
-    metrics.assert_rotated_close(got, ref, G)
+    metrics.assert_rotated_close(emulate_rotate(img, lay, x, K, d), ref, G)
 
 
 def test_schedule_general_form_with_identity_pairs(paro):
@@ -226,9 +225,8 @@ def test_schedule_general_form_with_identity_pairs(paro):
     img, lay = paro.paro_rotation_plan_host(layer.pairs, theta, layer.alpha, G)
     assert not lay["fast"]
     check_slots_conflict_free(img, lay, K, d)
-    got = emulate_rotate(img, lay, x, K, d)
     ref = oracle.rotate_activations(x, layer.pairs, theta, layer.alpha)
-    metrics.assert_rotated_close(got, ref, G)
+    metrics.assert_rotated_close(emulate_rotate(img, lay, x, K, d), ref, G)
 
 
 def test_schedule_full_decode_layer(paro):
@@ -238,6 +236,5 @@ def test_schedule_full_decode_layer(paro):
     img, lay = paro.paro_rotation_plan_host(layer.pairs, layer.theta, layer.alpha, 128)
     assert lay["fast"]
     check_slots_conflict_free(img, lay, 8, 4096)
-    got = emulate_rotate(img, lay, x, 8, 4096)
     ref = oracle.rotate_activations(x, layer.pairs, layer.theta, layer.alpha)
-    metrics.assert_rotated_close(got, ref, 128)
+    metrics.assert_rotated_close(emulate_rotate(img, lay, x, 8, 4096), ref, 128)
