@@ -58,33 +58,49 @@ bool augment(int u, const std::vector<std::vector<std::pair<int, int>>>& adj,
   return false;
 }
 
-// Colour the virtual lanes with 8 colours so that every block of 8 writers and
-// every block of 8 readers of one LDS instruction hits 8 different 16-byte bank
-// groups. src[v] is the lane whose Y the lane v reads. Returns slot[v].
+// LDS slots for one exchange. On gfx950 a 16-byte LDS write is conflict-free
+// when every 8 consecutive lanes hit 8 distinct 16-byte positions modulo 8, and
+// a 16-byte read when every 16 consecutive lanes hit positions distinct modulo
+// 16. src[v] is the lane whose value v reads; the lane u is written by writer
+// block u / 8 and read by reader block src_inv[u] / 16. Colour c = lo + 8 hi:
+// lo is an 8-edge-colouring of the bipartite multigraph (writer block) --
+// (reader block half), which is 8-regular once every reader block's 16 edges
+// are split into two halves of 8, so lo is distinct inside every writer block
+// and appears exactly twice inside every reader block; hi then separates the
+// two. slot = c + 16 k keeps slot % 8 = lo and slot % 16 = c. Returns slot[v].
 std::vector<int> plan_lds_slots(const std::vector<int>& src) {
   const int nv = (int)src.size();
-  const int nb = nv / 8;
+  const int nw = nv / 8, nr = nv / 16;
   std::vector<int> src_inv(nv);
   for (int v = 0; v < nv; ++v) src_inv[src[v]] = v;
-  // edge u: writer block u/8 -- reader block src_inv[u]/8
-  std::vector<std::vector<std::pair<int, int>>> adj(nb);
-  for (int u = 0; u < nv; ++u) adj[u / 8].push_back({src_inv[u] / 8, u});
+  // reader half-node of u: (src_inv[u] / 16) * 2 + (position of u among that block's lanes) / 8
+  std::vector<int> half_of(nv), seen_in_block(nr, 0);
+  for (int r = 0; r < nv; ++r) {  // iterate readers in order; each reads exactly one u
+    const int u = src[r];
+    const int blk = r / 16;
+    half_of[u] = blk * 2 + (seen_in_block[blk]++ >= 8 ? 1 : 0);
+  }
+  std::vector<std::vector<std::pair<int, int>>> adj(nw);
+  for (int u = 0; u < nv; ++u) adj[u / 8].push_back({half_of[u], u});
   std::vector<char> used(nv, 0);
-  std::vector<int> colour(nv, -1);
+  std::vector<int> lo(nv, -1);
   for (int col = 0; col < 8; ++col) {
-    std::vector<int> match_r(nb, -1), match_e(nb, -1);
-    for (int u = 0; u < nb; ++u) {
-      std::vector<char> seen(nb, 0);
+    std::vector<int> match_r(2 * nr, -1), match_e(2 * nr, -1);
+    for (int u = 0; u < nw; ++u) {
+      std::vector<char> seen(2 * nr, 0);
       augment(u, adj, match_r, match_e, seen, used);
     }
-    for (int v = 0; v < nb; ++v) {
+    for (int v = 0; v < 2 * nr; ++v) {
       if (match_e[v] < 0) return {};  // cannot happen for a regular bipartite multigraph
       used[match_e[v]] = 1;
-      colour[match_e[v]] = col;
+      lo[match_e[v]] = col;
     }
   }
-  std::vector<int> slot(nv), next(8, 0);
-  for (int u = 0; u < nv; ++u) slot[u] = colour[u] + 8 * next[colour[u]]++;
+  // hi: inside every reader block each lo value occurs twice (once per half)
+  std::vector<int> colour(nv);
+  for (int u = 0; u < nv; ++u) colour[u] = lo[u] + 8 * (half_of[u] & 1);
+  std::vector<int> slot(nv), next(16, 0);
+  for (int u = 0; u < nv; ++u) slot[u] = colour[u] + 16 * next[colour[u]]++;
   return slot;
 }
 

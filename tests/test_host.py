@@ -190,6 +190,9 @@ def emulate_rotate(img, lay, x, K, d):
 
 
 def check_slots_conflict_free(img, lay, K, d):
+    """gfx950 16-byte LDS accesses: writes conflict-free when every 8 consecutive
+    lanes hit slots distinct mod 8, reads when every 16 consecutive lanes hit
+    slots distinct mod 16."""
     nv = lay["seg_ch"] // 2
     tab = img.reshape(d // lay["seg_ch"], lay["words"], nv)
     for s in range(tab.shape[0]):
@@ -200,7 +203,8 @@ def check_slots_conflict_free(img, lay, K, d):
             assert sorted(rd.tolist()) == list(range(nv))
             for blk in range(nv // 8):
                 assert len(set((wr[8 * blk:8 * blk + 8] % 8).tolist())) == 8
-                assert len(set((rd[8 * blk:8 * blk + 8] % 8).tolist())) == 8
+            for blk in range(nv // 16):
+                assert len(set((rd[16 * blk:16 * blk + 16] % 16).tolist())) == 16
 
 
 @pytest.mark.parametrize("G,K,d,M", [(128, 8, 256, 5), (128, 1, 256, 3), (64, 8, 256, 4),
