@@ -78,7 +78,8 @@ typedef struct paro_rotation paro_rotation;
 /*
  * Create a rotation plan on the current HIP device (synchronous).
  *
- *   d      number of input channels; d % group == 0; d % 128 == 0.
+ *   d      number of input channels; d % group == 0; d % 128 == 0;
+ *          d <= 2^24.
  *   group  rotation group size: 64, 128 or 256 (pairs never leave a group,
  *          paper notes "关键设计").
  *   K      number of stages, 0 <= K <= 32 (the pages' default is 8).
@@ -95,7 +96,8 @@ typedef struct paro_rotation paro_rotation;
  *   out    receives the handle.
  *
  * Errors: PARO_ERR_NULL, PARO_ERR_SHAPE, PARO_ERR_PAIRING, PARO_ERR_VALUE,
- * PARO_ERR_UNSUPPORTED (group not in {64,128,256}, K > 32, d % 128 != 0),
+ * PARO_ERR_UNSUPPORTED (group not in {64,128,256}, K > 32, d % 128 != 0,
+ * d > 2^24),
  * PARO_ERR_HIP (device allocation or copy failed). The host arrays are only
  * read during the call.
  */
@@ -115,11 +117,12 @@ int paro_rotation_info(const paro_rotation* r, int64_t* d, int32_t* group, int32
  *
  *   x, y   device fp16 [M][d], 16-byte aligned. y == x (in place) is allowed;
  *          any other overlap is undefined.
- *   M      number of token rows, >= 0; M == 0 is a no-op.
+ *   M      number of token rows, 0 <= M <= 2^31 - 1; M == 0 is a no-op.
  *   stream HIP stream the kernel is enqueued on (0 = the null stream).
  *
  * Arithmetic: fp32 inside, one fp16 round-to-nearest-even per output.
- * Errors: PARO_ERR_NULL, PARO_ERR_SHAPE (M < 0), PARO_ERR_ALIGN, PARO_ERR_HIP.
+ * Errors: PARO_ERR_NULL, PARO_ERR_SHAPE (M out of range), PARO_ERR_ALIGN,
+ * PARO_ERR_HIP.
  */
 int paro_rotate(const paro_rotation* r, const uint16_t* x, uint16_t* y, int64_t M,
                 hipStream_t stream);

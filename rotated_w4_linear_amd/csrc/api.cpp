@@ -144,8 +144,8 @@ int paro_rotate(const paro_rotation* r, const uint16_t* x, uint16_t* y, int64_t 
     set_error("paro_rotate: NULL handle");
     return PARO_ERR_NULL;
   }
-  if (M < 0) {
-    set_error("paro_rotate: M < 0");
+  if (M < 0 || M > INT32_MAX) {
+    set_error("paro_rotate: M must be in [0, 2^31 - 1]");
     return PARO_ERR_SHAPE;
   }
   if (M == 0) return PARO_OK;

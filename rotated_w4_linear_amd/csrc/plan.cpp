@@ -27,8 +27,8 @@ uint32_t fbits(float f) {
 // v_perm_b32 byte selectors (result byte k <- byte sel[k] of {src0:src1}).
 constexpr uint32_t kSelLoadKeep = 0x03020100u;  // kept channel is the low half
 constexpr uint32_t kSelLoadSwap = 0x01000302u;  // kept channel is the high half
-constexpr uint32_t kSelStoreX = 0x05040100u;    // X (src1) low, fetched (src0) high
-constexpr uint32_t kSelStoreB = 0x01000504u;    // fetched low, X high
+constexpr uint32_t kSelStoreX = 0x03020100u;    // packed (X low, fetched high) as is
+constexpr uint32_t kSelStoreB = 0x01000302u;    // halves swapped: fetched low, X high
 
 // One segment's sequence of pairings: index 0 is the natural pairing before
 // stage 0, 1..K are the stages, K+1 is the natural pairing after the last
@@ -136,8 +136,8 @@ int build_rotation_plan(int64_t d, int32_t group, int32_t K, const int32_t* pair
     set_error("K > 32 is not supported");
     return PARO_ERR_UNSUPPORTED;
   }
-  if (d > (int64_t(1) << 30)) {
-    set_error("d too large");
+  if (d > (int64_t(1) << 24)) {
+    set_error("d > 2^24 is not supported");
     return PARO_ERR_UNSUPPORTED;
   }
   for (int64_t k = 0; k < d; ++k) {

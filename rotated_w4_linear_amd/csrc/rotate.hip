@@ -16,7 +16,8 @@
 // register through a per-wave LDS tile that interleaves four tokens per
 // 16-byte slot (b128 writes and reads, bank-conflict-free slots planned on the
 // host). HBM traffic is one coalesced dword load and one dword store per lane
-// and token; the schedule tables are read once per wavefront.
+// and token, the loads one batch ahead of the arithmetic; the schedule tables
+// are read once per wavefront.
 #include <cstring>
 #include <type_traits>
 
@@ -26,15 +27,16 @@ namespace paro {
 namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// Word 3 of a gfx9 buffer resource: 32-bit data format, no swizzle.
+constexpr int kRsrcWord3 = 0x00020000;
 
 __device__ __forceinline__ float half_lo(uint32_t v) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
 }
 __device__ __forceinline__ float half_hi(uint32_t v) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
-}
-__device__ __forceinline__ uint32_t half_bits(float f) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 __device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
 
@@ -45,7 +47,7 @@ __device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(fl
 // T: tokens per batch (a multiple of 4: one LDS quad holds 4 tokens).
 template <int PPL, int KMAX, bool KEXACT, bool FAST, int T>
 __global__ __launch_bounds__(256) void rotate_kernel(const uint16_t* x, uint16_t* y,
-                                                     const uint32_t* __restrict__ tab, int64_t M,
+                                                     const uint32_t* __restrict__ tab, int M,
                                                      int64_t row, int segs, int K, int tpw) {
   constexpr int NV = 64 * PPL;             // virtual lanes (pairs) per segment
   constexpr int SEG = 2 * NV;              // channels per segment
@@ -57,12 +59,14 @@ __global__ __launch_bounds__(256) void rotate_kernel(const uint16_t* x, uint16_t
 
   if constexpr (KEXACT) K = KMAX;
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  // wave-uniform: keeps the token and address arithmetic in scalar registers
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t gw = (int64_t)blockIdx.x * 4 + wid;
   const int seg = (int)(gw % segs);
-  const int64_t tok0 = (gw / segs) * (int64_t)tpw;
-  if (tok0 >= M) return;
-  const int64_t tok1 = (tok0 + tpw < M) ? tok0 + tpw : M;
+  const int64_t tok0l = (gw / segs) * (int64_t)tpw;
+  if (tok0l >= M) return;
+  const int tok0 = (int)tok0l;
+  const int tok1 = (tok0 + tpw < M) ? tok0 + tpw : M;
   const int W = 1 + 2 * (K + 1) + C * K + 4;
   const uint32_t* tb = tab + (size_t)seg * W * NV + lane;
   char* lds = (char*)&lds_all[wid][0];
@@ -113,8 +117,29 @@ __global__ __launch_bounds__(256) void rotate_kernel(const uint16_t* x, uint16_t
   const uint16_t* xseg = x + (int64_t)seg * SEG;
   uint16_t* yseg = y + (int64_t)seg * SEG;
 
-  auto process = [&](int64_t t0, auto guarded_tag) {
-    constexpr bool GUARD = decltype(guarded_tag)::value;
+  // Raw fp16 pairs of one batch. The next batch is loaded while the current
+  // one is rotated so that a wavefront always has HBM reads in flight; loads
+  // past the end of the chunk re-read its last token (in bounds, cached).
+  // Buffer instructions take the token row as a scalar offset from a
+  // wave-uniform base, so addressing costs no vector instructions.
+  const uint32_t rowb = (uint32_t)row * 2u;  // bytes per token row
+  typedef uint32_t Raw[PPL][T];
+  Raw raw;
+  auto load = [&](int t0, Raw& nxt) {
+    const int tl = (t0 < tok1) ? t0 : tok1 - 1;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(xseg + (int64_t)tl * row), (short)0, 0x7fffffff, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      const int di = (tl + i < tok1) ? i : tok1 - 1 - tl;
+#pragma unroll
+      for (int h = 0; h < PPL; ++h)
+        nxt[h][i] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (64 * h + lane), di * rowb, 0);
+    }
+  };
+
+  // Rotates the batch at t0 held in cur, then refills cur with the batch at tn.
+  auto process = [&](int t0, Raw& cur, int tn) {
     float X[PPL][T], B[PPL][T];
 
     auto exchange = [&](int tau) {
@@ -143,20 +168,17 @@ __global__ __launch_bounds__(256) void rotate_kernel(const uint16_t* x, uint16_t
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
-    // ---- load ---------------------------------------------------------------
+    // ---- unpack the current batch, start loading the next one -----------------
 #pragma unroll
     for (int i = 0; i < T; ++i) {
-      const int64_t tok = t0 + i;
-      const bool ok = !GUARD || tok < tok1;
-      const char* rowp = (const char*)(xseg + tok * row);
 #pragma unroll
       for (int h = 0; h < PPL; ++h) {
-        uint32_t v = ok ? ((const uint32_t*)rowp)[64 * h + lane] : 0u;
-        v = __builtin_amdgcn_perm(v, v, ldsel[h]);
+        const uint32_t v = __builtin_amdgcn_perm(cur[h][i], cur[h][i], ldsel[h]);
         X[h][i] = half_lo(v);
         B[h][i] = half_hi(v);
       }
     }
+    load(tn, cur);
     // ---- stages and exchanges -------------------------------------------------
     if constexpr (KMAX > 0) {
       exchange(0);
@@ -182,24 +204,24 @@ __global__ __launch_bounds__(256) void rotate_kernel(const uint16_t* x, uint16_t
       }
     }
     // ---- deferred scales, fp16 rounding, store --------------------------------
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(yseg + (int64_t)t0 * row), (short)0, 0x7fffffff, kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < T; ++i) {
-      const int64_t tok = t0 + i;
-      if (!GUARD || tok < tok1) {
-        char* rowp = (char*)(yseg + tok * row);
+      if (t0 + i < tok1) {
 #pragma unroll
         for (int h = 0; h < PPL; ++h) {
-          const uint32_t ux = half_bits(X[h][i] * lamX[h]);
-          const uint32_t ub = half_bits(B[h][i] * lamB[h]);
-          *(uint32_t*)(rowp + stoff[h]) = __builtin_amdgcn_perm(ub, ux, stsel[h]);
+          const h2 pk = {(_Float16)(X[h][i] * lamX[h]), (_Float16)(B[h][i] * lamB[h])};
+          const uint32_t u = __builtin_bit_cast(uint32_t, pk);
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_perm(u, u, stsel[h]), rs, stoff[h],
+                                                i * rowb, 0);
         }
       }
     }
   };
 
-  const int64_t nfull = ((tok1 - tok0) / T) * T;
-  for (int64_t t0 = tok0; t0 < tok0 + nfull; t0 += T) process(t0, std::false_type{});
-  if (nfull < tok1 - tok0) process(tok0 + nfull, std::true_type{});
+  load(tok0, raw);
+  for (int t0 = tok0; t0 < tok1; t0 += T) process(t0, raw, t0 + T);
 }
 
 // Tokens per wavefront: enough wavefronts to fill the chip (target_waves), a
@@ -219,7 +241,7 @@ hipError_t launch_t(const paro_rotation* r, const uint16_t* x, uint16_t* y, int6
   const int64_t waves = chunks * segs;
   const int64_t blocks = (waves + 3) / 4;
   hipLaunchKernelGGL((rotate_kernel<PPL, KMAX, KEXACT, FAST, T>), dim3((unsigned)blocks),
-                     dim3(256), 0, stream, x, y, r->d_table, M, r->d, segs, r->K, (int)tpw);
+                     dim3(256), 0, stream, x, y, r->d_table, (int)M, r->d, segs, r->K, (int)tpw);
   return hipGetLastError();
 }
 

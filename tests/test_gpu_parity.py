@@ -10,6 +10,8 @@ Full-size workloads are checked on sampled token rows / weight rows (every row
 is independent, so the oracle computes them one by one) in the same launch
 configuration the benchmark times.
 """
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -108,6 +110,12 @@ def test_rotate_inplace_and_empty(paro):
     empty = torch.empty((0, 512), dtype=torch.float16, device="cuda")
     out = paro.paro_rotate(r, empty)
     assert out.shape == (0, 512)
+    # token counts past the 32-bit row index are rejected before any launch
+    lib = paro.load_library()
+    buf = torch.zeros((4, 512), dtype=torch.float16, device="cuda")
+    st = lib.paro_rotate(r.handle, ctypes.c_void_p(buf.data_ptr()), ctypes.c_void_p(buf.data_ptr()),
+                         ctypes.c_int64(2 ** 31), None)
+    assert paro.STATUS[st] == "PARO_ERR_SHAPE"
 
 
 def test_rotate_deterministic(paro):

@@ -126,7 +126,7 @@ def test_hot_calls_validate_before_any_launch(paro):
 # ----------------------------------------------------------------------------
 
 SEL_LOAD_KEEP, SEL_LOAD_SWAP = 0x03020100, 0x01000302
-SEL_STORE_X, SEL_STORE_B = 0x05040100, 0x01000504
+SEL_STORE_X, SEL_STORE_B = 0x03020100, 0x01000302
 
 
 def f32(a):
