@@ -156,9 +156,10 @@ int paro_quantize_weights(const paro_rotation* r, const uint16_t* w, int64_t N, 
                           int32_t group, uint8_t* qweight, uint16_t* scales, uint8_t* zeros,
                           hipStream_t stream);
 
-/* Bytes of device workspace paro_w4_linear needs for this plan and M (0 when
+/* Bytes of device workspace paro_w4_linear needs for this plan (NULL: plain
+ * W4) and these sizes. 0 means the call needs no workspace (M > 16 with
  * r == NULL). */
-size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t d);
+size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t N, int64_t d);
 
 /*
  * The W4G128 linear layer on rotated activations:
@@ -170,13 +171,26 @@ size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t 
  *            paro_quantize_weights with group 128; bias device fp16 [N] or NULL;
  *   y        device fp16 [M][N] (must not overlap x).
  *   group    must be 128 (W4G128); other values return PARO_ERR_UNSUPPORTED.
+ *            A plan r must have the same d and group (the pairs stay inside
+ *            quantization groups), else PARO_ERR_SHAPE.
  *   N % 16 == 0, d % 128 == 0, M >= 0 (M == 0 is a no-op).
  *   workspace, workspace_bytes: device memory of at least
- *            paro_w4_linear_workspace_size(r, M, d) bytes, 16-byte aligned
- *            (may be NULL when that size is 0). Its contents are scratch.
+ *            paro_w4_linear_workspace_size(r, M, N, d) bytes, 256-byte
+ *            aligned (may be NULL when that size is 0). Its first 16 KiB hold
+ *            arrival counters that must be zero before the first call that
+ *            uses the workspace (zero-fill it once after allocating it); every
+ *            call leaves them zero again. The rest is scratch. Calls that may
+ *            run at the same time (different streams) need different
+ *            workspaces.
  *
- * Arithmetic: fp32 accumulation of exact fp16 products against the fp16
- * rounding of each dequantized weight (q - z) * s; fp16 output.
+ * Execution: M <= 16 runs one kernel that streams the packed weights and, for
+ * plans with K <= 8, applies the transform to the activations inside the same
+ * kernel; plans with more stages rotate into the workspace first. M > 16 rotates into the workspace and then runs
+ * the matrix-core kernel.
+ *
+ * Arithmetic: X' exactly as paro_rotate computes it (fp16); fp32 accumulation
+ * of exact fp16 products against the fp16 rounding of each dequantized weight
+ * (q - z) * s, in an order that depends on M but not on timing; fp16 output.
  * Errors: PARO_ERR_NULL, PARO_ERR_SHAPE, PARO_ERR_ALIGN, PARO_ERR_UNSUPPORTED,
  * PARO_ERR_WORKSPACE, PARO_ERR_HIP.
  */

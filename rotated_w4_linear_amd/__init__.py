@@ -61,7 +61,7 @@ def load_library() -> ctypes.CDLL:
     lib.paro_quantize_weights.restype = ctypes.c_int
     lib.paro_quantize_weights.argtypes = [vp, vp, c_i64, c_i64, c_i32, vp, vp, vp, vp]
     lib.paro_w4_linear_workspace_size.restype = c_size
-    lib.paro_w4_linear_workspace_size.argtypes = [vp, c_i64, c_i64]
+    lib.paro_w4_linear_workspace_size.argtypes = [vp, c_i64, c_i64, c_i64]
     lib.paro_w4_linear.restype = ctypes.c_int
     lib.paro_w4_linear.argtypes = [vp, vp, vp, vp, vp, vp, vp, c_i64, c_i64, c_i64, c_i32, vp,
                                    c_size, vp]
@@ -167,8 +167,15 @@ def paro_quantize_weights(r: Optional[Rotation], w, group: int = 128, stream=Non
     return qweight, scales, zeros
 
 
-def paro_w4_linear_workspace_size(r: Optional[Rotation], M: int, d: int) -> int:
-    return int(load_library().paro_w4_linear_workspace_size(_handle(r), M, d))
+def paro_w4_linear_workspace_size(r: Optional[Rotation], M: int, N: int, d: int) -> int:
+    return int(load_library().paro_w4_linear_workspace_size(_handle(r), M, N, d))
+
+
+def new_workspace(r: Optional[Rotation], M: int, N: int, d: int, device="cuda"):
+    """A zero-filled workspace for paro_w4_linear (None when none is needed)."""
+    import torch
+    need = paro_w4_linear_workspace_size(r, M, N, d)
+    return torch.zeros(need, dtype=torch.uint8, device=device) if need else None
 
 
 def paro_w4_linear(r: Optional[Rotation], x, qweight, scales, zeros, bias=None, y=None,
@@ -179,9 +186,8 @@ def paro_w4_linear(r: Optional[Rotation], x, qweight, scales, zeros, bias=None, 
     N = qweight.shape[0]
     if y is None:
         y = torch.empty((M, N), dtype=torch.float16, device=x.device)
-    need = paro_w4_linear_workspace_size(r, M, d)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace is None:
+        workspace = new_workspace(r, M, N, d, x.device)
     ws_ptr = _dptr(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load_library().paro_w4_linear(

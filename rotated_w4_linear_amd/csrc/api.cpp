@@ -207,10 +207,18 @@ int paro_quantize_weights(const paro_rotation* r, const uint16_t* w, int64_t N, 
   return PARO_OK;
 }
 
-size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t d) {
-  if (!r || M <= 0 || d <= 0) return 0;
-  size_t bytes = (size_t)M * (size_t)d * 2;
-  return (bytes + 255) & ~(size_t)255;
+size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t N, int64_t d) {
+  if (M <= 0 || N <= 0 || d <= 0) return 0;
+  auto round256 = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  if (M <= kDecodeMaxM) {
+    size_t bytes = kDecodeCounterBytes;
+    const size_t ksl = (size_t)((d / 128 + 3) / 4);
+    if (ksl > 1) bytes += round256(ksl * (size_t)M * (size_t)N * 4);
+    if (r && !decode_fuses_rotation(r)) bytes += round256((size_t)M * (size_t)d * 2);
+    return bytes;
+  }
+  if (!r) return 0;
+  return kDecodeCounterBytes + round256((size_t)M * (size_t)d * 2);
 }
 
 int paro_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qweight,
@@ -233,8 +241,8 @@ int paro_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qwe
     set_error("paro_w4_linear: sizes too large");
     return PARO_ERR_UNSUPPORTED;
   }
-  if (r && r->d != d) {
-    set_error("paro_w4_linear: d differs from the rotation plan");
+  if (r && (r->d != d || r->group != group)) {
+    set_error("paro_w4_linear: d or group differs from the rotation plan");
     return PARO_ERR_SHAPE;
   }
   if (M == 0) return PARO_OK;
@@ -246,22 +254,45 @@ int paro_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qwe
     set_error("paro_w4_linear: x, qweight, y must be 16-byte aligned (bias 8-byte)");
     return PARO_ERR_ALIGN;
   }
-  const uint16_t* xin = x;
-  if (r) {
-    const size_t need = paro_w4_linear_workspace_size(r, M, d);
+  if (M <= kDecodeMaxM && (uint64_t)((d / 128 + 3) / 4) * (uint64_t)M * (uint64_t)N * 4 >= (1ull << 31)) {
+    set_error("paro_w4_linear: ceil(d / 512) * M * N * 4 must be below 2^31 for M <= 16");
+    return PARO_ERR_UNSUPPORTED;
+  }
+  const size_t need = paro_w4_linear_workspace_size(r, M, N, d);
+  if (need) {
     if (!workspace || workspace_bytes < need) {
       set_error("paro_w4_linear: workspace missing or smaller than paro_w4_linear_workspace_size");
       return PARO_ERR_WORKSPACE;
     }
-    if (!aligned16(workspace)) {
-      set_error("paro_w4_linear: workspace must be 16-byte aligned");
+    if ((uintptr_t)workspace & 255) {
+      set_error("paro_w4_linear: workspace must be 256-byte aligned");
       return PARO_ERR_ALIGN;
     }
-    hipError_t e = launch_rotate(r, x, (uint16_t*)workspace, M, stream);
-    if (e != hipSuccess) return hip_fail(e, "paro_w4_linear rotate launch");
-    xin = (const uint16_t*)workspace;
   }
-  hipError_t e = launch_w4_linear(xin, qweight, scales, zeros, bias, y, M, N, d, stream);
+  char* ws = (char*)workspace;
+  hipError_t e = hipSuccess;
+  if (M <= kDecodeMaxM) {
+    const paro_rotation* fused = r;
+    const uint16_t* xin = x;
+    if (r && !decode_fuses_rotation(r)) {
+      // stand-alone transform into the workspace tail, then the plain kernel
+      uint16_t* xr = (uint16_t*)(ws + need - (((size_t)M * (size_t)d * 2 + 255) & ~(size_t)255));
+      e = launch_rotate(r, x, xr, M, stream);
+      if (e != hipSuccess) return hip_fail(e, "paro_w4_linear rotate launch");
+      xin = xr;
+      fused = nullptr;
+    }
+    e = launch_w4_decode(xin, qweight, scales, zeros, bias, y, M, N, d, fused, ws, stream);
+  } else {
+    const uint16_t* xin = x;
+    if (r) {
+      uint16_t* xr = (uint16_t*)(ws + kDecodeCounterBytes);
+      e = launch_rotate(r, x, xr, M, stream);
+      if (e != hipSuccess) return hip_fail(e, "paro_w4_linear rotate launch");
+      xin = xr;
+    }
+    e = launch_w4_gemm(xin, qweight, scales, zeros, bias, y, M, N, d, stream);
+  }
   if (e != hipSuccess) return hip_fail(e, "paro_w4_linear launch");
   return PARO_OK;
 }

@@ -1,0 +1,373 @@
+// gfx950 kernel for the W4G128 linear layer with few tokens (decode, M <= 16),
+// with the online activation transform fused in:
+//   Y[m][n] = sum_k X'[m][k] (q[n][k] - z[n][k/128]) s[n][k/128] + b[n],
+//   X' = X T^-1
+// (CSDN article section 2.1: Y = (X T^-1)(T W) + b; paper notes "关键设计"
+// for the rotation and "主实验" for the 4-bit, group-128 weights).
+//
+// With at most 16 tokens the layer is a stream over the packed weights, so
+// the kernel is organised around keeping HBM busy:
+//  * a workgroup owns a k-slice of 512 input channels (four 128-channel
+//    groups) and 128 output channels. Each wavefront first loads the
+//    activations (and schedule) of segment w of the slice, then issues all
+//    of its weight loads (32 rows x 512 k, 8 KB);
+//  * while the weights are in flight, wavefront w rotates its segment for
+//    all tokens in registers (the per-lane machinery of the stand-alone
+//    rotation: K stages, K + 1 LDS exchanges) and writes X' into a shared,
+//    swizzled LDS tile; without a plan it copies X there;
+//  * the weights are dequantized in registers group by group as they land
+//    and multiplied on the matrix cores (v_mfma_f32_16x16x32_f16: 16 output
+//    channels x 32 k x 16 tokens; columns past M are ignored);
+//  * k-slices meet through fp32 partial sums in the workspace; the last
+//    workgroup of an n-block to arrive (an atomic arrival counter, reset to
+//    zero by that workgroup) adds them in k-slice order, adds the bias and
+//    rounds to fp16, so the result does not depend on arrival order.
+// Partial sums and counters must be coherent between the workgroups of one
+// n-block. MI355X's L2 is per XCD and not coherent across XCDs, and an
+// agent-scope fence (write-back of the whole L2) costs more than the layer.
+// Workgroup b is dispatched to XCD b % 8, and all k-slices of an n-block get
+// equal b % 8, so they meet in one L2: plain stores, an L2 atomic and loads
+// that skip the per-CU L1 suffice. The library checks that dispatch rule once
+// per device (a probe kernel reads each workgroup's XCC id); where it does not
+// hold, the partial sums and the counter go through memory-side (system
+// scope) stores, loads and atomics instead.
+// The rotation is recomputed by each of the N / 128 n-blocks that read a
+// segment: with M <= 16 this is ALU work hidden under the weight loads.
+//
+// Dequantization: v = (1024 + q) is built in fp16 by OR-ing a nibble into the
+// mantissa of 1024.0, (v - (1024 + z)) = q - z is exact, and one packed
+// multiply by the fp16 scale rounds once. Nibbles e and e + 4 of a 32-bit word
+// share one packed pair, so the eight codes of a word come out in the k order
+// (0, 4, 1, 5, 2, 6, 3, 7); X' is stored in LDS in the same order.
+#include <mutex>
+#include <vector>
+
+#include "paro_internal.h"
+#include "rotate_core.h"
+#include "w4_common.h"
+
+#pragma clang fp contract(off)
+
+namespace paro {
+namespace {
+
+using namespace w4;
+
+constexpr int DK_SEGS = 4;                 // 128-channel groups per k-slice
+constexpr int DK_NB = 128;                 // output channels per workgroup
+constexpr int DK_TOK = 16;                 // token columns of the MFMA tile
+constexpr int kRsrcWord3 = 0x00020000;     // gfx9 buffer resource word 3
+constexpr int kAuxL2 = 1;                  // sc0: skip the per-CU cache
+constexpr int kAuxSys = 17;                // sc0 | sc1: memory-side coherence
+
+// Eight codes of a word -> fp16 (q - z) s in k order (0, 4, 1, 5, 2, 6, 3, 7).
+__device__ __forceinline__ h8 dequant8_interleaved(uint32_t w, h2 zz, h2 ss) {
+  constexpr uint32_t kMask = 0x000F000Fu, kOne = 0x64006400u;  // fp16 1024.0 pairs
+  uint32_t p[4];
+  p[0] = (w & kMask) | kOne;
+  p[1] = ((w >> 4) & kMask) | kOne;
+  p[2] = ((w >> 8) & kMask) | kOne;
+  p[3] = ((w >> 12) & kMask) | kOne;
+  h8 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h2 v = __builtin_bit_cast(h2, p[i]);
+    v = (v - zz) * ss;
+    out[2 * i] = v.x;
+    out[2 * i + 1] = v.y;
+  }
+  return out;
+}
+
+// Byte offset in the X' tile of channel k (local to the 512-wide slice) of
+// token m: chunk k / 8 at position (k / 8) ^ m, half (k % 4) * 2 + (k % 8) / 4.
+__device__ __forceinline__ int xl_offset(int m, int k) {
+  const int c = k >> 3, e = k & 7;
+  return (m * 64 + (c ^ m)) * 16 + 2 * (((e & 3) << 1) | (e >> 2));
+}
+
+// T: token rows staged and rotated (4 for M <= 4, else 16); MFMA columns past
+// T read tile rows that were never written and are ignored like those past M.
+template <bool ROT, int KMAX, bool KEXACT, bool FAST, int T>
+__global__ __launch_bounds__(256) void w4_decode_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ qw,
+    const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zr,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N, int d,
+    const uint32_t* __restrict__ tab, int K, float* part, uint32_t* cnt, int ksl, int nbl,
+    int nb_base, int sys) {
+  // X' tile: [16 tokens][64 chunks of 16 bytes]; chunk c of token m is stored
+  // at position c ^ m, so the 16 tokens of one MFMA operand read land on 16
+  // distinct 16-byte positions.
+  __shared__ u4 xl[DK_TOK * 64];
+  __shared__ rot::f4 xch[ROT ? 4 * (T / 4) * 64 : 1];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int xcd = blockIdx.x & 7, j8 = blockIdx.x >> 3;
+  const int nb = xcd + 8 * (j8 / ksl);  // n-block inside this launch
+  const int ks = j8 % ksl;              // k-slice
+  if (nb >= nbl) return;
+  const int nbg = nb_base + nb;
+  const int groups = d >> 7;
+  const int g0 = ks * DK_SEGS;
+  const int nq = min(DK_SEGS, groups - g0);
+  const int r = lane & 15, kq = lane >> 4;
+  const int rb = nbg * DK_NB + 32 * w;  // this wavefront's first output channel
+  char* xlb = (char*)xl;
+
+  // ---- 1. activations of segment g0 + w (token rows past M repeat M - 1) ---
+  // (in a slice cut short by the end of d, wavefronts without a segment
+  // process a copy of the last one into their own, never read, part of the
+  // tile: no branch lets the compiler sink these loads behind the weights)
+  const int seg = min(g0 + w, groups - 1);
+  uint32_t raw[T];
+  rot::Lane<1, KMAX, KEXACT, FAST> L;
+  {
+    const uint32_t* xs = (const uint32_t*)(x + seg * 128) + lane;
+#pragma unroll
+    for (int i = 0; i < T; ++i) raw[i] = xs[(size_t)min(i, M - 1) * (size_t)(d >> 1)];
+    if constexpr (ROT) L.load(tab, seg, K, lane);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 2. packed weights and group parameters: rows rb + 16 j + r ----------
+  // lane (r, kq) holds bytes 16 kq .. 16 kq + 15 of group g0 + q of its row,
+  // i.e. codes 128 (g0 + q) + 32 kq + 8 i + e for MFMA step i. All loads are
+  // issued here, group by group, without waiting: groups past the end of d
+  // re-read the last group (never used) and the scale and zero are converted
+  // only when their group is multiplied.
+  u4 wv[2][DK_SEGS];
+  uint32_t sraw[2][DK_SEGS], zraw[2][DK_SEGS];
+  const uint8_t* wrow[2];
+  size_t grow[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int nc = min(rb + 16 * j + r, N - 1);  // rows past N are never stored
+    wrow[j] = qw + (size_t)nc * (size_t)(d >> 1) + 16 * kq;
+    grow[j] = (size_t)nc * groups;
+  }
+#pragma unroll
+  for (int q = 0; q < DK_SEGS; ++q) {
+    const int g = min(g0 + q, groups - 1);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      wv[j][q] = *(const u4*)(wrow[j] + 64 * g);
+      sraw[j][q] = sc[grow[j] + g];
+      zraw[j][q] = zr[grow[j] + g];
+    }
+  }
+  // keep every load above ahead of the first use of the activations: the
+  // in-order load counter would otherwise hold the weight loads back
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 3. X' of the segment into the LDS tile --------------------------------
+  {
+    uint32_t pk[T];
+    int k0;  // slice-local channel of the low half of this lane's pair
+    if constexpr (ROT) {
+      float X[1][T], B[1][T];
+#pragma unroll
+      for (int i = 0; i < T; ++i) L.unpack(raw[i], 0, X[0][i], B[0][i]);
+      L.template run<T>(X, B, (char*)&xch[w * (T / 4) * 64]);
+#pragma unroll
+      for (int i = 0; i < T; ++i) pk[i] = L.pack(X[0][i], B[0][i], 0);
+      k0 = 128 * w + (int)(L.stoff[0] >> 1);
+    } else {
+#pragma unroll
+      for (int i = 0; i < T; ++i) pk[i] = raw[i];
+      k0 = 128 * w + 2 * lane;
+    }
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      *(uint16_t*)(xlb + xl_offset(i, k0)) = (uint16_t)pk[i];
+      *(uint16_t*)(xlb + xl_offset(i, k0 + 1)) = (uint16_t)(pk[i] >> 16);
+    }
+  }
+  __syncthreads();
+
+  // ---- 4. dequantize and multiply, group by group as the weights land -------
+  f4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int q = 0; q < DK_SEGS; ++q) {
+    if (q < nq) {
+      h2 ss[2], zz[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        ss[j] = splat2(__builtin_bit_cast(_Float16, (uint16_t)sraw[j][q]));
+        zz[j] = splat2((_Float16)(1024.0f + (float)zraw[j][q]));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const h8 b = *(const h8*)(xlb + (r * 64 + ((16 * q + 4 * kq + i) ^ r)) * 16);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              dequant8_interleaved(wv[j][q][i], zz[j], ss[j]), b, acc[j], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- 5. acc[j][e] = Y[n = rb + 16 j + 4 kq + e][m = r] ------------------------
+  auto store_y = [&](int m, int n, f4 v) {
+    if (bias) {
+      const uint2 braw = *(const uint2*)(bias + n);
+      v[0] += half_lo(braw.x);
+      v[1] += half_hi(braw.x);
+      v[2] += half_lo(braw.y);
+      v[3] += half_hi(braw.y);
+    }
+    uint2 o;
+    o.x = half_bits(v[0]) | (half_bits(v[1]) << 16);
+    o.y = half_bits(v[2]) | (half_bits(v[3]) << 16);
+    *(uint2*)(y + (size_t)m * N + n) = o;
+  };
+  if (ksl == 1) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = rb + 16 * j + 4 * kq;
+      if (r < M && n < N) store_y(r, n, acc[j]);
+    }
+    return;
+  }
+  // partial sums: [k-slice][M][N] fp32; offsets in bytes from part (< 2^31,
+  // checked on the host)
+  const __amdgpu_buffer_rsrc_t rp =
+      __builtin_amdgcn_make_buffer_rsrc((void*)part, (short)0, 0x7fffffff, kRsrcWord3);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = rb + 16 * j + 4 * kq;
+    if (r < M && n < N) {
+      const int off = (int)((((size_t)ks * M + r) * N + n) * 4);
+      const u4 v = __builtin_bit_cast(u4, acc[j]);
+      if (sys) __builtin_amdgcn_raw_buffer_store_b128(v, rp, off, 0, kAuxSys);
+      else __builtin_amdgcn_raw_buffer_store_b128(v, rp, off, 0, 0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wavefront's stores have reached L2 / memory
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t old;
+    if (sys) old = __hip_atomic_fetch_add(&cnt[nb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    else old = __hip_atomic_fetch_add(&cnt[nb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = old == (uint32_t)(ksl - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+
+  // ---- 6. last k-slice to arrive: sum in k-slice order, bias, fp16 ----------
+  for (int it = tid; it < M * (DK_NB / 4); it += 256) {
+    const int m = it / (DK_NB / 4);
+    const int n = nbg * DK_NB + 4 * (it % (DK_NB / 4));
+    if (n >= N) continue;
+    f4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int k2 = 0; k2 < ksl; ++k2) {
+      const int off = (int)((((size_t)k2 * M + m) * N + n) * 4);
+      const u4 v = sys ? __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kAuxSys)
+                       : __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kAuxL2);
+      s = k2 == 0 ? __builtin_bit_cast(f4, v) : s + __builtin_bit_cast(f4, v);
+    }
+    store_y(m, n, s);
+  }
+  if (tid == 0) {
+    if (sys) __hip_atomic_store(&cnt[nb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    else __hip_atomic_store(&cnt[nb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Reads the XCC id of the XCD each workgroup runs on (hardware register 20,
+// bits 0..3).
+__global__ void xcc_probe_kernel(uint32_t* out) {
+  if (threadIdx.x == 0) out[blockIdx.x] = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xFu;
+}
+
+// Whether workgroup b runs on the XCD of every other workgroup with the same
+// b % 8 and the eight classes use eight XCDs (the round-robin dispatch the
+// kernel relies on), decided once per device.
+bool xcd_dispatch_is_round_robin() {
+  static std::mutex mu;
+  static int known[64];
+  static bool value[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  if (known[dev]) return value[dev];
+  constexpr int kBlocks = 4096;
+  bool ok = false;
+  uint32_t* d_out = nullptr;
+  if (hipMalloc(&d_out, kBlocks * sizeof(uint32_t)) == hipSuccess) {
+    std::vector<uint32_t> h(kBlocks, 0xFFFFFFFFu);
+    hipLaunchKernelGGL(xcc_probe_kernel, dim3(kBlocks), dim3(64), 0, 0, d_out);
+    if (hipGetLastError() == hipSuccess &&
+        hipMemcpy(h.data(), d_out, kBlocks * sizeof(uint32_t), hipMemcpyDeviceToHost) == hipSuccess) {
+      ok = true;
+      uint32_t seen = 0;
+      for (int b = 0; b < kBlocks; ++b) {
+        if (h[b] != h[b & 7]) ok = false;
+        if (h[b] < 32) seen |= 1u << h[b];
+        else ok = false;
+      }
+      if (__builtin_popcount(seen) != 8) ok = false;
+    }
+    (void)hipFree(d_out);
+  }
+  (void)hipGetLastError();
+  known[dev] = 1;
+  value[dev] = ok;
+  return ok;
+}
+
+template <bool ROT, int KMAX, bool KEXACT, bool FAST, int T>
+hipError_t launch_t(const uint16_t* x, const uint8_t* qw, const uint16_t* sc, const uint8_t* zr,
+                    const uint16_t* bias, uint16_t* y, int M, int N, int d,
+                    const paro_rotation* r, void* ws, hipStream_t stream) {
+  const int ksl = (d / 128 + DK_SEGS - 1) / DK_SEGS;
+  const int nbl_all = (N + DK_NB - 1) / DK_NB;
+  uint32_t* cnt = (uint32_t*)ws;
+  float* part = (float*)((char*)ws + kDecodeCounterBytes);
+  const uint32_t* tab = r ? r->d_table : nullptr;
+  const int K = r ? r->K : 0;
+  constexpr int kMaxNb = (int)(kDecodeCounterBytes / 4);
+  const int sys = ksl > 1 && !xcd_dispatch_is_round_robin();
+  for (int nb0 = 0; nb0 < nbl_all; nb0 += kMaxNb) {
+    const int nbl = min(kMaxNb, nbl_all - nb0);
+    const unsigned blocks = 8u * (unsigned)ksl * (unsigned)((nbl + 7) / 8);
+    hipLaunchKernelGGL((w4_decode_kernel<ROT, KMAX, KEXACT, FAST, T>), dim3(blocks), dim3(256), 0,
+                       stream, x, qw, sc, zr, bias, y, M, N, d, tab, K, part, cnt, ksl, nbl, nb0,
+                       sys);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int T>
+hipError_t launch_plan(const uint16_t* x, const uint8_t* qw, const uint16_t* sc, const uint8_t* zr,
+                       const uint16_t* bias, uint16_t* y, int m, int n, int k,
+                       const paro_rotation* r, void* ws, hipStream_t stream) {
+  if (!r) return launch_t<false, 0, true, true, T>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
+  if (r->K == 0) return launch_t<true, 0, true, true, T>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
+  if (r->lay.fast) {
+    if (r->K == 8) return launch_t<true, 8, true, true, T>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
+    return launch_t<true, 8, false, true, T>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
+  }
+  return launch_t<true, 8, false, false, T>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
+}
+
+}  // namespace
+
+bool decode_fuses_rotation(const paro_rotation* r) {
+  return r == nullptr || (r->lay.ppl == 1 && r->K <= 8);
+}
+
+hipError_t launch_w4_decode(const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
+                            const uint8_t* zeros, const uint16_t* bias, uint16_t* y, int64_t M,
+                            int64_t N, int64_t d, const paro_rotation* r, void* ws,
+                            hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const int m = (int)M, n = (int)N, k = (int)d;
+  if (M <= 4) return launch_plan<4>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream);
+  return launch_plan<16>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream);
+}
+
+}  // namespace paro

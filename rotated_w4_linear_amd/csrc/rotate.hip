@@ -19,45 +19,30 @@
 // and token, the loads one batch ahead of the arithmetic; the schedule tables
 // are read once per wavefront.
 #include <cstring>
-#include <type_traits>
 
 #include "paro_internal.h"
+#include "rotate_core.h"
 
 namespace paro {
 namespace {
 
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+using rot::f4;
 
 // Word 3 of a gfx9 buffer resource: 32-bit data format, no swizzle.
 constexpr int kRsrcWord3 = 0x00020000;
 
-__device__ __forceinline__ float half_lo(uint32_t v) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
-}
-__device__ __forceinline__ float half_hi(uint32_t v) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
-}
-__device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
-
-// PPL: pairs per lane (1: 128-channel segments, 2: 256-channel segments).
-// KMAX: compile-time number of stages; with KEXACT the runtime K equals KMAX
-//   (straight-line code), otherwise K <= KMAX and stages past K are skipped.
-// FAST: factored two-FMA stage form (else the general 2x2 form).
-// T: tokens per batch (a multiple of 4: one LDS quad holds 4 tokens).
+// PPL, KMAX, KEXACT, FAST: see rot::Lane. T: tokens per batch (a multiple of
+// 4: one LDS quad holds 4 tokens). A wavefront owns segment gw % segs of the
+// token chunk gw / segs (tpw tokens).
 template <int PPL, int KMAX, bool KEXACT, bool FAST, int T>
 __global__ __launch_bounds__(256) void rotate_kernel(const uint16_t* x, uint16_t* y,
                                                      const uint32_t* __restrict__ tab, int M,
                                                      int64_t row, int segs, int K, int tpw) {
-  constexpr int NV = 64 * PPL;             // virtual lanes (pairs) per segment
-  constexpr int SEG = 2 * NV;              // channels per segment
-  constexpr int NQ = T / 4;                // 4-token LDS quads per batch
-  constexpr int C = FAST ? 2 : 4;          // coefficients per stage
-  constexpr bool TREG = KMAX <= 8;         // keep the whole schedule in VGPRs
-  constexpr int KR = TREG ? KMAX : 0;
-  __shared__ f4 lds_all[4][NQ * NV];
+  using L = rot::Lane<PPL, KMAX, KEXACT, FAST>;
+  constexpr int NV = L::NV;
+  constexpr int SEG = 2 * NV;  // channels per segment
+  __shared__ f4 lds_all[4][T / 4 * NV];
 
-  if constexpr (KEXACT) K = KMAX;
   const int lane = threadIdx.x & 63;
   // wave-uniform: keeps the token and address arithmetic in scalar registers
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -67,52 +52,10 @@ __global__ __launch_bounds__(256) void rotate_kernel(const uint16_t* x, uint16_t
   if (tok0l >= M) return;
   const int tok0 = (int)tok0l;
   const int tok1 = (tok0 + tpw < M) ? tok0 + tpw : M;
-  const int W = 1 + 2 * (K + 1) + C * K + 4;
-  const uint32_t* tb = tab + (size_t)seg * W * NV + lane;
   char* lds = (char*)&lds_all[wid][0];
-  const int ff = 3 + 2 * K + C * K;
 
-  uint32_t ldsel[PPL], stoff[PPL], stsel[PPL];
-  float lamX[PPL], lamB[PPL];
-  uint32_t wr[KR + 1][PPL], rd[KR + 1][PPL];
-  float cf[KR > 0 ? KR : 1][C][PPL];
-#pragma unroll
-  for (int h = 0; h < PPL; ++h) {
-    ldsel[h] = tb[64 * h];
-    lamX[h] = as_f(tb[(size_t)(ff + 0) * NV + 64 * h]);
-    lamB[h] = as_f(tb[(size_t)(ff + 1) * NV + 64 * h]);
-    stoff[h] = tb[(size_t)(ff + 2) * NV + 64 * h];
-    stsel[h] = tb[(size_t)(ff + 3) * NV + 64 * h];
-    if constexpr (TREG) {
-#pragma unroll
-      for (int tau = 0; tau <= KR; ++tau) {
-        if (KEXACT || tau <= K) {
-          wr[tau][h] = tb[(size_t)(1 + 2 * tau) * NV + 64 * h];
-          rd[tau][h] = tb[(size_t)(2 + 2 * tau) * NV + 64 * h];
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < KR; ++t) {
-        if (KEXACT || t < K) {
-#pragma unroll
-          for (int e = 0; e < C; ++e) cf[t][e][h] = as_f(tb[(size_t)(3 + 2 * K + C * t + e) * NV + 64 * h]);
-        }
-      }
-    }
-  }
-
-  auto wr_off = [&](int tau, int h) -> uint32_t {
-    if constexpr (TREG) return wr[tau][h];
-    else return tb[(size_t)(1 + 2 * tau) * NV + 64 * h];
-  };
-  auto rd_off = [&](int tau, int h) -> uint32_t {
-    if constexpr (TREG) return rd[tau][h];
-    else return tb[(size_t)(2 + 2 * tau) * NV + 64 * h];
-  };
-  auto coef = [&](int t, int e, int h) -> float {
-    if constexpr (TREG) return cf[t][e][h];
-    else return as_f(tb[(size_t)(3 + 2 * K + C * t + e) * NV + 64 * h]);
-  };
+  L sch;
+  sch.load(tab, seg, K, lane);
 
   const uint16_t* xseg = x + (int64_t)seg * SEG;
   uint16_t* yseg = y + (int64_t)seg * SEG;
@@ -138,90 +81,27 @@ __global__ __launch_bounds__(256) void rotate_kernel(const uint16_t* x, uint16_t
     }
   };
 
-  // Rotates the batch at t0 held in cur, then refills cur with the batch at tn.
-  auto process = [&](int t0, Raw& cur, int tn) {
+  load(tok0, raw);
+  for (int t0 = tok0; t0 < tok1; t0 += T) {
     float X[PPL][T], B[PPL][T];
-
-    auto exchange = [&](int tau) {
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) {
+    for (int i = 0; i < T; ++i)
 #pragma unroll
-        for (int h = 0; h < PPL; ++h) {
-          f4 v = {B[h][4 * q], B[h][4 * q + 1], B[h][4 * q + 2], B[h][4 * q + 3]};
-          *(f4*)(lds + q * NV * 16 + wr_off(tau, h)) = v;
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-#pragma unroll
-        for (int h = 0; h < PPL; ++h) {
-          f4 v = *(const f4*)(lds + q * NV * 16 + rd_off(tau, h));
-          B[h][4 * q] = v.x;
-          B[h][4 * q + 1] = v.y;
-          B[h][4 * q + 2] = v.z;
-          B[h][4 * q + 3] = v.w;
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-
-    // ---- unpack the current batch, start loading the next one -----------------
-#pragma unroll
-    for (int i = 0; i < T; ++i) {
-#pragma unroll
-      for (int h = 0; h < PPL; ++h) {
-        const uint32_t v = __builtin_amdgcn_perm(cur[h][i], cur[h][i], ldsel[h]);
-        X[h][i] = half_lo(v);
-        B[h][i] = half_hi(v);
-      }
-    }
-    load(tn, cur);
-    // ---- stages and exchanges -------------------------------------------------
-    if constexpr (KMAX > 0) {
-      exchange(0);
-#pragma unroll
-      for (int t = 0; t < KMAX; ++t) {
-        if (KEXACT || t < K) {
-#pragma unroll
-          for (int h = 0; h < PPL; ++h) {
-#pragma unroll
-            for (int i = 0; i < T; ++i) {
-              const float a = X[h][i], b = B[h][i];
-              if constexpr (FAST) {
-                B[h][i] = __builtin_fmaf(coef(t, 1, h), a, b);
-                X[h][i] = __builtin_fmaf(coef(t, 0, h), b, a);
-              } else {
-                B[h][i] = __builtin_fmaf(coef(t, 2, h), a, coef(t, 3, h) * b);
-                X[h][i] = __builtin_fmaf(coef(t, 1, h), b, coef(t, 0, h) * a);
-              }
-            }
-          }
-          exchange(t + 1);
-        }
-      }
-    }
-    // ---- deferred scales, fp16 rounding, store --------------------------------
+      for (int h = 0; h < PPL; ++h) sch.unpack(raw[h][i], h, X[h][i], B[h][i]);
+    load(t0 + T, raw);
+    sch.template run<T>(X, B, lds);
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(yseg + (int64_t)t0 * row), (short)0, 0x7fffffff, kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < T; ++i) {
       if (t0 + i < tok1) {
 #pragma unroll
-        for (int h = 0; h < PPL; ++h) {
-          const h2 pk = {(_Float16)(X[h][i] * lamX[h]), (_Float16)(B[h][i] * lamB[h])};
-          const uint32_t u = __builtin_bit_cast(uint32_t, pk);
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_perm(u, u, stsel[h]), rs, stoff[h],
+        for (int h = 0; h < PPL; ++h)
+          __builtin_amdgcn_raw_buffer_store_b32(sch.pack(X[h][i], B[h][i], h), rs, sch.stoff[h],
                                                 i * rowb, 0);
-        }
       }
     }
-  };
-
-  load(tok0, raw);
-  for (int t0 = tok0; t0 < tok1; t0 += T) process(t0, raw, t0 + T);
+  }
 }
 
 // Tokens per wavefront: enough wavefronts to fill the chip (target_waves), a

@@ -1,123 +1,21 @@
-// gfx950 kernels for the W4G128 linear layer on rotated activations:
+// gfx950 kernel for the W4G128 linear layer on rotated activations with
+// many tokens (prefill, M > 16):
 //   Y[m][n] = sum_k X'[m][k] (q[n][k] - z[n][k/128]) s[n][k/128] + b[n]
 // (CSDN article section 2.1: Y = (X T^-1)(T W) + b; paper notes "主实验":
-// 4-bit weights, group 128).
-//
-// Both kernels use the gfx950 MFMA v_mfma_f32_16x16x32_f16 with the
-// dequantized weights as operand A (16 output channels x 32 k) and the
-// activations as operand B (32 k x 16 tokens), so each lane's accumulator
-// holds four consecutive output channels of one token and the epilogue stores
-// 8 bytes per lane. Dequantization: two nibbles are spread into the mantissas
-// of two fp16 1024.0 values with v_perm, (1024 + q) - (1024 + z) = q - z is
-// exact in packed fp16, and one packed multiply by the fp16 scale rounds once.
-//
-//  * decode (M <= 16): weight streaming. A workgroup owns 16 output channels
-//    and all of d; its four wavefronts split d, each lane streams 16 bytes of
-//    packed weights per group, and the partial 16x16 tiles are summed through
-//    LDS. Rows of X' beyond M are zero operands.
-//  * prefill (M > 16): a 128x128 output tile per workgroup, k-tiles of 64
-//    staged through double-buffered, padded LDS (conflict-free 16-byte
-//    reads), weights dequantized once per tile on the way into LDS.
+// 4-bit weights, group 128). Here the layer is a dense contraction and runs
+// on the matrix cores. Dequantization: two nibbles are spread into the
+// mantissas of two fp16 1024.0 values with v_perm, (1024 + q) - (1024 + z) =
+// q - z is exact in packed fp16, and one packed multiply by the fp16 scale
+// rounds once.
 #include "paro_internal.h"
+#include "w4_common.h"
 
 #pragma clang fp contract(off)
 
 namespace paro {
 namespace {
 
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-
-// Eight 4-bit codes (k0 in bits 0..3, ..., k7 in bits 28..31) -> eight fp16
-// values (q - z) * s in k order.
-__device__ __forceinline__ h8 dequant8(uint32_t w, h2 zz, h2 ss) {
-  const uint32_t lo = w & 0x0F0F0F0Fu;         // q0 q2 q4 q6 (one per byte)
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // q1 q3 q5 q7
-  uint32_t p[4];
-  p[0] = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x64006400u;
-  p[1] = __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x64006400u;
-  p[2] = __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x64006400u;
-  p[3] = __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x64006400u;
-  h8 out;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    h2 v = __builtin_bit_cast(h2, p[i]);
-    v = (v - zz) * ss;
-    out[2 * i] = v.x;
-    out[2 * i + 1] = v.y;
-  }
-  return out;
-}
-
-__device__ __forceinline__ h2 splat2(_Float16 v) { return h2{v, v}; }
-__device__ __forceinline__ float half_lo(uint32_t v) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
-}
-__device__ __forceinline__ float half_hi(uint32_t v) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
-}
-__device__ __forceinline__ uint32_t half_bits(float f) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
-}
-
-// --------------------------------------------------------------------------
-// decode: M <= 16
-// --------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void w4_gemv_kernel(const uint16_t* __restrict__ x,
-                                                      const uint8_t* __restrict__ qw,
-                                                      const uint16_t* __restrict__ sc,
-                                                      const uint8_t* __restrict__ zr,
-                                                      const uint16_t* __restrict__ bias,
-                                                      uint16_t* __restrict__ y, int M, int N, int d) {
-  __shared__ f4 red[4][64];
-  const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  const int n0 = blockIdx.x * 16;
-  const int groups = d >> 7;
-  const int gpw = (groups + 3) >> 2;
-  const int g0 = wid * gpw;
-  const int g1 = min(groups, g0 + gpw);
-  const int n = n0 + (lane & 15);
-  const int kq = lane >> 4;
-  const int m = lane & 15;
-  const uint8_t* wrow = qw + (size_t)n * (d >> 1) + kq * 16;
-  const uint16_t* xrow = x + (size_t)m * d + kq * 32;
-  f4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int g = g0; g < g1; ++g) {
-    const u4 wv = *(const u4*)(wrow + (size_t)g * 64);
-    const _Float16 s = __builtin_bit_cast(_Float16, sc[(size_t)n * groups + g]);
-    const _Float16 zf = (_Float16)(1024.0f + (float)zr[(size_t)n * groups + g]);
-    const h2 ss = splat2(s), zz = splat2(zf);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const h8 a = dequant8(wv[i], zz, ss);
-      h8 b = {};
-      if (m < M) b = *(const h8*)(xrow + (size_t)g * 128 + 8 * i);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
-    }
-  }
-  red[wid][lane] = acc;
-  __syncthreads();
-  if (wid == 0) {
-    f4 t = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
-    if (m < M) {
-      const int nb = n0 + 4 * kq;
-      uint16_t o[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float v = t[e];
-        if (bias) v += (float)__builtin_bit_cast(_Float16, bias[nb + e]);
-        o[e] = __builtin_bit_cast(uint16_t, (_Float16)v);
-      }
-      uint2 pk;
-      pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
-      pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
-      *(uint2*)(y + (size_t)m * N + nb) = pk;
-    }
-  }
-}
+using namespace w4;
 
 // --------------------------------------------------------------------------
 // prefill (M > 16): MFMA v_mfma_f32_32x32x16_f16 with the dequantized weights
@@ -346,15 +244,10 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_w4_linear(const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
-                            const uint8_t* zeros, const uint16_t* bias, uint16_t* y, int64_t M,
-                            int64_t N, int64_t d, hipStream_t stream) {
+hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
+                          const uint8_t* zeros, const uint16_t* bias, uint16_t* y, int64_t M,
+                          int64_t N, int64_t d, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  if (M <= 16) {
-    hipLaunchKernelGGL(w4_gemv_kernel, dim3((unsigned)(N / 16)), dim3(256), 0, stream, x, qweight,
-                       scales, zeros, bias, y, (int)M, (int)N, (int)d);
-    return hipGetLastError();
-  }
   const int nblk = (int)((N + GB_N - 1) / GB_N);
   const int mblk = (int)((M + GB_M - 1) / GB_M);
   const int64_t tiles = (int64_t)nblk * mblk;

@@ -291,7 +291,108 @@ def test_linear_workspace_errors(paro):
     with pytest.raises(paro.ParoError) as e:
         paro.paro_w4_linear(r, dev(x), qw, s, z, workspace=small)
     assert e.value.status == -7
-    assert paro.paro_w4_linear_workspace_size(r, 8, 256) >= 8 * 256 * 2
+    assert paro.paro_w4_linear_workspace_size(r, 8, 32, 256) >= 16384
+    assert paro.paro_w4_linear_workspace_size(r, 17, 32, 256) >= 16384 + 17 * 256 * 2
+
+
+# ----------------------------------------------------------------------------
+# small batches (M <= 16): one kernel, transform fused in, split over k
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,d,N", [(1, 640, 400), (16, 640, 400), (5, 384, 48), (2, 4096, 4096),
+                                   (16, 14336, 256), (11, 1152, 1040), (1, 128, 16)])
+def test_decode_fused_equals_rotate_then_plain(paro, M, d, N):
+    """The fused transform yields the X' bits paro_rotate yields and the k-split
+    sum order does not depend on where X' came from: equal outputs bit for bit."""
+    log(f"decode fused vs separate M={M} d={d} N={N}")
+    x, layer, b = synthetic.linear_case(seed=40 + M + d, M=M, d=d, N=N)
+    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, 128)
+    qw, s, z = paro.paro_quantize_weights(r, dev(layer.w), 128)
+    xd = dev(x)
+    y_fused = host(paro.paro_w4_linear(r, xd, qw, s, z, dev(b)))
+    y_sep = host(paro.paro_w4_linear(None, paro.paro_rotate(r, xd), qw, s, z, dev(b)))
+    assert np.array_equal(y_fused.view(np.uint16), y_sep.view(np.uint16))
+    ref = oracle.rotated_w4_linear(x, host(qw), host(s), host(z), 128, layer.pairs, layer.theta,
+                                   layer.alpha, b)
+    metrics.assert_linear_close(y_fused, ref)
+
+
+@pytest.mark.parametrize("K", [12, 32, 0, 3])
+def test_decode_other_stage_counts(paro, K):
+    """K > 8 rotates into the workspace first; K = 0 and K < 8 run fused."""
+    log(f"decode plan K={K}")
+    x, layer, b = synthetic.linear_case(seed=60 + K, M=7, d=1024, N=272, K=K)
+    check_linear(paro, x, layer, bias=b)
+
+
+@pytest.mark.parametrize("group", [64, 256])
+def test_linear_rejects_other_rotation_groups(paro, group):
+    x, layer, b = synthetic.linear_case(seed=65, M=3, d=512, N=32, group=group)
+    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, group)
+    qw, s, z = paro.paro_quantize_weights(None, dev(layer.w), 128)
+    with pytest.raises(paro.ParoError) as e:
+        paro.paro_w4_linear(r, dev(x), qw, s, z)
+    assert e.value.status == -2
+
+
+def test_decode_general_form(paro):
+    log("decode with theta=0 pairs (general 2x2 form, fused)")
+    x, layer, b = synthetic.linear_case(seed=71, M=6, d=768, N=144)
+    layer.theta[:, ::3] = 0.0
+    _, lay = paro.paro_rotation_plan_host(layer.pairs, layer.theta, layer.alpha, 128)
+    assert not lay["fast"]
+    check_linear(paro, x, layer, bias=b)
+
+
+def test_decode_workspace_reuse(paro):
+    """The arrival counters return to zero: repeated calls, and calls of other
+    sizes, on one workspace give identical results."""
+    log("decode workspace reuse")
+    cases = [synthetic.linear_case(seed=80 + i, M=M, d=d, N=N)
+             for i, (M, d, N) in enumerate([(16, 640, 400), (1, 4096, 4096), (3, 1024, 96)])]
+    need = 0
+    prepared = []
+    for x, layer, b in cases:
+        r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, 128)
+        qw, s, z = paro.paro_quantize_weights(r, dev(layer.w), 128)
+        prepared.append((r, dev(x), qw, s, z, dev(b)))
+        need = max(need, paro.paro_w4_linear_workspace_size(r, x.shape[0], qw.shape[0], x.shape[1]))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    first = [host(paro.paro_w4_linear(*p[:5], p[5], workspace=ws)) for p in prepared]
+    again = [host(paro.paro_w4_linear(*p[:5], p[5], workspace=ws)) for p in reversed(prepared)][::-1]
+    for a, c in zip(first, again):
+        assert np.array_equal(a.view(np.uint16), c.view(np.uint16))
+    counters = host(ws[:16384].view(torch.int32))
+    assert not counters.any()
+    for (x, layer, b), y, p in zip(cases, first, prepared):
+        ref = oracle.rotated_w4_linear(x, host(p[2]), host(p[3]), host(p[4]), 128, layer.pairs,
+                                       layer.theta, layer.alpha, b)
+        metrics.assert_linear_close(y, ref)
+
+
+@pytest.mark.slow
+def test_decode_more_n_blocks_than_counters(paro):
+    """N = 4096 * 128 + 128 output channels: more n-blocks than the 4096
+    arrival counters, so the launch is split; sampled channels of both parts."""
+    M, d, N = 2, 640, 4096 * 128 + 128
+    log(f"decode M={M} d={d} N={N} (split launch)")
+    rng = synthetic.rng_for(3600, 0)
+    x = synthetic.draw_x(rng, M, d, synthetic.n_outliers(d), 20.0)
+    pairs, theta, alpha = synthetic.draw_rotation(rng, d, 128, 8)
+    w = (rng.standard_normal((N, d), dtype=np.float32) * np.float32(0.02)).astype(np.float16)
+    b = synthetic.draw_bias(rng, N)
+    r = paro.Rotation(pairs, theta, alpha, 128)
+    wd = dev(w)
+    del w
+    qw, s, z = paro.paro_quantize_weights(r, wd, 128)
+    del wd
+    y = host(paro.paro_w4_linear(r, dev(x), qw, s, z, dev(b)))
+    cols = np.concatenate([np.arange(0, 32), np.arange(N - 160, N),
+                           np.sort(rng.choice(N, 64, replace=False))])
+    ci = torch.from_numpy(cols).cuda()
+    ref = oracle.rotated_w4_linear(x, host(qw[ci]), host(s[ci]), host(z[ci]), 128, pairs, theta,
+                                   alpha, b[cols])
+    metrics.assert_linear_close(y[:, cols], ref)
 
 
 def test_linear_prefill_mlp_sampled(paro):

@@ -117,7 +117,12 @@ def test_hot_calls_validate_before_any_launch(paro):
     assert lib.paro_quantize_weights(None, dummy, 8, 256, 96, dummy, dummy, dummy, None) == -6
     assert lib.paro_quantize_weights(None, dummy, 8, 200, 128, dummy, dummy, dummy, None) == -2
     assert lib.paro_quantize_weights(None, None, 8, 256, 128, dummy, dummy, dummy, None) == -1
-    assert lib.paro_w4_linear_workspace_size(None, 16, 4096) == 0
+    # workspace: none for plain large-batch calls; counters + fp32 partial sums
+    # [ceil(d / 512)][M][N] for small batches; + X' for rotated large batches
+    assert lib.paro_w4_linear_workspace_size(None, 17, 64, 4096) == 0
+    assert lib.paro_w4_linear_workspace_size(None, 16, 64, 4096) == 16384 + 8 * 16 * 64 * 4
+    assert lib.paro_w4_linear_workspace_size(None, 1, 64, 512) == 16384
+    assert lib.paro_w4_linear_workspace_size(None, 0, 64, 512) == 0
     lib.paro_rotation_destroy(None)  # no-op
 
 
