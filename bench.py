@@ -47,9 +47,13 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def source_sha(path):
-    with open(os.path.join(ROOT, path), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_sha(paths):
+    """Hash of the kernel's source files (one path or a list, in order)."""
+    h = hashlib.sha256()
+    for path in ([paths] if isinstance(paths, str) else paths):
+        with open(os.path.join(ROOT, path), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(kernel_key):
@@ -246,7 +250,8 @@ def bench_decode(args, paro, torch):
     res = {}
     total_ms = 0.0
     total_flops = 0.0
-    for M in (1, 4, 16):
+    ms = [int(v) for v in args.decode_m.split(",")]
+    for M in ms:
         x = torch.from_numpy(synthetic.decode_x(M)).cuda()
         y = torch.empty((M, N), dtype=torch.float16, device="cuda")
         ws = paro.new_workspace(r, M, N, d)
@@ -284,16 +289,18 @@ def bench_decode(args, paro, torch):
         }
         total_ms += timing["rot"]
         total_flops += 2.0 * M * N * d
-    g1 = res["M1"]["rotated_gbps"]
+    g1 = res[f"M{ms[0]}"]["rotated_gbps"]
     return {
         "metric": METRIC, "value": round(total_flops / (total_ms * 1e-3) / 1e12, 4), "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(total_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": "decode_q_proj_4096x4096_M1_4_16", "group": 128, "stages_K": 8},
+        "config": {"workload": "decode_q_proj_4096x4096_M" + "_".join(map(str, ms)), "group": 128,
+                   "stages_K": 8, "roofline_at_M": ms[0]},
         "decode": res,
         "roofline": {"bound": "hbm", "achieved": g1, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(g1 / HBM_PEAK_GBPS, 4), "traffic": traffic_for("w4_decode:decode_M1")},
+                     "frac": round(g1 / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_for(f"w4_decode:decode_M{ms[0]}")},
     }
 
 
@@ -367,6 +374,7 @@ def main():
     ap.add_argument("--workload", default="prefill_mlp",
                     choices=["prefill_mlp", "prefill_down", "decode", "sweep", "tiny", "copy"])
     ap.add_argument("--ring", type=int, default=0, help="distinct input copies cycled (0 = auto)")
+    ap.add_argument("--decode-m", default="1,4,16", help="token counts of the decode workload")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
