@@ -23,19 +23,26 @@ using namespace w4;
 // tokens). A wavefront owns a 64 (n) x 128 (m) tile: 2 x 4 accumulator tiles,
 // 128 fp32 per lane, so two wavefronts fit on a SIMD and one's dequantization
 // overlaps the other's MFMAs. A group of four wavefronts shares a 128 (m) x
-// 256 (n) workgroup tile through double-buffered LDS:
+// 256 (n) workgroup tile.
+//
+// Staging: every operand of a k-tile of 64 (X' tile, packed codes, the
+// tile's group scale and zero of each row) goes from global memory straight
+// into LDS with load-to-LDS DMA (16 bytes per lane for X' and codes), into
+// two stages: the DMA of k-tile kt + 1 runs while k-tile kt is multiplied,
+// and nothing is staged through registers. Each stage is its own LDS object,
+// so the compiler sees that the stage being filled never aliases the one
+// being read; the kernel waits for the DMA counter itself (s_waitcnt) before
+// the one barrier per k-tile.
 //  * X' tile [128 rows][8 chunks of 8 halfs]; chunk c of row r stored at
 //    position c ^ ((r >> 1) & 7);
 //  * packed int4 weight tile [256 rows][2 halves of 16 bytes]; half h of row r
 //    at position h ^ ((r >> 3) & 1).
 // A gfx950 16-byte LDS read is conflict-free when every 16 consecutive lanes
-// address positions distinct modulo 16, a 16-byte write when every 8 consecutive
-// lanes do modulo 8: the operand reads take 16 consecutive rows at a fixed
-// chunk, which these swizzles spread over all 16 positions, and the staging
-// writes are lane-contiguous. Global loads are staged through registers one
-// k-tile ahead of the LDS buffer being written, so every load has a whole
-// multiply phase to land before its data is needed. Each
-// wavefront dequantizes its own 64 rows in registers.
+// address positions distinct modulo 16: the operand reads take 16 consecutive
+// rows at a fixed chunk, which these swizzles spread over all 16 positions.
+// DMA writes land lane-contiguously, so the swizzle is applied by choosing
+// which source chunk each lane fetches. Each wavefront dequantizes its own 64
+// rows in registers.
 // With KS = 2 two groups of four wavefronts split k in halves inside the
 // workgroup (for layers with few output tiles) and add their accumulators
 // through LDS at the end.
@@ -46,10 +53,14 @@ using namespace w4;
 // k = 8 i + {0..7, 32..39}, and X' is read with the same mapping.
 // --------------------------------------------------------------------------
 typedef float f16v __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int GB_M = 128, GB_N = 256, GB_K = 64;
-constexpr int GB_XSTAGE = GB_M * GB_K;  // halfs per X' buffer (16 KB)
-constexpr int GB_WSTAGE = GB_N * 2;     // 16-byte chunks per weight buffer (8 KB)
+constexpr int GB_XSTAGE = GB_M * GB_K;  // halfs per X' stage (16 KB)
+constexpr int GB_WSTAGE = GB_N * 2;     // 16-byte chunks per weight stage (8 KB)
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 buffer resource word 3
+// s_waitcnt immediate (gfx9 encoding): vmcnt(0) lgkmcnt(0), expcnt untouched
+constexpr int kWaitVmLgkm0 = 0x70;
 
 template <int KS>
 __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -57,22 +68,23 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
                     const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zr,
                     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N,
                     int d, int mblk, int nblk) {
-  __shared__ __attribute__((aligned(1024))) _Float16 Xl[KS][2][GB_XSTAGE];
-  __shared__ __attribute__((aligned(1024))) u4 Wl[KS][2][GB_WSTAGE];
+  __shared__ __attribute__((aligned(1024))) _Float16 X0[KS][GB_XSTAGE], X1[KS][GB_XSTAGE];
+  __shared__ __attribute__((aligned(1024))) u4 W0[KS][GB_WSTAGE], W1[KS][GB_WSTAGE];
+  __shared__ __attribute__((aligned(16))) uint32_t S0[KS][GB_N], S1[KS][GB_N];
+  __shared__ __attribute__((aligned(16))) uint32_t Z0[KS][GB_N], Z1[KS][GB_N];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int kg = tid >> 8;          // k half (KS = 2)
-  const int w = (tid >> 6) & 3;     // wavefront inside the group
+  const int kg = __builtin_amdgcn_readfirstlane(tid >> 8);     // k half (KS = 2)
+  const int w = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // wavefront inside the group
   // XCD-aware tile order: workgroup b runs on XCD b % 8. XCD x owns the
-  // n-blocks [x nbp, (x + 1) nbp) and walks them in super-blocks of 8 m-blocks
-  // x all its n-blocks, so the ~64 workgroups resident on one XCD share both
-  // their X' and their weight k-tiles through its L2.
-  const int nbp = (nblk + 7) >> 3;
+  // n-blocks x, x + 8, ... and walks them in super-blocks of 8 m-blocks x all
+  // its n-blocks, so the workgroups resident on one XCD share both their X'
+  // and their weight k-tiles through its L2.
   const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
-  const int nbx = min(nbp, nblk - xcd * nbp);
+  const int nbx = (nblk - xcd + 7) >> 3;
   if (nbx <= 0) return;
   const int mg = idx / (8 * nbx), rem = idx - mg * 8 * nbx;
-  const int nb = xcd * nbp + rem / 8;
+  const int nb = xcd + 8 * (rem / 8);
   const int mb = mg * 8 + (rem & 7);
   if (mb >= mblk) return;
   const int m0 = mb * GB_M;
@@ -83,59 +95,50 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
   const int kt0 = kg * KT;
   const int l32 = lane & 31, g = lane >> 5;
 
-  // scales / zeros of the lane's rows n0 + 32 j + l32 (rows past N: zero scale)
-  uint32_t soff[2];
-  bool wok[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + 32 * j + l32;
-    wok[j] = n < N;
-    soff[j] = (uint32_t)(wok[j] ? n : N - 1) * (uint32_t)groups;
-  }
-  // X' staging: chunk c of wavefront w covers tile rows 8 (4 w + c) .. + 7; the
-  // lane at position l % 8 of row l / 8 carries the source chunk (l % 8) ^ swizzle
+  // Buffer resources based at this tile's first row (byte offsets < 2^31,
+  // checked on the host); rows past M or N are clamped to the last row.
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(x + (size_t)m0 * d), (short)0, min(M - m0, GB_M) * d * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(qw + (size_t)nw0 * (d >> 1)), (short)0, min(N - nw0, GB_N) * (d >> 1), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(sc + (size_t)nw0 * groups), (short)0, min(N - nw0, GB_N) * groups * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(zr + (size_t)nw0 * groups), (short)0, min(N - nw0, GB_N) * groups, kRsrcWord3);
+  // X' DMA c of wavefront w fills tile rows 8 (4 w + c) .. + 7; the lane at
+  // position l % 8 of row l / 8 fetches the source chunk (l % 8) ^ swizzle
   uint32_t xoff[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int r = 8 * (4 * w + c) + (lane >> 3);
-    const int row = min(m0 + r, M - 1);  // rows past M are never stored
-    xoff[c] = (uint32_t)row * (uint32_t)d + 8u * ((lane & 7) ^ ((r >> 1) & 7));
+    const int row = min(r, M - 1 - m0);
+    xoff[c] = (uint32_t)(row * d + 8 * ((lane & 7) ^ ((r >> 1) & 7))) * 2u;
   }
-  // weight staging: chunk c of wavefront w covers tile rows 32 (2 w + c) .. + 31
+  // code DMA c of wavefront w fills tile rows 32 (2 w + c) .. + 31
   uint32_t woff[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int r = 32 * (2 * w + c) + (lane >> 1);
-    const int row = min(nw0 + r, N - 1);
-    woff[c] = (uint32_t)row * (uint32_t)(d >> 1) + 16u * ((lane & 1) ^ ((r >> 3) & 1));
+    const int row = min(r, N - 1 - nw0);
+    woff[c] = (uint32_t)(row * (d >> 1) + 16 * ((lane & 1) ^ ((r >> 3) & 1)));
   }
+  // group scale and zero: lane l of wavefront w fetches row 64 w + l
+  const uint32_t szrow = (uint32_t)(min(64 * w + lane, N - 1 - nw0) * groups);
 
-  u4 xr[4], wr[2];
-  uint32_t sraw[2], zraw[2];
-  h2 ss[2], zz[2], ss_n[2], zz_n[2];
-  auto load_regs = [&](int kt) {  // k-tile kt of this group's range: X', codes, scales
+  // the DMA of one k-tile: ten load-to-LDS instructions per lane
+  auto dma = [&](int kt, _Float16* xs, u4* ws, uint32_t* ss_l, uint32_t* zs_l) {
     const int kglob = kt0 + kt;
+    const uint32_t gi = (uint32_t)(kglob >> 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)&ss_l[64 * w], 2, (szrow + gi) * 2u, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_void*)&zs_l[64 * w], 1, szrow + gi, 0, 0, 0);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) xr[c] = *(const u4*)(x + xoff[c] + kglob * GB_K);
+    for (int c = 0; c < 4; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)&xs[(4 * w + c) * 64 * 8], 16, xoff[c],
+                                               kglob * GB_K * 2, 0, 0);
 #pragma unroll
-    for (int c = 0; c < 2; ++c) wr[c] = *(const u4*)(qw + woff[c] + kglob * (GB_K / 2));
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      sraw[j] = sc[soff[j] + (kglob >> 1)];
-      zraw[j] = zr[soff[j] + (kglob >> 1)];
-    }
-  };
-  auto store_regs = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) *(u4*)&Xl[kg][buf][((4 * w + c) * 64 + lane) * 8] = xr[c];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) Wl[kg][buf][(2 * w + c) * 64 + lane] = wr[c];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const _Float16 s = wok[j] ? __builtin_bit_cast(_Float16, (uint16_t)sraw[j]) : (_Float16)0.0f;
-      ss_n[j] = splat2(s);
-      zz_n[j] = splat2((_Float16)(1024.0f + (float)zraw[j]));
-    }
+    for (int c = 0; c < 2; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)&ws[(2 * w + c) * 64], 16, woff[c],
+                                               kglob * (GB_K / 2), 0, 0);
   };
 
   f16v acc[2][4];
@@ -146,30 +149,22 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[j][mm][e] = 0.0f;
 
-  // Iteration kt: write the staged k-tile kt + 1 to the buffer last read in
-  // iteration kt - 1 (its loads were issued a whole iteration ago), issue the
-  // loads of k-tile kt + 2, multiply k-tile kt, then one barrier. The loop is
-  // branch-free: past the last tile it writes a buffer nobody reads again and
-  // reloads the last tile.
-  load_regs(0);
-  store_regs(0);
-  load_regs(min(1, KT - 1));
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      ss[j] = ss_n[j];
-      zz[j] = zz_n[j];
-    }
-    store_regs(buf ^ 1);
-    load_regs(min(kt + 2, KT - 1));
-    const _Float16* xb = &Xl[kg][buf][0];
+  // One k-tile from stage (xs, ws, ss_l, zs_l) while the DMA of the next
+  // k-tile fills the other stage, then wait for that DMA and one barrier.
+  // Past the last tile the DMA reloads the last tile into a stage nobody reads.
+  auto step = [&](int kt, const _Float16* xb, const u4* wl, const uint32_t* ss_l,
+                  const uint32_t* zs_l, _Float16* xn, u4* wn, uint32_t* sn, uint32_t* zn) {
+    dma(min(kt + 1, KT - 1), xn, wn, sn, zn);
+    __builtin_amdgcn_sched_barrier(0);
     u4 wf[2];
+    h2 ss[2], zz[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int r = 64 * w + 32 * j + l32;
-      wf[j] = Wl[kg][buf][2 * r + (g ^ ((r >> 3) & 1))];
+      wf[j] = wl[2 * r + (g ^ ((r >> 3) & 1))];
+      const bool ok = nw0 + r < N;
+      ss[j] = splat2(ok ? __builtin_bit_cast(_Float16, (uint16_t)(ss_l[r] & 0xffffu)) : (_Float16)0.0f);
+      zz[j] = splat2((_Float16)(1024.0f + (float)(zs_l[r] & 0xffu)));
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -187,29 +182,42 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
         for (int mm = 0; mm < 4; ++mm)
           acc[j][mm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[j], b[mm], acc[j][mm], 0, 0, 0);
     }
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+    __builtin_amdgcn_s_barrier();
+  };
+
+  dma(0, X0[kg], W0[kg], S0[kg], Z0[kg]);
+  __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+  __builtin_amdgcn_s_barrier();
+  for (int kt = 0; kt < KT; kt += 2) {
+    step(kt, X0[kg], W0[kg], S0[kg], Z0[kg], X1[kg], W1[kg], S1[kg], Z1[kg]);
+    if (kt + 1 < KT) step(kt + 1, X1[kg], W1[kg], S1[kg], Z1[kg], X0[kg], W0[kg], S0[kg], Z0[kg]);
   }
 
   if constexpr (KS == 2) {
-    // the second k half hands its partial sums to the first through LDS, one
-    // 64 KB half of the accumulators at a time
-    float* red = (float*)&Xl[0][0][0];
+    // the second k half hands its partial sums to the first through LDS (the
+    // X' stages 0 of both halves, 32 KB), a quarter of the accumulators at a time
+    float* red = (float*)&X0[0][0];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      if (kg == 1) {
 #pragma unroll
-        for (int mm = 0; mm < 4; ++mm)
+      for (int h = 0; h < 2; ++h) {
+        if (kg == 1) {
 #pragma unroll
-          for (int e = 0; e < 16; ++e) red[((w * 4 + mm) * 16 + e) * 64 + lane] = acc[j][mm][e];
+          for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) red[((w * 2 + mm) * 16 + e) * 64 + lane] = acc[j][2 * h + mm][e];
+        }
+        __syncthreads();
+        if (kg == 0) {
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[j][2 * h + mm][e] += red[((w * 2 + mm) * 16 + e) * 64 + lane];
+        }
+        __syncthreads();
       }
-      __syncthreads();
-      if (kg == 0) {
-#pragma unroll
-        for (int mm = 0; mm < 4; ++mm)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[j][mm][e] += red[((w * 4 + mm) * 16 + e) * 64 + lane];
-      }
-      __syncthreads();
     }
     if (kg == 1) return;
   }
@@ -251,7 +259,7 @@ hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint1
   const int nblk = (int)((N + GB_N - 1) / GB_N);
   const int mblk = (int)((M + GB_M - 1) / GB_M);
   const int64_t tiles = (int64_t)nblk * mblk;
-  // 8 XCDs, each with its n-block range walked in super-blocks of 8 m-blocks
+  // 8 XCDs, each owning every 8th n-block, walked in super-blocks of 8 m-blocks
   const int64_t nbp = (nblk + 7) / 8;
   const int64_t blocks = 8 * nbp * (((int64_t)mblk + 7) / 8) * 8;
   // too few tiles to give every SIMD two wavefronts: split k inside the workgroup
