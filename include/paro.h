@@ -173,7 +173,8 @@ size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t 
  *   group    must be 128 (W4G128); other values return PARO_ERR_UNSUPPORTED.
  *            A plan r must have the same d and group (the pairs stay inside
  *            quantization groups), else PARO_ERR_SHAPE.
- *   N % 16 == 0, d % 128 == 0, M >= 0 (M == 0 is a no-op).
+ *   N % 16 == 0, d % 128 == 0, M >= 0 (M == 0 is a no-op); N <= 2^30,
+ *   d <= 2^22, M < 2^30, else PARO_ERR_UNSUPPORTED.
  *   workspace, workspace_bytes: device memory of at least
  *            paro_w4_linear_workspace_size(r, M, N, d) bytes, 256-byte
  *            aligned (may be NULL when that size is 0). Its first 16 KiB hold

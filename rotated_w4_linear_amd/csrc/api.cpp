@@ -237,8 +237,9 @@ int paro_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qwe
     set_error("paro_w4_linear: N must be a multiple of 16 and d of 128");
     return PARO_ERR_SHAPE;
   }
-  if (N > (int64_t(1) << 30) || d > (int64_t(1) << 30) || M > (int64_t(1) << 31) / 2) {
-    set_error("paro_w4_linear: sizes too large");
+  // (the kernels address one tile of rows with 32-bit byte offsets)
+  if (N > (int64_t(1) << 30) || d > (int64_t(1) << 22) || M > (int64_t(1) << 31) / 2) {
+    set_error("paro_w4_linear: sizes too large (N <= 2^30, d <= 2^22, M < 2^30)");
     return PARO_ERR_UNSUPPORTED;
   }
   if (r && (r->d != d || r->group != group)) {

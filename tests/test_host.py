@@ -107,6 +107,11 @@ def test_hot_calls_validate_before_any_launch(paro):
     assert lib.paro_w4_linear(*args, 4, 60, 256, 128, None, 0, None) == -2
     assert lib.paro_w4_linear(*args, 4, 64, 200, 128, None, 0, None) == -2
     assert lib.paro_w4_linear(*args, -1, 64, 256, 128, None, 0, None) == -2
+    # sizes past the kernels' 32-bit tile offsets are unsupported
+    assert lib.paro_w4_linear(*args, 4, 64, 1 << 23, 128, None, 0, None) == -6
+    assert lib.paro_w4_linear(*args, 4, 1 << 31, 256, 128, None, 0, None) == -6
+    # small batches: ceil(d / 512) * M * N * 4 bytes of partial sums must stay below 2^31
+    assert lib.paro_w4_linear(*args, 16, 1 << 24, 1 << 16, 128, None, 0, None) == -6
     assert lib.paro_w4_linear(None, bad, dummy, dummy, dummy, None, dummy, 4, 64, 256, 128,
                               None, 0, None) == -5
     assert lib.paro_w4_linear(None, None, dummy, dummy, dummy, None, dummy, 4, 64, 256, 128,
