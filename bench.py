@@ -16,8 +16,9 @@ the timed region.
 
 Other workloads (``--workload``): prefill_down (2048 x 14336 -> 4096),
 decode (M = 1, 4, 16 tokens, 4096 -> 4096; weight streaming), sweep (the 27
-rotation-only points, 8192 x d), copy (a plain device copy, for calibrating
-HBM byte counters).
+rotation-only points, 8192 x d), chain (the seven linears of a Llama-3-8B
+decoder layer as rotated W4, plain W4 and dense fp16 chains), copy (a plain
+device copy, for calibrating HBM byte counters).
 
 Prints one JSON line on stdout.
 """
@@ -39,8 +40,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
 METRIC = "rotated-W4G128 linear TFLOP/s + rotation HBM GB/s; % overhead vs plain W4"
-KERNEL_SOURCES = ["rotated_w4_linear_amd/csrc/rotate.hip", "rotated_w4_linear_amd/csrc/w4_linear.hip",
-                  "rotated_w4_linear_amd/csrc/plan.cpp"]
+
 
 
 def log(msg):
@@ -168,7 +168,29 @@ def time_layer(paro, torch, r, xs, qr, qp, steps, warmup, M, N, d):
         "lin_ms": float(np.mean(lin)),
         "fused_call_ms": fused,
         "plain_ms": float(np.mean(plain_ms)),
+        "pct": {k: [round(float(np.percentile(v, p)), 4) for p in (10, 50, 90)]
+                for k, v in (("rotation_ms", rot), ("linear_ms", lin), ("plain_w4_ms", plain_ms))},
     }
+
+
+def copy_rate_gbps(torch, nbytes, ring=4, reps=12):
+    """Read + write GB/s of a plain device copy of nbytes, cycling a ring of buffers
+    (the same cold-cache condition as the kernels)."""
+    src = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(ring)]
+    dst = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(ring)]
+    for i in range(ring):
+        dst[i].copy_(src[i])
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(reps):
+        dst[i % ring].copy_(src[(i + 1) % ring])
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del src, dst
+    return 2.0 * nbytes / (ms * 1e-3) / 1e9
 
 
 def cpu_baseline(x, layer, paro_q, N, d, target_s=12.0):
@@ -202,6 +224,8 @@ def bench_layer(args, paro, torch, name, x, layer):
     flops = 2.0 * M * N * d
     rot_bytes = 4.0 * M * d
     lin_tflops = flops / (tm["lin_ms"] * 1e-3) / 1e12
+    copy_gbps = copy_rate_gbps(torch, M * d * 2)
+    rot_gbps = rot_bytes / (tm["rot_ms"] * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": round(flops / (tm["step_ms"] * 1e-3) / 1e12, 3),
@@ -220,6 +244,9 @@ def bench_layer(args, paro, torch, name, x, layer):
         "fused_entry_ms": round(tm["fused_call_ms"], 4),
         "overhead_vs_plain_pct": round(100.0 * (tm["step_ms"] - tm["plain_ms"]) / tm["plain_ms"], 2),
         "rotation_share_pct": round(100.0 * tm["rot_ms"] / tm["step_ms"], 2),
+        "p10_p50_p90_ms": tm["pct"],
+        "copy_same_bytes_gbps": round(copy_gbps, 1),
+        "rotation_frac_of_copy": round(rot_gbps / copy_gbps, 4),
         "roofline": {"bound": "mfma", "achieved": round(lin_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(lin_tflops / MFMA_F16_PEAK_TFLOPS, 4),
                      "traffic": traffic_for(f"w4_gemm:{name}")},
@@ -344,6 +371,91 @@ def bench_sweep(args, paro, torch):
     }
 
 
+def bench_chain(args, paro, torch):
+    """The seven linears of one Llama-3-8B decoder layer in sequence (q, k, v, o,
+    gate, up, down; attention and activations left out), as rotated W4G128,
+    plain W4G128 and dense fp16 (torch.matmul, i.e. hipBLASLt) chains."""
+    import synthetic
+    layers = synthetic.decoder_layer()
+    ring = args.ring or 2
+    T = Timer(torch)
+    plans, qr, qp, wf = [], [], [], []
+    for name, layer in layers:
+        r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, 128)
+        w = torch.from_numpy(layer.w).cuda()
+        q1 = paro.paro_quantize_weights(r, w, 128)
+        p1 = paro.paro_quantize_weights(None, w, 128)
+        plans.append(r)
+        qr.append([q1] + [tuple(t.clone() for t in q1) for _ in range(ring - 1)])
+        qp.append([p1] + [tuple(t.clone() for t in p1) for _ in range(ring - 1)])
+        wf.append([w] + [w.clone() for _ in range(ring - 1)])
+    torch.cuda.synchronize()
+    res = {}
+    for M in [int(v) for v in args.chain_m.split(",")]:
+        xs = [torch.from_numpy(synthetic.decoder_x(i, M)).cuda() for i in range(len(layers))]
+        ys = [torch.empty((M, layers[i][1].w.shape[0]), dtype=torch.float16, device="cuda")
+              for i in range(len(layers))]
+        wsr = [paro.new_workspace(plans[i], M, ys[i].shape[1], xs[i].shape[1]) for i in range(len(layers))]
+        wsp = [paro.new_workspace(None, M, ys[i].shape[1], xs[i].shape[1]) for i in range(len(layers))]
+
+        def chain(kind, k):
+            for i in range(len(layers)):
+                if kind == "rot":
+                    paro.paro_w4_linear(plans[i], xs[i], *qr[i][k], y=ys[i], workspace=wsr[i])
+                elif kind == "plain":
+                    paro.paro_w4_linear(None, xs[i], *qp[i][k], y=ys[i], workspace=wsp[i])
+                else:
+                    torch.matmul(xs[i], wf[i][k].t(), out=ys[i])
+
+        timing = {}
+        for kind in ("rot", "plain", "fp16"):
+            for k in range(max(2, args.warmup)):
+                chain(kind, k % ring)
+            torch.cuda.synchronize()
+            n = max(args.steps, 20)
+            s = T.event()
+            for k in range(n):
+                chain(kind, k % ring)
+            e = T.event()
+            torch.cuda.synchronize()
+            timing[kind] = s.elapsed_time(e) / n
+        # per-linear times (events around each launch), rotated W4 and fp16
+        per = {}
+        for kind in ("rot", "fp16"):
+            evs = []
+            for k in range(max(args.steps, 20)):
+                row = []
+                for i in range(len(layers)):
+                    a = T.event()
+                    if kind == "rot":
+                        paro.paro_w4_linear(plans[i], xs[i], *qr[i][k % ring], y=ys[i], workspace=wsr[i])
+                    else:
+                        torch.matmul(xs[i], wf[i][k % ring].t(), out=ys[i])
+                    row.append((a, T.event()))
+                evs.append(row)
+            torch.cuda.synchronize()
+            per[kind] = [round(1e3 * float(np.mean([evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(len(evs))])), 1)
+                         for i in range(len(layers))]
+        res[f"M{M}"] = {
+            "per_linear_us": {layers[i][0]: {"rotated_w4": per["rot"][i], "fp16": per["fp16"][i]}
+                              for i in range(len(layers))},
+            "rotated_w4_us": round(1e3 * timing["rot"], 1), "plain_w4_us": round(1e3 * timing["plain"], 1),
+            "fp16_us": round(1e3 * timing["fp16"], 1),
+            "speedup_vs_fp16": round(timing["fp16"] / timing["rot"], 3),
+            "overhead_vs_plain_pct": round(100 * (timing["rot"] - timing["plain"]) / timing["plain"], 1),
+        }
+        log(f"[bench] chain M={M}: {res[f'M{M}']}")
+    first = res[next(iter(res))]
+    return {"metric": "decoder-layer linear chain speedup vs fp16 (rotated W4G128)",
+            "value": first["speedup_vs_fp16"], "unit": "x", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(first["rotated_w4_us"] / 1e3, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+            "data": "synthetic",
+            "config": {"workload": "llama3_8b_layer_linears_M" + args.chain_m.replace(",", "_"),
+                       "group": 128, "stages_K": 8},
+            "chain": res}
+
+
 def bench_copy(args, torch):
     """A plain device copy of known size (for calibrating HBM byte counters)."""
     n = 256 << 20
@@ -372,9 +484,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill_mlp",
-                    choices=["prefill_mlp", "prefill_down", "decode", "sweep", "tiny", "copy"])
+                    choices=["prefill_mlp", "prefill_down", "decode", "sweep", "tiny", "copy", "chain"])
     ap.add_argument("--ring", type=int, default=0, help="distinct input copies cycled (0 = auto)")
     ap.add_argument("--decode-m", default="1,4,16", help="token counts of the decode workload")
+    ap.add_argument("--chain-m", default="1,16,2048", help="token counts of the layer-chain workload")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -404,6 +517,8 @@ def main():
         out = bench_decode(args, paro, torch)
     elif args.workload == "sweep":
         out = bench_sweep(args, paro, torch)
+    elif args.workload == "chain":
+        out = bench_chain(args, paro, torch)
     else:
         out = bench_copy(args, torch)
     print(json.dumps(out), flush=True)

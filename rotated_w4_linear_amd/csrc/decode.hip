@@ -8,9 +8,10 @@
 // With at most 16 tokens the layer is a stream over the packed weights, so
 // the kernel is organised around keeping HBM busy:
 //  * a workgroup owns a k-slice of 512 input channels (four 128-channel
-//    groups) and 128 output channels. Each wavefront first loads the
-//    activations (and schedule) of segment w of the slice, then issues all
-//    of its weight loads (32 rows x 512 k, 8 KB);
+//    groups) and 128 output channels (64 for layers where 128 would leave
+//    CUs idle). Each wavefront first loads the activations (and schedule) of
+//    segment w of the slice, then issues all of its weight loads (32 or 16
+//    rows x 512 k);
 //  * while the weights are in flight, wavefront w rotates its segment for
 //    all tokens in registers (the per-lane machinery of the stand-alone
 //    rotation: K stages, K + 1 LDS exchanges) and writes X' into a shared,
@@ -54,7 +55,6 @@ namespace {
 using namespace w4;
 
 constexpr int DK_SEGS = 4;                 // 128-channel groups per k-slice
-constexpr int DK_NB = 128;                 // output channels per workgroup
 constexpr int DK_TOK = 16;                 // token columns of the MFMA tile
 constexpr int kRsrcWord3 = 0x00020000;     // gfx9 buffer resource word 3
 constexpr int kAuxL2 = 1;                  // sc0: skip the per-CU cache
@@ -88,7 +88,8 @@ __device__ __forceinline__ int xl_offset(int m, int k) {
 
 // T: token rows staged and rotated (4 for M <= 4, else 16); MFMA columns past
 // T read tile rows that were never written and are ignored like those past M.
-template <bool ROT, int KMAX, bool KEXACT, bool FAST, int T>
+// TJ: 16-row tiles per wavefront (the workgroup owns 64 TJ output channels).
+template <bool ROT, int KMAX, bool KEXACT, bool FAST, int T, int TJ>
 __global__ __launch_bounds__(256) void w4_decode_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zr,
@@ -102,6 +103,7 @@ __global__ __launch_bounds__(256) void w4_decode_kernel(
   __shared__ rot::f4 xch[ROT ? 4 * (T / 4) * 64 : 1];
   __shared__ int s_last;
 
+  constexpr int NB = 64 * TJ;  // output channels per workgroup
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int xcd = blockIdx.x & 7, j8 = blockIdx.x >> 3;
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(256) void w4_decode_kernel(
   const int g0 = ks * DK_SEGS;
   const int nq = min(DK_SEGS, groups - g0);
   const int r = lane & 15, kq = lane >> 4;
-  const int rb = nbg * DK_NB + 32 * w;  // this wavefront's first output channel
+  const int rb = nbg * NB + 16 * TJ * w;  // this wavefront's first output channel
   char* xlb = (char*)xl;
 
   // ---- 1. activations of segment g0 + w (token rows past M repeat M - 1) ---
@@ -137,12 +139,12 @@ __global__ __launch_bounds__(256) void w4_decode_kernel(
   // issued here, group by group, without waiting: groups past the end of d
   // re-read the last group (never used) and the scale and zero are converted
   // only when their group is multiplied.
-  u4 wv[2][DK_SEGS];
-  uint32_t sraw[2][DK_SEGS], zraw[2][DK_SEGS];
-  const uint8_t* wrow[2];
-  size_t grow[2];
+  u4 wv[TJ][DK_SEGS];
+  uint32_t sraw[TJ][DK_SEGS], zraw[TJ][DK_SEGS];
+  const uint8_t* wrow[TJ];
+  size_t grow[TJ];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < TJ; ++j) {
     const int nc = min(rb + 16 * j + r, N - 1);  // rows past N are never stored
     wrow[j] = qw + (size_t)nc * (size_t)(d >> 1) + 16 * kq;
     grow[j] = (size_t)nc * groups;
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(256) void w4_decode_kernel(
   for (int q = 0; q < DK_SEGS; ++q) {
     const int g = min(g0 + q, groups - 1);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < TJ; ++j) {
       wv[j][q] = *(const u4*)(wrow[j] + 64 * g);
       sraw[j][q] = sc[grow[j] + g];
       zraw[j][q] = zr[grow[j] + g];
@@ -187,13 +189,15 @@ __global__ __launch_bounds__(256) void w4_decode_kernel(
   __syncthreads();
 
   // ---- 4. dequantize and multiply, group by group as the weights land -------
-  f4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  f4 acc[TJ];
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int q = 0; q < DK_SEGS; ++q) {
     if (q < nq) {
-      h2 ss[2], zz[2];
+      h2 ss[TJ], zz[TJ];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < TJ; ++j) {
         ss[j] = splat2(__builtin_bit_cast(_Float16, (uint16_t)sraw[j][q]));
         zz[j] = splat2((_Float16)(1024.0f + (float)zraw[j][q]));
       }
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(256) void w4_decode_kernel(
       for (int i = 0; i < 4; ++i) {
         const h8 b = *(const h8*)(xlb + (r * 64 + ((16 * q + 4 * kq + i) ^ r)) * 16);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TJ; ++j)
           acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
               dequant8_interleaved(wv[j][q][i], zz[j], ss[j]), b, acc[j], 0, 0, 0);
       }
@@ -224,7 +228,7 @@ __global__ __launch_bounds__(256) void w4_decode_kernel(
   };
   if (ksl == 1) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < TJ; ++j) {
       const int n = rb + 16 * j + 4 * kq;
       if (r < M && n < N) store_y(r, n, acc[j]);
     }
@@ -235,7 +239,7 @@ __global__ __launch_bounds__(256) void w4_decode_kernel(
   const __amdgpu_buffer_rsrc_t rp =
       __builtin_amdgcn_make_buffer_rsrc((void*)part, (short)0, 0x7fffffff, kRsrcWord3);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < TJ; ++j) {
     const int n = rb + 16 * j + 4 * kq;
     if (r < M && n < N) {
       const int off = (int)((((size_t)ks * M + r) * N + n) * 4);
@@ -256,16 +260,25 @@ __global__ __launch_bounds__(256) void w4_decode_kernel(
   if (!s_last) return;
 
   // ---- 6. last k-slice to arrive: sum in k-slice order, bias, fp16 ----------
-  for (int it = tid; it < M * (DK_NB / 4); it += 256) {
-    const int m = it / (DK_NB / 4);
-    const int n = nbg * DK_NB + 4 * (it % (DK_NB / 4));
+  // (eight slices' loads in flight at a time; the adds keep slice order)
+  const int slice_bytes = M * N * 4;
+  for (int it = tid; it < M * (NB / 4); it += 256) {
+    const int m = it / (NB / 4);
+    const int n = nbg * NB + 4 * (it % (NB / 4));
     if (n >= N) continue;
+    const int off0 = (int)(((size_t)m * N + n) * 4);
     f4 s = {0.f, 0.f, 0.f, 0.f};
-    for (int k2 = 0; k2 < ksl; ++k2) {
-      const int off = (int)((((size_t)k2 * M + m) * N + n) * 4);
-      const u4 v = sys ? __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kAuxSys)
-                       : __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kAuxL2);
-      s = k2 == 0 ? __builtin_bit_cast(f4, v) : s + __builtin_bit_cast(f4, v);
+    for (int k2 = 0; k2 < ksl; k2 += 8) {
+      u4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int off = off0 + min(k2 + u, ksl - 1) * slice_bytes;
+        v[u] = sys ? __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kAuxSys)
+                   : __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kAuxL2);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (k2 + u < ksl) s = (k2 + u == 0) ? __builtin_bit_cast(f4, v[u]) : s + __builtin_bit_cast(f4, v[u]);
     }
     store_y(m, n, s);
   }
@@ -317,12 +330,12 @@ bool xcd_dispatch_is_round_robin() {
   return ok;
 }
 
-template <bool ROT, int KMAX, bool KEXACT, bool FAST, int T>
+template <bool ROT, int KMAX, bool KEXACT, bool FAST, int T, int TJ>
 hipError_t launch_t(const uint16_t* x, const uint8_t* qw, const uint16_t* sc, const uint8_t* zr,
                     const uint16_t* bias, uint16_t* y, int M, int N, int d,
                     const paro_rotation* r, void* ws, hipStream_t stream) {
   const int ksl = (d / 128 + DK_SEGS - 1) / DK_SEGS;
-  const int nbl_all = (N + DK_NB - 1) / DK_NB;
+  const int nbl_all = (N + 64 * TJ - 1) / (64 * TJ);
   uint32_t* cnt = (uint32_t*)ws;
   float* part = (float*)((char*)ws + kDecodeCounterBytes);
   const uint32_t* tab = r ? r->d_table : nullptr;
@@ -332,7 +345,7 @@ hipError_t launch_t(const uint16_t* x, const uint8_t* qw, const uint16_t* sc, co
   for (int nb0 = 0; nb0 < nbl_all; nb0 += kMaxNb) {
     const int nbl = min(kMaxNb, nbl_all - nb0);
     const unsigned blocks = 8u * (unsigned)ksl * (unsigned)((nbl + 7) / 8);
-    hipLaunchKernelGGL((w4_decode_kernel<ROT, KMAX, KEXACT, FAST, T>), dim3(blocks), dim3(256), 0,
+    hipLaunchKernelGGL((w4_decode_kernel<ROT, KMAX, KEXACT, FAST, T, TJ>), dim3(blocks), dim3(256), 0,
                        stream, x, qw, sc, zr, bias, y, M, N, d, tab, K, part, cnt, ksl, nbl, nb0,
                        sys);
     const hipError_t e = hipGetLastError();
@@ -341,17 +354,17 @@ hipError_t launch_t(const uint16_t* x, const uint8_t* qw, const uint16_t* sc, co
   return hipSuccess;
 }
 
-template <int T>
+template <int T, int TJ>
 hipError_t launch_plan(const uint16_t* x, const uint8_t* qw, const uint16_t* sc, const uint8_t* zr,
                        const uint16_t* bias, uint16_t* y, int m, int n, int k,
                        const paro_rotation* r, void* ws, hipStream_t stream) {
-  if (!r) return launch_t<false, 0, true, true, T>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
-  if (r->K == 0) return launch_t<true, 0, true, true, T>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
+  if (!r) return launch_t<false, 0, true, true, T, TJ>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
+  if (r->K == 0) return launch_t<true, 0, true, true, T, TJ>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
   if (r->lay.fast) {
-    if (r->K == 8) return launch_t<true, 8, true, true, T>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
-    return launch_t<true, 8, false, true, T>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
+    if (r->K == 8) return launch_t<true, 8, true, true, T, TJ>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
+    return launch_t<true, 8, false, true, T, TJ>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
   }
-  return launch_t<true, 8, false, false, T>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
+  return launch_t<true, 8, false, false, T, TJ>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
 }
 
 }  // namespace
@@ -366,8 +379,14 @@ hipError_t launch_w4_decode(const uint16_t* x, const uint8_t* qweight, const uin
                             hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const int m = (int)M, n = (int)N, k = (int)d;
-  if (M <= 4) return launch_plan<4>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream);
-  return launch_plan<16>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream);
+  // 64-channel workgroups when 128-channel ones would not give two per CU
+  const int64_t wg128 = ((N + 127) / 128) * ((d / 128 + DK_SEGS - 1) / DK_SEGS);
+  if (wg128 < 384) {
+    if (M <= 4) return launch_plan<4, 1>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream);
+    return launch_plan<16, 1>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream);
+  }
+  if (M <= 4) return launch_plan<4, 2>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream);
+  return launch_plan<16, 2>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream);
 }
 
 }  // namespace paro

@@ -198,3 +198,29 @@ def linear_case(seed: int, M: int, d: int, N: int, group: int = 128, K: int = 8,
     pairs, theta, alpha = draw_rotation(rng, d, group, K)
     b = draw_bias(rng, N) if bias else None
     return x, Layer(w, pairs, theta, alpha, group), b
+
+
+# Llama-3-8B decoder-layer linears (name, in_features d, out_features N).
+DECODER_LINEARS = [("q_proj", 4096, 4096), ("k_proj", 4096, 1024), ("v_proj", 4096, 1024),
+                   ("o_proj", 4096, 4096), ("gate_proj", 4096, 14336), ("up_proj", 4096, 14336),
+                   ("down_proj", 14336, 4096)]
+
+
+def decoder_layer():
+    """The seven linears of one Llama-3-8B decoder layer, each with its own
+    rotation (group 128, K = 8) and W ~ N(0, 0.02): [(name, Layer)]."""
+    out = []
+    for i, (name, d, N) in enumerate(DECODER_LINEARS):
+        rng = rng_for(6, i)
+        w = draw_w(rng, N, d, 0.02)
+        pairs, theta, alpha = draw_rotation(rng, d, 128, 8)
+        out.append((name, Layer(w, pairs, theta, alpha, 128)))
+    return out
+
+
+def decoder_x(i: int, M: int) -> np.ndarray:
+    """Activations for linear i of decoder_layer() at M tokens (1 % outliers x20)."""
+    d = DECODER_LINEARS[i][1]
+    rng = rng_for(7, 1000 * i + M)
+    return draw_x(rng, M, d, n_outliers(d), 20.0)
+
