@@ -12,7 +12,10 @@ Inputs are synthetic (seeded), resident in HBM before timing; distinct copies
 of X and of the quantized weights are cycled so that caches (incl. the 256 MB
 Infinity Cache) do not serve them from a previous step. Kernel durations are
 measured with HIP events recorded on the launch stream around every launch in
-the timed region.
+the timed region. Timing starts only after half a second of the same work (the
+GPU clock ramps up over the first tens of milliseconds of load), and variants
+that are compared (rotated vs plain, W4 vs fp16) are timed in alternating
+blocks.
 
 Other workloads (``--workload``): prefill_down (2048 x 14336 -> 4096),
 decode (M = 1, 4, 16 tokens, 4096 -> 4096; weight streaming), sweep (the 27
@@ -108,8 +111,29 @@ def setup_layer(paro, torch, x, layer, ring):
     return r, xs, qr, qp
 
 
+def settle(torch, fns, min_rounds, seconds=0.5):
+    """Run the callables round-robin for at least ``seconds`` of wall time and
+    ``min_rounds`` rounds. The GPU clock ramps up over the first few tens of
+    milliseconds of sustained work and then settles; every variant is timed
+    only after that, so that none of them is measured on the ramp."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < min_rounds or time.perf_counter() - t0 < seconds:
+        for f in fns:
+            f(i)
+        i += 1
+        if i % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def time_layer(paro, torch, r, xs, qr, qp, steps, warmup, M, N, d):
-    """Return per-step and per-kernel timings (ms) of the rotated and plain layer."""
+    """Return per-step and per-kernel timings (ms) of the rotated and plain layer.
+
+    After ``settle``, the rotated steps (the reported step) and the plain layer
+    are timed in alternating blocks, rotated / plain / rotated / plain, so that
+    any remaining clock drift affects both alike; the per-kernel figures
+    average both blocks, the step time is the first rotated block's."""
     ring = len(xs)
     xr = torch.empty((M, d), dtype=torch.float16, device="cuda")
     y = torch.empty((M, N), dtype=torch.float16, device="cuda")
@@ -122,21 +146,39 @@ def time_layer(paro, torch, r, xs, qr, qp, steps, warmup, M, N, d):
         paro.paro_w4_linear(None, xr, *qr[k], y=y)
         return e1
 
-    for i in range(warmup):
-        rotated_step(i)
-    torch.cuda.synchronize()
-    ev = []
-    start = T.event()
-    prev = start
-    for i in range(steps):
-        mid = rotated_step(i)
-        end = T.event()
-        ev.append((prev, mid, end))
-        prev = end
-    torch.cuda.synchronize()
-    total = start.elapsed_time(prev)
-    rot = [a.elapsed_time(b) for a, b, _ in ev]
-    lin = [b.elapsed_time(c) for _, b, c in ev]
+    def plain_step(i):
+        paro.paro_w4_linear(None, xs[i % ring], *qp[i % ring], y=y)
+
+    settle(torch, [rotated_step, plain_step], warmup)
+
+    def rotated_block():
+        ev = []
+        start = T.event()
+        prev = start
+        for i in range(steps):
+            mid = rotated_step(i)
+            end = T.event()
+            ev.append((prev, mid, end))
+            prev = end
+        torch.cuda.synchronize()
+        return (start.elapsed_time(prev), [a.elapsed_time(b) for a, b, _ in ev],
+                [b.elapsed_time(c) for _, b, c in ev])
+
+    def plain_block():
+        ev = []
+        for i in range(steps):
+            a = T.event()
+            plain_step(i)
+            ev.append((a, T.event()))
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    total, rot, lin = rotated_block()
+    plain_ms = plain_block()
+    _, rot2, lin2 = rotated_block()
+    plain_ms += plain_block()
+    rot += rot2
+    lin += lin2
 
     # the fused entry point (rotation handle passed to paro_w4_linear) on the same data
     ws = paro.new_workspace(r, M, N, d)
@@ -150,18 +192,6 @@ def time_layer(paro, torch, r, xs, qr, qp, steps, warmup, M, N, d):
     torch.cuda.synchronize()
     fused = s.elapsed_time(e) / steps
 
-    # plain W4 (no rotation) on the unrotated activations
-    for i in range(warmup):
-        paro.paro_w4_linear(None, xs[i % ring], *qp[i % ring], y=y)
-    torch.cuda.synchronize()
-    plain = []
-    for i in range(steps):
-        a = T.event()
-        paro.paro_w4_linear(None, xs[i % ring], *qp[i % ring], y=y)
-        b = T.event()
-        plain.append((a, b))
-    torch.cuda.synchronize()
-    plain_ms = [a.elapsed_time(b) for a, b in plain]
     return {
         "step_ms": total / steps,
         "rot_ms": float(np.mean(rot)),
@@ -293,18 +323,18 @@ def bench_decode(args, paro, torch):
             else:
                 paro.paro_rotate(r, x, xr)
 
-        timing = {}
-        for kind in ("rot", "plain", "rotate_only"):
-            for i in range(args.warmup + 3):
-                run(kind, i)
-            torch.cuda.synchronize()
-            n = max(args.steps, 100)
-            s = T.event()
-            for i in range(n):
-                run(kind, i)
-            e = T.event()
-            torch.cuda.synchronize()
-            timing[kind] = s.elapsed_time(e) / n
+        kinds = ("rot", "plain", "rotate_only")
+        settle(torch, [lambda i, k=k: run(k, i) for k in kinds], args.warmup + 3)
+        timing = {k: 0.0 for k in kinds}
+        for _ in range(2):   # alternating blocks; the mean of both
+            for kind in kinds:
+                n = max(args.steps, 100)
+                s = T.event()
+                for i in range(n):
+                    run(kind, i)
+                e = T.event()
+                torch.cuda.synchronize()
+                timing[kind] += s.elapsed_time(e) / n / 2
         # packed codes + fp16 scales + u8 zeros, activations in, outputs out
         wbytes = N * d / 2 + 3 * N * d / 128 + 2 * M * d + 2 * M * N
         res[f"M{M}"] = {
@@ -343,9 +373,8 @@ def bench_sweep(args, paro, torch):
         for _ in range(ring - 1):
             xs.append(xs[0].clone())
         ys = [torch.empty_like(xs[0]) for _ in range(ring)]
-        for i in range(args.warmup + 2):
-            paro.paro_rotate(r, xs[i % ring], ys[i % ring])
-        torch.cuda.synchronize()
+        settle(torch, [lambda i: paro.paro_rotate(r, xs[i % ring], ys[i % ring])], args.warmup + 2,
+               seconds=0.2)
         n = max(args.steps, 30)
         s = T.event()
         for i in range(n):
@@ -407,18 +436,18 @@ def bench_chain(args, paro, torch):
                 else:
                     torch.matmul(xs[i], wf[i][k].t(), out=ys[i])
 
-        timing = {}
-        for kind in ("rot", "plain", "fp16"):
-            for k in range(max(2, args.warmup)):
-                chain(kind, k % ring)
-            torch.cuda.synchronize()
-            n = max(args.steps, 20)
-            s = T.event()
-            for k in range(n):
-                chain(kind, k % ring)
-            e = T.event()
-            torch.cuda.synchronize()
-            timing[kind] = s.elapsed_time(e) / n
+        kinds = ("rot", "plain", "fp16")
+        settle(torch, [lambda k, c=c: chain(c, k % ring) for c in kinds], max(2, args.warmup))
+        timing = {c: 0.0 for c in kinds}
+        for _ in range(2):   # alternating blocks; the mean of both
+            for kind in kinds:
+                n = max(args.steps, 20)
+                s = T.event()
+                for k in range(n):
+                    chain(kind, k % ring)
+                e = T.event()
+                torch.cuda.synchronize()
+                timing[kind] += s.elapsed_time(e) / n / 2
         # per-linear times (events around each launch), rotated W4 and fp16
         per = {}
         for kind in ("rot", "fp16"):

@@ -300,7 +300,8 @@ def test_linear_workspace_errors(paro):
 # ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,d,N", [(1, 640, 400), (16, 640, 400), (5, 384, 48), (2, 4096, 4096),
-                                   (16, 14336, 256), (11, 1152, 1040), (1, 128, 16)])
+                                   (16, 14336, 256), (11, 1152, 1040), (1, 128, 16),
+                                   (3, 4096, 14336), (16, 14336, 4096)])
 def test_decode_fused_equals_rotate_then_plain(paro, M, d, N):
     """The fused transform yields the X' bits paro_rotate yields and the k-split
     sum order does not depend on where X' came from: equal outputs bit for bit."""
