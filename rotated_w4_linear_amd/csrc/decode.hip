@@ -89,7 +89,7 @@ __device__ __forceinline__ int xl_offset(int m, int k) {
 // T: token rows staged and rotated (4 for M <= 4, else 16); MFMA columns past
 // T read tile rows that were never written and are ignored like those past M.
 // TJ: 16-row tiles per wavefront (the workgroup owns 64 TJ output channels).
-template <bool ROT, int KMAX, bool KEXACT, bool FAST, int T, int TJ>
+template <bool ROT, int KMAX, bool KEXACT, bool FAST, int T, int TJ, bool SZV>
 __global__ __launch_bounds__(256) void w4_decode_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zr,
@@ -138,7 +138,11 @@ __global__ __launch_bounds__(256) void w4_decode_kernel(
   // i.e. codes 128 (g0 + q) + 32 kq + 8 i + e for MFMA step i. All loads are
   // issued here, group by group, without waiting: groups past the end of d
   // re-read the last group (never used) and the scale and zero are converted
-  // only when their group is multiplied.
+  // only when their group is multiplied. With SZV (the number of groups is a
+  // multiple of four, so every slice has four groups and a row's four scales
+  // and four zeros start 8- and 4-byte aligned) they come in as one 8-byte and
+  // one 4-byte load per row instead of eight 2- and 1-byte loads: small loads
+  // cost as much issue and queue time as 16-byte ones.
   u4 wv[TJ][DK_SEGS];
   uint32_t sraw[TJ][DK_SEGS], zraw[TJ][DK_SEGS];
   const uint8_t* wrow[TJ];
@@ -149,14 +153,35 @@ __global__ __launch_bounds__(256) void w4_decode_kernel(
     wrow[j] = qw + (size_t)nc * (size_t)(d >> 1) + 16 * kq;
     grow[j] = (size_t)nc * groups;
   }
-#pragma unroll
-  for (int q = 0; q < DK_SEGS; ++q) {
-    const int g = min(g0 + q, groups - 1);
+  if constexpr (SZV) {
+    uint2 s4[TJ];
+    uint32_t z4[TJ];
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
-      wv[j][q] = *(const u4*)(wrow[j] + 64 * g);
-      sraw[j][q] = sc[grow[j] + g];
-      zraw[j][q] = zr[grow[j] + g];
+      s4[j] = *(const uint2*)(sc + grow[j] + g0);
+      z4[j] = *(const uint32_t*)(zr + grow[j] + g0);
+    }
+#pragma unroll
+    for (int q = 0; q < DK_SEGS; ++q)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) wv[j][q] = *(const u4*)(wrow[j] + 64 * (g0 + q));
+#pragma unroll
+    for (int q = 0; q < DK_SEGS; ++q)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        sraw[j][q] = ((q < 2 ? s4[j].x : s4[j].y) >> (16 * (q & 1))) & 0xffffu;
+        zraw[j][q] = (z4[j] >> (8 * q)) & 0xffu;
+      }
+  } else {
+#pragma unroll
+    for (int q = 0; q < DK_SEGS; ++q) {
+      const int g = min(g0 + q, groups - 1);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        wv[j][q] = *(const u4*)(wrow[j] + 64 * g);
+        sraw[j][q] = sc[grow[j] + g];
+        zraw[j][q] = zr[grow[j] + g];
+      }
     }
   }
   // keep every load above ahead of the first use of the activations: the
@@ -330,7 +355,7 @@ bool xcd_dispatch_is_round_robin() {
   return ok;
 }
 
-template <bool ROT, int KMAX, bool KEXACT, bool FAST, int T, int TJ>
+template <bool ROT, int KMAX, bool KEXACT, bool FAST, int T, int TJ, bool SZV>
 hipError_t launch_t(const uint16_t* x, const uint8_t* qw, const uint16_t* sc, const uint8_t* zr,
                     const uint16_t* bias, uint16_t* y, int M, int N, int d,
                     const paro_rotation* r, void* ws, hipStream_t stream) {
@@ -345,7 +370,7 @@ hipError_t launch_t(const uint16_t* x, const uint8_t* qw, const uint16_t* sc, co
   for (int nb0 = 0; nb0 < nbl_all; nb0 += kMaxNb) {
     const int nbl = min(kMaxNb, nbl_all - nb0);
     const unsigned blocks = 8u * (unsigned)ksl * (unsigned)((nbl + 7) / 8);
-    hipLaunchKernelGGL((w4_decode_kernel<ROT, KMAX, KEXACT, FAST, T, TJ>), dim3(blocks), dim3(256), 0,
+    hipLaunchKernelGGL((w4_decode_kernel<ROT, KMAX, KEXACT, FAST, T, TJ, SZV>), dim3(blocks), dim3(256), 0,
                        stream, x, qw, sc, zr, bias, y, M, N, d, tab, K, part, cnt, ksl, nbl, nb0,
                        sys);
     const hipError_t e = hipGetLastError();
@@ -354,17 +379,17 @@ hipError_t launch_t(const uint16_t* x, const uint8_t* qw, const uint16_t* sc, co
   return hipSuccess;
 }
 
-template <int T, int TJ>
+template <int T, int TJ, bool SZV>
 hipError_t launch_plan(const uint16_t* x, const uint8_t* qw, const uint16_t* sc, const uint8_t* zr,
                        const uint16_t* bias, uint16_t* y, int m, int n, int k,
                        const paro_rotation* r, void* ws, hipStream_t stream) {
-  if (!r) return launch_t<false, 0, true, true, T, TJ>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
-  if (r->K == 0) return launch_t<true, 0, true, true, T, TJ>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
+  if (!r) return launch_t<false, 0, true, true, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
+  if (r->K == 0) return launch_t<true, 0, true, true, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
   if (r->lay.fast) {
-    if (r->K == 8) return launch_t<true, 8, true, true, T, TJ>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
-    return launch_t<true, 8, false, true, T, TJ>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
+    if (r->K == 8) return launch_t<true, 8, true, true, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
+    return launch_t<true, 8, false, true, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
   }
-  return launch_t<true, 8, false, false, T, TJ>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
+  return launch_t<true, 8, false, false, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
 }
 
 }  // namespace
@@ -381,12 +406,18 @@ hipError_t launch_w4_decode(const uint16_t* x, const uint8_t* qweight, const uin
   const int m = (int)M, n = (int)N, k = (int)d;
   // 64-channel workgroups when 128-channel ones would not give two per CU
   const int64_t wg128 = ((N + 127) / 128) * ((d / 128 + DK_SEGS - 1) / DK_SEGS);
-  if (wg128 < 384) {
-    if (M <= 4) return launch_plan<4, 1>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream);
-    return launch_plan<16, 1>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream);
+  const bool tj1 = wg128 < 384, small = M <= 4;
+  // full slices and aligned bases: vector scale / zero loads
+  if ((d / 128) % DK_SEGS == 0 && ((uintptr_t)scales & 7) == 0 && ((uintptr_t)zeros & 3) == 0) {
+    if (tj1) return small ? launch_plan<4, 1, true>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream)
+                          : launch_plan<16, 1, true>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream);
+    return small ? launch_plan<4, 2, true>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream)
+                 : launch_plan<16, 2, true>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream);
   }
-  if (M <= 4) return launch_plan<4, 2>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream);
-  return launch_plan<16, 2>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream);
+  if (tj1) return small ? launch_plan<4, 1, false>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream)
+                        : launch_plan<16, 1, false>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream);
+  return small ? launch_plan<4, 2, false>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream)
+               : launch_plan<16, 2, false>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream);
 }
 
 }  // namespace paro

@@ -318,6 +318,30 @@ def test_decode_fused_equals_rotate_then_plain(paro, M, d, N):
     metrics.assert_linear_close(y_fused, ref)
 
 
+@pytest.mark.parametrize("M,d,N", [(1, 4096, 640), (16, 2048, 384)])
+def test_decode_unaligned_group_params(paro, M, d, N):
+    """Scales and zeros placed at odd addresses take the per-group load path
+    instead of the vector loads; both give the same output bit for bit."""
+    log(f"decode scales/zeros at odd offsets M={M} d={d} N={N}")
+    x, layer, b = synthetic.linear_case(seed=80 + M, M=M, d=d, N=N)
+    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, 128)
+    qw, s, z = paro.paro_quantize_weights(r, dev(layer.w), 128)
+    xd, bd = dev(x), dev(b)
+    y_aligned = host(paro.paro_w4_linear(r, xd, qw, s, z, bd))
+    s_buf = torch.zeros(s.numel() + 1, dtype=s.dtype, device="cuda")
+    z_buf = torch.zeros(z.numel() + 1, dtype=z.dtype, device="cuda")
+    s_odd = s_buf[1:].view(s.shape)
+    z_odd = z_buf[1:].view(z.shape)
+    s_odd.copy_(s)
+    z_odd.copy_(z)
+    assert s_odd.data_ptr() % 8 != 0 and z_odd.data_ptr() % 4 != 0
+    y_odd = host(paro.paro_w4_linear(r, xd, qw, s_odd, z_odd, bd))
+    assert np.array_equal(y_aligned.view(np.uint16), y_odd.view(np.uint16))
+    ref = oracle.rotated_w4_linear(x, host(qw), host(s), host(z), 128, layer.pairs, layer.theta,
+                                   layer.alpha, b)
+    metrics.assert_linear_close(y_aligned, ref)
+
+
 @pytest.mark.parametrize("K", [12, 32, 0, 3])
 def test_decode_other_stage_counts(paro, K):
     """K > 8 rotates into the workspace first; K = 0 and K < 8 run fused."""
