@@ -208,7 +208,10 @@ int paro_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qwe
  * layout descriptor to *layout (may be NULL):
  *   layout[0] = channels per segment (128 or 256),
  *   layout[1] = pairs per lane (1 or 2),
- *   layout[2] = 32-bit words per lane per segment,
+ *   layout[2] = 32-bit words per virtual lane per segment (the schedule's
+ *               fields padded to a multiple of 4; the image of a segment is
+ *               [layout[2] / 4][virtual lane][4], four consecutive fields of
+ *               a lane side by side),
  *   layout[3] = 1 if the factored two-FMA stage form is used, 0 for the
  *               general 2x2 form.
  * Runs the same validation as paro_rotation_create and returns its errors;

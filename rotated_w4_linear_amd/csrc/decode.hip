@@ -284,28 +284,60 @@ __global__ __launch_bounds__(256) void w4_decode_kernel(
   __syncthreads();
   if (!s_last) return;
 
-  // ---- 6. last k-slice to arrive: sum in k-slice order, bias, fp16 ----------
-  // (eight slices' loads in flight at a time; the adds keep slice order)
+  // ---- 6. last k-slice to arrive: sum the k-slices, bias, fp16 --------------
+  // The order of the additions is fixed (it does not depend on which slice
+  // arrived last). Each four-output item's slices are added in slice order by
+  // one thread, loads issued eight slices at a time. With more than eight
+  // slices (one round of loads no longer covers them) and few items per
+  // n-block (at most 128), groups of consecutive slices are instead summed in
+  // parallel, each in slice order, and the group sums added in group order.
   const int slice_bytes = M * N * 4;
-  for (int it = tid; it < M * (NB / 4); it += 256) {
-    const int m = it / (NB / 4);
-    const int n = nbg * NB + 4 * (it % (NB / 4));
-    if (n >= N) continue;
-    const int off0 = (int)(((size_t)m * N + n) * 4);
-    f4 s = {0.f, 0.f, 0.f, 0.f};
-    for (int k2 = 0; k2 < ksl; k2 += 8) {
+  const int items = M * (NB / 4);
+  auto sum_slices = [&](int off0, int s0, int s1) {
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k2 = s0; k2 < s1; k2 += 8) {
       u4 v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int off = off0 + min(k2 + u, ksl - 1) * slice_bytes;
+        const int off = off0 + min(k2 + u, s1 - 1) * slice_bytes;
         v[u] = sys ? __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kAuxSys)
                    : __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kAuxL2);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        if (k2 + u < ksl) s = (k2 + u == 0) ? __builtin_bit_cast(f4, v[u]) : s + __builtin_bit_cast(f4, v[u]);
+        if (k2 + u < s1) acc = (k2 + u == s0) ? __builtin_bit_cast(f4, v[u]) : acc + __builtin_bit_cast(f4, v[u]);
     }
-    store_y(m, n, s);
+    return acc;
+  };
+  if (ksl > 8 && 2 * items <= 256) {
+    const int spg = (ksl + min(ksl, 256 / items) - 1) / min(ksl, 256 / items);  // slices per group
+    const int ng = (ksl + spg - 1) / spg;                                       // groups
+    f4* red = (f4*)xl;  // [group][item]; the X' tile is no longer read
+    if (tid < items * ng) {
+      const int item = tid % items, gi = tid / items;
+      const int m = item / (NB / 4);
+      const int n = nbg * NB + 4 * (item % (NB / 4));
+      f4 g = {0.f, 0.f, 0.f, 0.f};
+      if (n < N) g = sum_slices((int)(((size_t)m * N + n) * 4), gi * spg, min(gi * spg + spg, ksl));
+      red[gi * items + item] = g;
+    }
+    __syncthreads();
+    if (tid < items) {
+      const int m = tid / (NB / 4);
+      const int n = nbg * NB + 4 * (tid % (NB / 4));
+      if (n < N) {
+        f4 t = red[tid];
+        for (int gi = 1; gi < ng; ++gi) t += red[gi * items + tid];
+        store_y(m, n, t);
+      }
+    }
+  } else {
+    for (int it = tid; it < items; it += 256) {
+      const int m = it / (NB / 4);
+      const int n = nbg * NB + 4 * (it % (NB / 4));
+      if (n >= N) continue;
+      store_y(m, n, sum_slices((int)(((size_t)m * N + n) * 4), 0, ksl));
+    }
   }
   if (tid == 0) {
     if (sys) __hip_atomic_store(&cnt[nb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);

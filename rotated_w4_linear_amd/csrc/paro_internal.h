@@ -28,8 +28,11 @@ namespace paro {
 // per-wave LDS tile. The two pairings together form disjoint even cycles, so
 // a "keep one, fetch one" assignment always exists.
 //
-// Table image per segment: NW fields, each field NV words (one per virtual
-// lane), field-major: tab[seg][field][v]. Field order:
+// Table image per segment: NW fields (padded with zero words to a multiple of
+// four) for each of NV virtual lanes, four fields interleaved per lane so that
+// a lane loads four consecutive fields with one 16-byte load and a wavefront's
+// load is one contiguous 1 KB: field f of virtual lane v is word
+// ((f / 4) * NV + v) * 4 + f % 4 of the segment. Field order:
 //   0                 load selector (v_perm byte selector putting the kept
 //                     channel of the natural pair in the low half)
 //   1 + 2*tau         LDS byte offset the lane writes its Y to, tau = 0..K
@@ -44,15 +47,17 @@ struct RotPlanLayout {
   int ppl = 1;           // virtual lanes per hardware lane
   int nv = 64;           // virtual lanes per segment
   int coef = 2;          // coefficients per stage (2 factored, 4 general)
-  int words = 0;         // fields per virtual lane
+  int words = 0;         // words per virtual lane (fields rounded up to four)
   bool fast = true;      // factored two-FMA stage form
 };
 
 inline int rot_field_count(int K, int coef) { return 1 + 2 * (K + 1) + coef * K + 4; }
+// words per virtual lane in the image: the field count rounded up to four
+inline int rot_words(int K, int coef) { return (rot_field_count(K, coef) + 3) & ~3; }
 
 struct RotPlanHost {
   RotPlanLayout lay;
-  std::vector<uint32_t> table;  // [segs][words][nv]
+  std::vector<uint32_t> table;  // [segs][words / 4][nv][4]
   // canonical fp32 tables for the weight transform, per group, stage, pair:
   // local (i | j << 16), c bits, s bits
   std::vector<uint32_t> wt_pairs;  // [groups][K][G/2]

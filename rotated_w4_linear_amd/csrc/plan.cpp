@@ -213,7 +213,7 @@ int build_rotation_plan(int64_t d, int32_t group, int32_t K, const int32_t* pair
     lay.nv = nv;
     lay.fast = fast;
     lay.coef = fast ? 2 : 4;
-    lay.words = rot_field_count(K, lay.coef);
+    lay.words = rot_words(K, lay.coef);
     std::vector<uint32_t> table((size_t)segs * lay.words * nv, 0);
     bool ok = true;
 
@@ -309,7 +309,7 @@ int build_rotation_plan(int64_t d, int32_t group, int32_t K, const int32_t* pair
       std::vector<double> lam(seg_ch);
       for (int ch = 0; ch < seg_ch; ++ch) lam[ch] = 1.0 / (double)alpha[base + ch];
       uint32_t* T = &table[(size_t)sg * lay.words * nv];
-      auto put = [&](int field, int v, uint32_t w) { T[(size_t)field * nv + v] = w; };
+      auto put = [&](int field, int v, uint32_t w) { T[((size_t)(field >> 2) * nv + v) * 4 + (field & 3)] = w; };
       const double lo = std::ldexp(1.0, -60), hi = std::ldexp(1.0, 60), tiny = std::ldexp(1.0, -20);
       auto in_range = [&](double x) { double a = std::fabs(x); return a >= lo && a <= hi; };
       for (int t = 0; t < K && ok; ++t) {

@@ -17,11 +17,14 @@
 // interleaves four tokens per 16-byte slot; the slots are planned on the host
 // so that both the writes and the reads are free of bank conflicts.
 //
-// Schedule table image (built by the host plan): per segment NW fields of NV
-// words, field-major. Field 0 is the load selector, 1 + 2 tau / 2 + 2 tau the
-// LDS write / read byte offsets of exchange tau (tau = 0..K), then C words
-// per stage, then the final scales of X and B, the store byte offset of the
-// natural pair and the store selector.
+// Schedule table image (built by the host plan): per segment and virtual lane
+// NW words (the fields, padded to a multiple of four), four consecutive
+// fields of a lane side by side: field f of virtual lane v is word
+// ((f / 4) NV + v) 4 + f % 4, so a lane fetches four fields with one 16-byte
+// load and a wavefront's such load is 1 KB contiguous. Field 0 is the load
+// selector, 1 + 2 tau / 2 + 2 tau the LDS write / read byte offsets of
+// exchange tau (tau = 0..K), then C words per stage, then the final scales of
+// X and B, the store byte offset of the natural pair and the store selector.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -32,6 +35,7 @@ namespace paro {
 namespace rot {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
@@ -51,40 +55,77 @@ struct Lane {
   static constexpr bool TREG = KMAX <= 8;  // whole schedule held in VGPRs
   static constexpr int KR = TREG ? KMAX : 0;
 
-  const uint32_t* tb;  // this lane's column of the segment's table
+  const uint32_t* tb;  // this lane's first quad in the segment's table
   int K;
   uint32_t ldsel[PPL], stoff[PPL], stsel[PPL];
   float lamX[PPL], lamB[PPL];
   uint32_t wr[KR + 1][PPL], rd[KR + 1][PPL];
   float cf[KR > 0 ? KR : 1][C][PPL];
 
-  static __host__ __device__ constexpr int fields(int K) { return 1 + 2 * (K + 1) + C * K + 4; }
+  static __host__ __device__ constexpr int nfields(int K) { return 1 + 2 * (K + 1) + C * K + 4; }
+  static __host__ __device__ constexpr int fields(int K) { return (nfields(K) + 3) & ~3; }
+
+  // field f of virtual lane lane + 64 h
+  __device__ __forceinline__ uint32_t word(int f, int h) const {
+    return tb[(size_t)(f >> 2) * (NV * 4) + 256 * h + (f & 3)];
+  }
 
   __device__ __forceinline__ void load(const uint32_t* tab, int seg, int K_, int lane) {
     K = KEXACT ? KMAX : K_;
-    tb = tab + (size_t)seg * fields(K) * NV + lane;
-    const int ff = 3 + 2 * K + C * K;
+    tb = tab + (size_t)seg * fields(K) * NV + 4 * lane;
+    if constexpr (KEXACT && TREG) {
+      // the whole schedule with fields(K) / 4 16-byte loads per virtual lane
+      constexpr int NQ = fields(KMAX) / 4;
+      constexpr int ff = 3 + 2 * KMAX + C * KMAX;
 #pragma unroll
-    for (int h = 0; h < PPL; ++h) {
-      ldsel[h] = tb[64 * h];
-      lamX[h] = as_f(tb[(size_t)(ff + 0) * NV + 64 * h]);
-      lamB[h] = as_f(tb[(size_t)(ff + 1) * NV + 64 * h]);
-      stoff[h] = tb[(size_t)(ff + 2) * NV + 64 * h];
-      stsel[h] = tb[(size_t)(ff + 3) * NV + 64 * h];
-      if constexpr (TREG) {
+      for (int h = 0; h < PPL; ++h) {
+        uint32_t wv[4 * NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          const u4 v = *(const u4*)(tb + (size_t)q * (NV * 4) + 256 * h);
+          wv[4 * q] = v.x;
+          wv[4 * q + 1] = v.y;
+          wv[4 * q + 2] = v.z;
+          wv[4 * q + 3] = v.w;
+        }
+        ldsel[h] = wv[0];
 #pragma unroll
         for (int tau = 0; tau <= KR; ++tau) {
-          if (KEXACT || tau <= K) {
-            wr[tau][h] = tb[(size_t)(1 + 2 * tau) * NV + 64 * h];
-            rd[tau][h] = tb[(size_t)(2 + 2 * tau) * NV + 64 * h];
-          }
+          wr[tau][h] = wv[1 + 2 * tau];
+          rd[tau][h] = wv[2 + 2 * tau];
         }
 #pragma unroll
-        for (int t = 0; t < KR; ++t) {
-          if (KEXACT || t < K) {
+        for (int t = 0; t < KR; ++t)
 #pragma unroll
-            for (int e = 0; e < C; ++e)
-              cf[t][e][h] = as_f(tb[(size_t)(3 + 2 * K + C * t + e) * NV + 64 * h]);
+          for (int e = 0; e < C; ++e) cf[t][e][h] = as_f(wv[3 + 2 * KMAX + C * t + e]);
+        lamX[h] = as_f(wv[ff]);
+        lamB[h] = as_f(wv[ff + 1]);
+        stoff[h] = wv[ff + 2];
+        stsel[h] = wv[ff + 3];
+      }
+    } else {
+      const int ff = 3 + 2 * K + C * K;
+#pragma unroll
+      for (int h = 0; h < PPL; ++h) {
+        ldsel[h] = word(0, h);
+        lamX[h] = as_f(word(ff + 0, h));
+        lamB[h] = as_f(word(ff + 1, h));
+        stoff[h] = word(ff + 2, h);
+        stsel[h] = word(ff + 3, h);
+        if constexpr (TREG) {
+#pragma unroll
+          for (int tau = 0; tau <= KR; ++tau) {
+            if (tau <= K) {
+              wr[tau][h] = word(1 + 2 * tau, h);
+              rd[tau][h] = word(2 + 2 * tau, h);
+            }
+          }
+#pragma unroll
+          for (int t = 0; t < KR; ++t) {
+            if (t < K) {
+#pragma unroll
+              for (int e = 0; e < C; ++e) cf[t][e][h] = as_f(word(3 + 2 * K + C * t + e, h));
+            }
           }
         }
       }
@@ -93,15 +134,15 @@ struct Lane {
 
   __device__ __forceinline__ uint32_t wr_off(int tau, int h) const {
     if constexpr (TREG) return wr[tau][h];
-    else return tb[(size_t)(1 + 2 * tau) * NV + 64 * h];
+    else return word(1 + 2 * tau, h);
   }
   __device__ __forceinline__ uint32_t rd_off(int tau, int h) const {
     if constexpr (TREG) return rd[tau][h];
-    else return tb[(size_t)(2 + 2 * tau) * NV + 64 * h];
+    else return word(2 + 2 * tau, h);
   }
   __device__ __forceinline__ float coef(int t, int e, int h) const {
     if constexpr (TREG) return cf[t][e][h];
-    else return as_f(tb[(size_t)(3 + 2 * K + C * t + e) * NV + 64 * h]);
+    else return as_f(word(3 + 2 * K + C * t + e, h));
   }
 
   // Raw fp16 pair word of the natural pair (v) -> fp32 (kept, fetched).

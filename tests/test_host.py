@@ -148,12 +148,21 @@ def fma32(a, b, c):
     return (a.astype(np.float64) * b.astype(np.float64) + c.astype(np.float64)).astype(np.float32)
 
 
+def field_major(img, lay, segs):
+    """The image as [segment][field][virtual lane]: the library stores four
+    consecutive fields of a lane side by side, [segment][words / 4][lane][4]."""
+    nv = lay["seg_ch"] // 2
+    W = lay["words"]
+    assert W % 4 == 0 and img.size == segs * W * nv
+    return img.reshape(segs, W // 4, nv, 4).transpose(0, 1, 3, 2).reshape(segs, W, nv)
+
+
 def emulate_rotate(img, lay, x, K, d):
     nv = lay["seg_ch"] // 2
     W = lay["words"]
     C = 2 if lay["fast"] else 4
     segs = d // lay["seg_ch"]
-    tab = img.reshape(segs, W, nv)
+    tab = field_major(img, lay, segs)
     M = x.shape[0]
     out = np.zeros((M, d), np.float16)
     for s in range(segs):
@@ -204,7 +213,7 @@ def check_slots_conflict_free(img, lay, K, d):
     lanes hit slots distinct mod 8, reads when every 16 consecutive lanes hit
     slots distinct mod 16."""
     nv = lay["seg_ch"] // 2
-    tab = img.reshape(d // lay["seg_ch"], lay["words"], nv)
+    tab = field_major(img, lay, d // lay["seg_ch"])
     for s in range(tab.shape[0]):
         for tau in range(K + 1):
             wr = tab[s, 1 + 2 * tau] // 16
