@@ -21,6 +21,7 @@ HIPCC_FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt",  # IEEE division in the quantizer
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+    "-Wl,-z,defs",                                # no undefined symbols (e.g. a kernel stub) in the library
 ]
 
 

@@ -55,19 +55,26 @@ using namespace w4;
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int GB_M = 128, GB_N = 256, GB_K = 64;
-constexpr int GB_XSTAGE = GB_M * GB_K;  // halfs per X' stage (16 KB)
+constexpr int GB_N = 256, GB_K = 64;
 constexpr int GB_WSTAGE = GB_N * 2;     // 16-byte chunks per weight stage (8 KB)
 constexpr int kRsrcWord3 = 0x00020000;  // gfx9 buffer resource word 3
 // s_waitcnt immediate (gfx9 encoding): vmcnt(0) lgkmcnt(0), expcnt untouched
 constexpr int kWaitVmLgkm0 = 0x70;
+// Output tiles (at 128 tokens) below which 64-token tiles are used: measured
+// on MI355X, 64-token tiles win at 128 tiles (1024 x 4096 -> 4096: 699
+// against 581 TFLOP/s) and lose at 256 (2048 x 4096 -> 4096: 760 against 918).
+constexpr int64_t kHalfTileBelow = 256;
 
-template <int KS>
-__global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// MT: 32-token m tiles per wavefront (4: 128-token workgroup tiles; 2: 64,
+// for layers with few output tiles).
+template <int KS, int MT>
+__global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(2)))
 void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ qw,
                     const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zr,
                     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N,
                     int d, int mblk, int nblk) {
+  constexpr int GB_M = 32 * MT;           // tokens per workgroup tile
+  constexpr int GB_XSTAGE = GB_M * GB_K;  // halfs per X' stage (16 KB at MT = 4)
   __shared__ __attribute__((aligned(1024))) _Float16 X0[KS][GB_XSTAGE], X1[KS][GB_XSTAGE];
   __shared__ __attribute__((aligned(1024))) u4 W0[KS][GB_WSTAGE], W1[KS][GB_WSTAGE];
   __shared__ __attribute__((aligned(16))) uint32_t S0[KS][GB_N], S1[KS][GB_N];
@@ -105,12 +112,15 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
       (void*)(sc + (size_t)nw0 * groups), (short)0, min(N - nw0, GB_N) * groups * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(zr + (size_t)nw0 * groups), (short)0, min(N - nw0, GB_N) * groups, kRsrcWord3);
-  // X' DMA c of wavefront w fills tile rows 8 (4 w + c) .. + 7; the lane at
+  // X' DMA c of wavefront w fills tile rows 8 (MT w + c) .. + 7; the lane at
   // position l % 8 of row l / 8 fetches the source chunk (l % 8) ^ swizzle
+  // (arrays the lambdas below capture are sized for MT = 4: the host pass of
+  // hipcc cannot instantiate lambdas capturing arrays of template-dependent
+  // size)
   uint32_t xoff[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int r = 8 * (4 * w + c) + (lane >> 3);
+  for (int c = 0; c < MT; ++c) {
+    const int r = 8 * (MT * w + c) + (lane >> 3);
     const int row = min(r, M - 1 - m0);
     xoff[c] = (uint32_t)(row * d + 8 * ((lane & 7) ^ ((r >> 1) & 7))) * 2u;
   }
@@ -132,8 +142,8 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)&ss_l[64 * w], 2, (szrow + gi) * 2u, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_void*)&zs_l[64 * w], 1, szrow + gi, 0, 0, 0);
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)&xs[(4 * w + c) * 64 * 8], 16, xoff[c],
+    for (int c = 0; c < MT; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)&xs[(MT * w + c) * 64 * 8], 16, xoff[c],
                                                kglob * GB_K * 2, 0, 0);
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -141,11 +151,11 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
                                                kglob * (GB_K / 2), 0, 0);
   };
 
-  f16v acc[2][4];
+  f16v acc[2][4];  // m tiles mm < MT used
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int mm = 0; mm < 4; ++mm)
+    for (int mm = 0; mm < MT; ++mm)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[j][mm][e] = 0.0f;
 
@@ -168,18 +178,18 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      h8 a[2], b[4];
+      h8 a[2], b[MT];
 #pragma unroll
       for (int j = 0; j < 2; ++j) a[j] = dequant8(wf[j][i], zz[j], ss[j]);
 #pragma unroll
-      for (int mm = 0; mm < 4; ++mm) {
+      for (int mm = 0; mm < MT; ++mm) {
         const int r = 32 * mm + l32;
         b[mm] = *(const h8*)(xb + r * GB_K + 8 * ((4 * g + i) ^ ((r >> 1) & 7)));
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int mm = 0; mm < 4; ++mm)
+        for (int mm = 0; mm < MT; ++mm)
           acc[j][mm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[j], b[mm], acc[j][mm], 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -187,34 +197,36 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
     __builtin_amdgcn_s_barrier();
   };
 
-  dma(0, X0[kg], W0[kg], S0[kg], Z0[kg]);
+  dma(0, &X0[kg][0], &W0[kg][0], &S0[kg][0], &Z0[kg][0]);
   __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
   __builtin_amdgcn_s_barrier();
   for (int kt = 0; kt < KT; kt += 2) {
-    step(kt, X0[kg], W0[kg], S0[kg], Z0[kg], X1[kg], W1[kg], S1[kg], Z1[kg]);
-    if (kt + 1 < KT) step(kt + 1, X1[kg], W1[kg], S1[kg], Z1[kg], X0[kg], W0[kg], S0[kg], Z0[kg]);
+    step(kt, &X0[kg][0], &W0[kg][0], &S0[kg][0], &Z0[kg][0], &X1[kg][0], &W1[kg][0], &S1[kg][0], &Z1[kg][0]);
+    if (kt + 1 < KT) step(kt + 1, &X1[kg][0], &W1[kg][0], &S1[kg][0], &Z1[kg][0], &X0[kg][0], &W0[kg][0], &S0[kg][0], &Z0[kg][0]);
   }
 
   if constexpr (KS == 2) {
     // the second k half hands its partial sums to the first through LDS (the
-    // X' stages 0 of both halves, 32 KB), a quarter of the accumulators at a time
+    // X' stages 0 of both halves: 32 KB at MT = 4, 16 KB at MT = 2), PM m
+    // tiles of one n tile (16 KB per m tile) at a time
+    constexpr int PM = MT / 2;
     float* red = (float*)&X0[0][0];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < MT / PM; ++h) {
         if (kg == 1) {
 #pragma unroll
-          for (int mm = 0; mm < 2; ++mm)
+          for (int mm = 0; mm < PM; ++mm)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) red[((w * 2 + mm) * 16 + e) * 64 + lane] = acc[j][2 * h + mm][e];
+            for (int e = 0; e < 16; ++e) red[((w * PM + mm) * 16 + e) * 64 + lane] = acc[j][PM * h + mm][e];
         }
         __syncthreads();
         if (kg == 0) {
 #pragma unroll
-          for (int mm = 0; mm < 2; ++mm)
+          for (int mm = 0; mm < PM; ++mm)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[j][2 * h + mm][e] += red[((w * 2 + mm) * 16 + e) * 64 + lane];
+            for (int e = 0; e < 16; ++e) acc[j][PM * h + mm][e] += red[((w * PM + mm) * 16 + e) * 64 + lane];
         }
         __syncthreads();
       }
@@ -238,7 +250,7 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
         bv[3] = half_hi(braw.y);
       }
 #pragma unroll
-      for (int mm = 0; mm < 4; ++mm) {
+      for (int mm = 0; mm < MT; ++mm) {
         const int m = m0 + 32 * mm + l32;
         if (m >= M) continue;
         uint2 pk;
@@ -250,6 +262,14 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
   }
 }
 
+template <int KS, int MT>
+void launch_gemm(unsigned blocks, hipStream_t stream, const uint16_t* x, const uint8_t* qweight,
+                 const uint16_t* scales, const uint8_t* zeros, const uint16_t* bias, uint16_t* y,
+                 int64_t M, int64_t N, int64_t d, int mblk, int nblk) {
+  hipLaunchKernelGGL((w4_gemm_kernel<KS, MT>), dim3(blocks), dim3(256 * KS), 0, stream, x, qweight,
+                     scales, zeros, bias, y, (int)M, (int)N, (int)d, mblk, nblk);
+}
+
 }  // namespace
 
 hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
@@ -257,19 +277,21 @@ hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint1
                           int64_t N, int64_t d, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const int nblk = (int)((N + GB_N - 1) / GB_N);
-  const int mblk = (int)((M + GB_M - 1) / GB_M);
+  // 64-token tiles when 128-token ones would leave most SIMDs without work
+  const bool half = (int64_t)nblk * ((M + 127) / 128) < kHalfTileBelow;
+  const int gbm = half ? 64 : 128;
+  const int mblk = (int)((M + gbm - 1) / gbm);
   const int64_t tiles = (int64_t)nblk * mblk;
   // 8 XCDs, each owning every 8th n-block, walked in super-blocks of 8 m-blocks
   const int64_t nbp = (nblk + 7) / 8;
   const int64_t blocks = 8 * nbp * (((int64_t)mblk + 7) / 8) * 8;
   // too few tiles to give every SIMD two wavefronts: split k inside the workgroup
-  if (tiles < 512 && (d / GB_K) % 2 == 0 && d / GB_K >= 4) {
-    hipLaunchKernelGGL(w4_gemm_kernel<2>, dim3((unsigned)blocks), dim3(512), 0, stream, x, qweight,
-                       scales, zeros, bias, y, (int)M, (int)N, (int)d, mblk, nblk);
-  } else {
-    hipLaunchKernelGGL(w4_gemm_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, x, qweight,
-                       scales, zeros, bias, y, (int)M, (int)N, (int)d, mblk, nblk);
-  }
+  const bool ks2 = tiles < 512 && (d / GB_K) % 2 == 0 && d / GB_K >= 4;
+  const unsigned g = (unsigned)blocks;
+  if (half && ks2) launch_gemm<2, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, mblk, nblk);
+  else if (half) launch_gemm<1, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, mblk, nblk);
+  else if (ks2) launch_gemm<2, 4>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, mblk, nblk);
+  else launch_gemm<1, 4>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, mblk, nblk);
   return hipGetLastError();
 }
 

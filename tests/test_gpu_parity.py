@@ -248,8 +248,11 @@ def test_linear_decode(paro, M):
     check_linear(paro, synthetic.decode_x(M), layer, rotated=False)
 
 
+# (the first four and the last two prefill shapes give fewer than 256 output
+# tiles of 128 tokens and run 64-token tiles; (2100, 512, 4112) runs 128-token
+# tiles with k split in halves inside the workgroup, (4200, 256, 4208) without)
 @pytest.mark.parametrize("M,d,N", [(17, 256, 64), (130, 512, 272), (300, 384, 128), (256, 1024, 512),
-                                   (3, 512, 48), (9, 1152, 1040)])
+                                   (3, 512, 48), (9, 1152, 1040), (2100, 512, 4112), (4200, 256, 4208)])
 def test_linear_shapes_with_bias(paro, M, d, N):
     log(f"linear M={M} d={d} N={N}")
     x, layer, b = synthetic.linear_case(seed=M + d + N, M=M, d=d, N=N)
