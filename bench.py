@@ -127,6 +127,43 @@ def settle(torch, fns, min_rounds, seconds=0.5):
     torch.cuda.synchronize()
 
 
+def graph_us(torch, step, n, out=None, seconds=0.3, replays=20):
+    """GPU time per step (us) of n steps captured in one HIP graph and replayed.
+
+    Small-batch calls take a few microseconds, less than launching them from
+    Python costs, so back-to-back eager calls measure the host. The steps are
+    captured once (after eager warm-up calls, which also run any first-call
+    set-up) and the graph is replayed: events around the replays time the
+    GPU's work alone. With ``out`` (a tensor the steps write) the replay's
+    result is compared bit for bit with the eager one; the check is returned."""
+    for i in range(n):
+        step(i)
+    torch.cuda.synchronize()
+    ref = out.clone() if out is not None else None
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            step(i)
+    ok = True
+    for _ in range(3):
+        if out is not None:
+            out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        if ref is not None:
+            ok = ok and bool(torch.equal(out.view(torch.int16), ref.view(torch.int16)))
+    settle(torch, [lambda i: g.replay()], 2, seconds=seconds)
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(replays):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    del g
+    return s.elapsed_time(e) * 1e3 / (replays * n), ok
+
+
 def time_layer(paro, torch, r, xs, qr, qp, steps, warmup, M, N, d):
     """Return per-step and per-kernel timings (ms) of the rotated and plain layer.
 
@@ -325,16 +362,26 @@ def bench_decode(args, paro, torch):
 
         kinds = ("rot", "plain", "rotate_only")
         settle(torch, [lambda i, k=k: run(k, i) for k in kinds], args.warmup + 3)
+        # eager back-to-back calls from Python (host-bound at these sizes; kept for reference)
+        eager = {k: 0.0 for k in kinds}
+        for kind in kinds:
+            n = max(args.steps, 100)
+            s = T.event()
+            for i in range(n):
+                run(kind, i)
+            e = T.event()
+            torch.cuda.synchronize()
+            eager[kind] = s.elapsed_time(e) / n
+        # GPU time: one graph per kind over the ring of weight copies, two
+        # alternating rounds, the mean of both
         timing = {k: 0.0 for k in kinds}
-        for _ in range(2):   # alternating blocks; the mean of both
+        checks = {}
+        for _ in range(2):
             for kind in kinds:
-                n = max(args.steps, 100)
-                s = T.event()
-                for i in range(n):
-                    run(kind, i)
-                e = T.event()
-                torch.cuda.synchronize()
-                timing[kind] += s.elapsed_time(e) / n / 2
+                us, ok = graph_us(torch, lambda i, k=kind: run(k, i), ring,
+                                  out=xr if kind == "rotate_only" else y)
+                timing[kind] += us / 1e3 / 2
+                checks[kind] = checks.get(kind, True) and ok
         # packed codes + fp16 scales + u8 zeros, activations in, outputs out
         wbytes = N * d / 2 + 3 * N * d / 128 + 2 * M * d + 2 * M * N
         res[f"M{M}"] = {
@@ -343,6 +390,8 @@ def bench_decode(args, paro, torch):
             "rotated_gbps": round(wbytes / (timing["rot"] * 1e-3) / 1e9, 1),
             "plain_gbps": round(wbytes / (timing["plain"] * 1e-3) / 1e9, 1),
             "overhead_vs_plain_pct": round(100 * (timing["rot"] - timing["plain"]) / timing["plain"], 1),
+            "eager_python_us": {k: round(1e3 * v, 2) for k, v in eager.items()},
+            "graph_replay_equals_eager": checks,
         }
         total_ms += timing["rot"]
         total_flops += 2.0 * M * N * d
@@ -438,33 +487,38 @@ def bench_chain(args, paro, torch):
 
         kinds = ("rot", "plain", "fp16")
         settle(torch, [lambda k, c=c: chain(c, k % ring) for c in kinds], max(2, args.warmup))
+        # eager chains launched from Python (host-bound for small M; for reference)
+        eager = {c: 0.0 for c in kinds}
+        for kind in kinds:
+            n = max(args.steps, 20)
+            s = T.event()
+            for k in range(n):
+                chain(kind, k % ring)
+            e = T.event()
+            torch.cuda.synchronize()
+            eager[kind] = s.elapsed_time(e) / n
+        # GPU time: each chain captured in a HIP graph (over the ring of weight
+        # copies) and replayed; two alternating rounds, the mean of both
         timing = {c: 0.0 for c in kinds}
-        for _ in range(2):   # alternating blocks; the mean of both
+        checks = {}
+        for _ in range(2):
             for kind in kinds:
-                n = max(args.steps, 20)
-                s = T.event()
-                for k in range(n):
-                    chain(kind, k % ring)
-                e = T.event()
-                torch.cuda.synchronize()
-                timing[kind] += s.elapsed_time(e) / n / 2
-        # per-linear times (events around each launch), rotated W4 and fp16
+                us, ok = graph_us(torch, lambda k, c=kind: chain(c, k % ring), max(ring, 4), out=ys[-1])
+                timing[kind] += us / 1e3 / 2
+                checks[kind] = checks.get(kind, True) and ok
+        # per-linear GPU times, rotated W4 and fp16: each linear in a graph of
+        # its own, alternating its weight copies (small layers then partly hit
+        # the 256 MB Infinity Cache, for both variants alike)
+        def one(kind, i, k):
+            if kind == "rot":
+                paro.paro_w4_linear(plans[i], xs[i], *qr[i][k], y=ys[i], workspace=wsr[i])
+            else:
+                torch.matmul(xs[i], wf[i][k].t(), out=ys[i])
+
         per = {}
         for kind in ("rot", "fp16"):
-            evs = []
-            for k in range(max(args.steps, 20)):
-                row = []
-                for i in range(len(layers)):
-                    a = T.event()
-                    if kind == "rot":
-                        paro.paro_w4_linear(plans[i], xs[i], *qr[i][k % ring], y=ys[i], workspace=wsr[i])
-                    else:
-                        torch.matmul(xs[i], wf[i][k % ring].t(), out=ys[i])
-                    row.append((a, T.event()))
-                evs.append(row)
-            torch.cuda.synchronize()
-            per[kind] = [round(1e3 * float(np.mean([evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(len(evs))])), 1)
-                         for i in range(len(layers))]
+            per[kind] = [round(graph_us(torch, lambda k, c=kind, i=i: one(c, i, k % ring), 4 * ring,
+                                        seconds=0.05)[0], 1) for i in range(len(layers))]
         res[f"M{M}"] = {
             "per_linear_us": {layers[i][0]: {"rotated_w4": per["rot"][i], "fp16": per["fp16"][i]}
                               for i in range(len(layers))},
@@ -472,6 +526,8 @@ def bench_chain(args, paro, torch):
             "fp16_us": round(1e3 * timing["fp16"], 1),
             "speedup_vs_fp16": round(timing["fp16"] / timing["rot"], 3),
             "overhead_vs_plain_pct": round(100 * (timing["rot"] - timing["plain"]) / timing["plain"], 1),
+            "eager_python_us": {k: round(1e3 * v, 1) for k, v in eager.items()},
+            "graph_replay_equals_eager": checks,
         }
         log(f"[bench] chain M={M}: {res[f'M{M}']}")
     first = res[next(iter(res))]
