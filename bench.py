@@ -210,24 +210,28 @@ def time_layer(paro, torch, r, xs, qr, qp, steps, warmup, M, N, d):
         torch.cuda.synchronize()
         return [a.elapsed_time(b) for a, b in ev]
 
+    # the fused entry point (rotation handle passed to paro_w4_linear) on the
+    # same data, timed in the same alternation
+    ws = paro.new_workspace(r, M, N, d)
+
+    def fused_block():
+        for i in range(2):
+            paro.paro_w4_linear(r, xs[i % ring], *qr[i % ring], y=y, workspace=ws)
+        s = T.event()
+        for i in range(steps):
+            paro.paro_w4_linear(r, xs[i % ring], *qr[i % ring], y=y, workspace=ws)
+        e = T.event()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / steps
+
     total, rot, lin = rotated_block()
     plain_ms = plain_block()
+    fused = fused_block() / 2
     _, rot2, lin2 = rotated_block()
     plain_ms += plain_block()
+    fused += fused_block() / 2
     rot += rot2
     lin += lin2
-
-    # the fused entry point (rotation handle passed to paro_w4_linear) on the same data
-    ws = paro.new_workspace(r, M, N, d)
-    for i in range(2):
-        paro.paro_w4_linear(r, xs[i % ring], *qr[i % ring], y=y, workspace=ws)
-    torch.cuda.synchronize()
-    s = T.event()
-    for i in range(steps):
-        paro.paro_w4_linear(r, xs[i % ring], *qr[i % ring], y=y, workspace=ws)
-    e = T.event()
-    torch.cuda.synchronize()
-    fused = s.elapsed_time(e) / steps
 
     return {
         "step_ms": total / steps,
