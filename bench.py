@@ -19,7 +19,8 @@ blocks.
 
 Other workloads (``--workload``): prefill_down (2048 x 14336 -> 4096),
 decode (M = 1, 4, 16 tokens, 4096 -> 4096; weight streaming), sweep (the 27
-rotation-only points, 8192 x d), chain (the seven linears of a Llama-3-8B
+rotation-only points, 8192 x d), sparse (the transform with sparse pairings, in
+which only a fraction of the pairs rotate), chain (the seven linears of a Llama-3-8B
 decoder layer as rotated W4, plain W4 and dense fp16 chains), copy (a plain
 device copy, for calibrating HBM byte counters).
 
@@ -453,6 +454,60 @@ def bench_sweep(args, paro, torch):
     }
 
 
+def bench_sparse(args, paro, torch):
+    """The transform with sparse pairings: each pair keeps its angle with
+    probability `keep` and is an exact identity otherwise; the plan runs the
+    compacted schedule (fewer stages than K)."""
+    import synthetic
+    T = Timer(torch)
+    ring = args.ring or 6
+    shapes = [(8192, 4096), (2048, 14336)]
+    keeps = [1.0, 0.25, 0.1, 0.05]
+    cases = []
+    for M, d in shapes:
+        for keep in keeps:
+            x, layer = synthetic.sparse_rotation_case(seed=7, M=M, d=d, group=128, K=8, keep=keep)
+            _, lay = paro.paro_rotation_plan_host(layer.pairs, layer.theta, layer.alpha, 128)
+            r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, 128)
+            xs = [torch.from_numpy(x).cuda()]
+            for _ in range(ring - 1):
+                xs.append(xs[0].clone())
+            ys = [torch.empty_like(xs[0]) for _ in range(ring)]
+            cases.append({"M": M, "d": d, "keep": keep, "stages": lay["stages"], "fast": lay["fast"],
+                          "r": r, "xs": xs, "ys": ys, "ms": []})
+    fns = [lambda i, c=c: paro.paro_rotate(c["r"], c["xs"][i % ring], c["ys"][i % ring]) for c in cases]
+    settle(torch, fns, args.warmup + 2)
+    n = max(args.steps, 50)
+    for _ in range(2):  # two rounds over all cases against clock drift
+        for c, fn in zip(cases, fns):
+            s = T.event()
+            for i in range(n):
+                fn(i)
+            e = T.event()
+            torch.cuda.synchronize()
+            c["ms"].append(s.elapsed_time(e) / n)
+    pts = []
+    for c in cases:
+        ms = min(c["ms"])
+        gbps = 4.0 * c["M"] * c["d"] / (ms * 1e-3) / 1e9
+        pts.append({"tokens": c["M"], "d": c["d"], "keep": c["keep"], "stages": c["stages"],
+                    "factored": c["fast"], "us": round(ms * 1e3, 2), "gbps": round(gbps, 1),
+                    "frac": round(gbps / HBM_PEAK_GBPS, 4)})
+        log(f"[sparse] {c['M']}x{c['d']} keep={c['keep']}: {c['stages']} stages, "
+            f"{ms*1e3:.1f} us, {gbps:.0f} GB/s")
+    head = [q for q in pts if q["tokens"] == 8192 and q["keep"] == 0.1][0]
+    return {
+        "metric": "rotation HBM GB/s with sparse pairings (paro_rotate)", "value": head["gbps"],
+        "unit": "GB/s", "n_gpus": 1, "steps": n, "warmup": args.warmup,
+        "ms_per_step": round(head["us"] / 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "rotation_sparse_pairings_8192x4096_keep0.1", "group": 128, "K": 8},
+        "points": pts,
+        "roofline": {"bound": "hbm", "achieved": head["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": head["frac"], "traffic": None},
+    }
+
+
 def bench_chain(args, paro, torch):
     """The seven linears of one Llama-3-8B decoder layer in sequence (q, k, v, o,
     gate, up, down; attention and activations left out), as rotated W4G128,
@@ -573,7 +628,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill_mlp",
-                    choices=["prefill_mlp", "prefill_down", "decode", "sweep", "tiny", "copy", "chain"])
+                    choices=["prefill_mlp", "prefill_down", "decode", "sweep", "sparse", "tiny", "copy",
+                             "chain"])
     ap.add_argument("--ring", type=int, default=0, help="distinct input copies cycled (0 = auto)")
     ap.add_argument("--decode-m", default="1,4,16", help="token counts of the decode workload")
     ap.add_argument("--chain-m", default="1,16,2048", help="token counts of the layer-chain workload")
@@ -608,6 +664,8 @@ def main():
         out = bench_sweep(args, paro, torch)
     elif args.workload == "chain":
         out = bench_chain(args, paro, torch)
+    elif args.workload == "sparse":
+        out = bench_sparse(args, paro, torch)
     else:
         out = bench_copy(args, torch)
     print(json.dumps(out), flush=True)

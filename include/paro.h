@@ -87,8 +87,11 @@ typedef struct paro_rotation paro_rotation;
  *          channel appears exactly once and i / group == j / group. The
  *          order of pairs inside a stage is free; the order (i, j) inside a
  *          pair selects the sign as in the update above (swapping i and j is
- *          the same as negating theta). Partial pairings are expressed with
- *          theta = 0, which is an exact identity.
+ *          the same as negating theta). Partial and sparse pairings (only
+ *          some pairs rotate; paper notes "核心观察") are expressed with
+ *          theta = 0, an exact identity; the activation side then skips the
+ *          identities and runs fewer stages where the remaining rotations
+ *          allow it (see paro_rotation_plan_host's layout[4]).
  *   theta  host float [K][d/2], radians, finite. The library evaluates
  *          c = (float)cos((double)theta), s = (float)sin((double)theta) on the
  *          host.
@@ -213,13 +216,20 @@ int paro_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qwe
  *               [layout[2] / 4][virtual lane][4], four consecutive fields of
  *               a lane side by side),
  *   layout[3] = 1 if the factored two-FMA stage form is used, 0 for the
- *               general 2x2 form.
+ *               general 2x2 form,
+ *   layout[4] = stages the activation schedule executes: K for a plan
+ *               without identities; with pairs of theta == 0 (exact
+ *               identities, a partial or sparse pairing) the identities are
+ *               dropped and each other rotation goes to the first stage after
+ *               the last rotation on either of its channels, which gives the
+ *               length of the longest chain of rotations linked by shared
+ *               channels (<= K).
  * Runs the same validation as paro_rotation_create and returns its errors;
  * PARO_ERR_WORKSPACE when out is non-NULL and out_bytes is too small.
  */
 int paro_rotation_plan_host(int64_t d, int32_t group, int32_t K, const int32_t* pairs,
                             const float* theta, const float* alpha, void* out, size_t out_bytes,
-                            size_t* needed, int32_t layout[4]);
+                            size_t* needed, int32_t layout[5]);
 
 #ifdef __cplusplus
 }

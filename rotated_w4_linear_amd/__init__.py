@@ -205,11 +205,12 @@ def paro_rotation_plan_host(pairs, theta, alpha, group: int) -> Tuple[np.ndarray
     d = int(alpha.shape[0])
     K = int(pairs.shape[0]) if pairs.ndim == 3 else 0
     need = ctypes.c_size_t()
-    lay = (ctypes.c_int32 * 4)()
+    lay = (ctypes.c_int32 * 5)()
     _check(lib.paro_rotation_plan_host(d, group, K, _ptr(pairs), _ptr(theta), _ptr(alpha), None,
                                        0, ctypes.byref(need), lay))
     img = np.zeros(need.value // 4, dtype=np.uint32)
     _check(lib.paro_rotation_plan_host(d, group, K, _ptr(pairs), _ptr(theta), _ptr(alpha),
                                        img.ctypes.data_as(ctypes.c_void_p), need.value,
                                        ctypes.byref(need), lay))
-    return img, {"seg_ch": lay[0], "ppl": lay[1], "words": lay[2], "fast": bool(lay[3])}
+    return img, {"seg_ch": lay[0], "ppl": lay[1], "words": lay[2], "fast": bool(lay[3]),
+                 "stages": lay[4]}

@@ -70,7 +70,7 @@ const char* paro_last_error(void) { return g_last_error.c_str(); }
 
 int paro_rotation_plan_host(int64_t d, int32_t group, int32_t K, const int32_t* pairs,
                             const float* theta, const float* alpha, void* out, size_t out_bytes,
-                            size_t* needed, int32_t layout[4]) {
+                            size_t* needed, int32_t layout[5]) {
   RotPlanHost plan;
   int st = build_rotation_plan(d, group, K, pairs, theta, alpha, &plan);
   if (st != PARO_OK) return st;
@@ -81,6 +81,7 @@ int paro_rotation_plan_host(int64_t d, int32_t group, int32_t K, const int32_t* 
     layout[1] = plan.lay.ppl;
     layout[2] = plan.lay.words;
     layout[3] = plan.lay.fast ? 1 : 0;
+    layout[4] = plan.lay.stages;
   }
   if (out) {
     if (out_bytes < bytes) {

@@ -396,7 +396,7 @@ hipError_t launch_t(const uint16_t* x, const uint8_t* qw, const uint16_t* sc, co
   uint32_t* cnt = (uint32_t*)ws;
   float* part = (float*)((char*)ws + kDecodeCounterBytes);
   const uint32_t* tab = r ? r->d_table : nullptr;
-  const int K = r ? r->K : 0;
+  const int K = r ? r->lay.stages : 0;
   constexpr int kMaxNb = (int)(kDecodeCounterBytes / 4);
   const int sys = ksl > 1 && !xcd_dispatch_is_round_robin();
   for (int nb0 = 0; nb0 < nbl_all; nb0 += kMaxNb) {
@@ -416,9 +416,9 @@ hipError_t launch_plan(const uint16_t* x, const uint8_t* qw, const uint16_t* sc,
                        const uint16_t* bias, uint16_t* y, int m, int n, int k,
                        const paro_rotation* r, void* ws, hipStream_t stream) {
   if (!r) return launch_t<false, 0, true, true, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
-  if (r->K == 0) return launch_t<true, 0, true, true, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
+  if (r->lay.stages == 0) return launch_t<true, 0, true, true, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
   if (r->lay.fast) {
-    if (r->K == 8) return launch_t<true, 8, true, true, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
+    if (r->lay.stages == 8) return launch_t<true, 8, true, true, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
     return launch_t<true, 8, false, true, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
   }
   return launch_t<true, 8, false, false, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
@@ -427,7 +427,7 @@ hipError_t launch_plan(const uint16_t* x, const uint8_t* qw, const uint16_t* sc,
 }  // namespace
 
 bool decode_fuses_rotation(const paro_rotation* r) {
-  return r == nullptr || (r->lay.ppl == 1 && r->K <= 8);
+  return r == nullptr || (r->lay.ppl == 1 && r->lay.stages <= 8);
 }
 
 hipError_t launch_w4_decode(const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,

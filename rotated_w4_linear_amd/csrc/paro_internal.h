@@ -48,6 +48,7 @@ struct RotPlanLayout {
   int nv = 64;           // virtual lanes per segment
   int coef = 2;          // coefficients per stage (2 factored, 4 general)
   int words = 0;         // words per virtual lane (fields rounded up to four)
+  int stages = 0;        // stages the activation schedule executes (<= K)
   bool fast = true;      // factored two-FMA stage form
 };
 

@@ -42,6 +42,150 @@ struct SegPairings {
   std::vector<std::vector<double>> c, s;
 };
 
+// Identity pairs for the factored stage form, which cannot swap the members of
+// an identity pair: a lane that holds one has to keep the channel it kept at
+// the exchange before. On entry S holds the segment's rotations at stages
+// 1..KA (partner -1 where a stage leaves a channel free) and the natural
+// pairings of stages 0 and KA+1 that load and store it.
+//
+// Every rotation, and every natural pair of stage 0, is a node with one bit:
+// whether its lower channel is the one that stays in its lane at the exchange
+// right after it. A channel's standing at exchange tau is then fixed by the
+// last node it belongs to up to stage tau (an identity pair changes nothing).
+// The lanes work out when every pair of stage tau+1 has one member that stays
+// and one that does not; for a rotation, or a natural pair of stage KA+1, that
+// ties the bits of its members' previous nodes with a parity. A node meets at
+// most two such ties, one through each member, so the ties form paths and
+// cycles; going once round a cycle enters and leaves every node through
+// different members, the parities cancel, and the ties always have a solution
+// (found with a union-find that tracks parities). Free bits go, in stage order,
+// to whichever keeps the larger of a rotation's |cos| and |sin| on the register
+// it stays in. With the bits fixed, the channels a stage leaves free split
+// evenly into those that stay at the exchange before it and those that do not;
+// pairing one half with the other gives identity pairs whose lanes keep their
+// registers. kset[tau][ch] says whether ch stays at exchange tau.
+bool fill_kept(SegPairings& S, int KA, double tiny, std::vector<std::vector<uint8_t>>& kset) {
+  const int C = S.C;
+  struct Node { int stage, lo, hi, prev_lo, prev_hi; };
+  std::vector<Node> nodes;
+  std::vector<int> uf_par, uf_x;
+  auto add_node = [&](Node n) {
+    uf_par.push_back((int)nodes.size());
+    uf_x.push_back(0);
+    nodes.push_back(n);
+    return (int)nodes.size() - 1;
+  };
+  auto find = [&](int v, int& parity) {
+    int p = 0, u = v;
+    while (uf_par[u] != u) {
+      p ^= uf_x[u];
+      u = uf_par[u];
+    }
+    for (int w = v, pw = p; uf_par[w] != w;) {  // path compression
+      const int nx = uf_par[w], xw = uf_x[w];
+      uf_par[w] = u;
+      uf_x[w] = pw;
+      pw ^= xw;
+      w = nx;
+    }
+    parity = p;
+    return u;
+  };
+  std::vector<int> node_of(C);
+  std::vector<std::vector<int>> node_at(KA + 1, std::vector<int>(C, -1));
+  for (int ch = 0; ch < C; ch += 2) node_of[ch] = node_of[ch + 1] = add_node({0, ch, ch + 1, -1, -1});
+  for (int ch = 0; ch < C; ++ch) node_at[0][ch] = node_of[ch];
+  for (int tt = 1; tt <= KA + 1; ++tt) {
+    for (int u = 0; u < C; ++u) {
+      const int w = S.partner[tt][u];
+      if (w < u) continue;  // free (-1), or visited from the lower member
+      const int nu = node_of[u], nw = node_of[w];
+      // stays(ch) = bit(node) ^ (ch is not the node's lower member); one of u, w stays
+      const int rel = 1 ^ (u != nodes[nu].lo) ^ (w != nodes[nw].lo);
+      int pu, pw;
+      const int ru = find(nu, pu), rw = find(nw, pw);
+      if (ru == rw) {
+        if ((pu ^ pw) != rel) return false;
+      } else {
+        uf_par[ru] = rw;
+        uf_x[ru] = pu ^ pw ^ rel;
+      }
+      if (tt <= KA) node_of[u] = node_of[w] = node_at[tt][u] = node_at[tt][w] = add_node({tt, u, w, nu, nw});
+    }
+  }
+  // a rotation whose cos (or sin) is below `tiny` has to keep (or swap) the
+  // channel in its register: a tie with the previous node of its lower member
+  // (these extra ties can contradict the others; the caller then falls back)
+  for (size_t n = 0; n < nodes.size(); ++n) {
+    const Node& nd = nodes[n];
+    if (nd.stage == 0) continue;
+    const double c = std::fabs(S.c[nd.stage][nd.lo]), s = std::fabs(S.s[nd.stage][nd.lo]);
+    if (c >= tiny && s >= tiny) continue;
+    // lo stays at both exchanges iff bit(n) ^ bit(prev) == (lo is not prev's lower member)
+    const int rel = (nd.lo != nodes[nd.prev_lo].lo ? 1 : 0) ^ (c < tiny ? 1 : 0);
+    int pa, pb;
+    const int ra = find((int)n, pa), rb = find(nd.prev_lo, pb);
+    if (ra == rb) {
+      if ((pa ^ pb) != rel) return false;
+    } else {
+      uf_par[ra] = rb;
+      uf_x[ra] = pa ^ pb ^ rel;
+    }
+  }
+  // bits, in stage order
+  std::vector<int> root_bit(nodes.size(), -1), bit(nodes.size(), 0);
+  auto stays = [&](int n, int ch) { return bit[n] ^ (ch != nodes[n].lo ? 1 : 0); };
+  for (size_t n = 0; n < nodes.size(); ++n) {
+    int parity;
+    const int root = find((int)n, parity);
+    if (root_bit[root] < 0) {
+      int b = 1;
+      const Node& nd = nodes[n];
+      if (nd.stage > 0) {
+        const int x = stays(nd.prev_lo, nd.lo) ? nd.lo : nd.hi;  // in the register that stays
+        const bool keep = std::fabs(S.c[nd.stage][nd.lo]) >= std::fabs(S.s[nd.stage][nd.lo]);
+        b = ((x == nd.lo) == keep) ? 1 : 0;
+      }
+      root_bit[root] = b ^ parity;
+    }
+    bit[n] = root_bit[root] ^ parity;
+  }
+  // standings per exchange
+  kset.assign(KA + 1, std::vector<uint8_t>(C, 0));
+  for (int ch = 0; ch < C; ++ch) node_of[ch] = node_at[0][ch];
+  for (int tau = 0; tau <= KA; ++tau) {
+    for (int ch = 0; ch < C; ++ch) {
+      if (node_at[tau][ch] >= 0) node_of[ch] = node_at[tau][ch];
+      kset[tau][ch] = (uint8_t)stays(node_of[ch], ch);
+    }
+  }
+  // identity pairs: a free channel that stays with a free one that does not,
+  // the previous stage's partner first
+  for (int tt = 1; tt <= KA; ++tt) {
+    auto pair_id = [&](int a, int b) {
+      S.partner[tt][a] = b;
+      S.partner[tt][b] = a;
+      S.first[tt][std::min(a, b)] = 1;
+    };
+    std::vector<int> A, B;
+    for (int ch = 0; ch < C; ++ch) {
+      if (S.partner[tt][ch] >= 0) continue;
+      const int q = S.partner[tt - 1][ch];
+      if (kset[tt - 1][ch] && S.partner[tt][q] < 0 && !kset[tt - 1][q]) {
+        pair_id(ch, q);
+        continue;
+      }
+      (kset[tt - 1][ch] ? A : B).push_back(ch);
+    }
+    std::vector<int> A2, B2;
+    for (int ch : A) if (S.partner[tt][ch] < 0) A2.push_back(ch);
+    for (int ch : B) if (S.partner[tt][ch] < 0) B2.push_back(ch);
+    if (A2.size() != B2.size()) return false;
+    for (size_t i = 0; i < A2.size(); ++i) pair_id(A2[i], B2[i]);
+  }
+  return true;
+}
+
 // Kuhn augmenting path on a bipartite multigraph given as edge lists.
 bool augment(int u, const std::vector<std::vector<std::pair<int, int>>>& adj,
              std::vector<int>& match_r, std::vector<int>& match_edge_r, std::vector<char>& seen,
@@ -204,6 +348,44 @@ int build_rotation_plan(int64_t d, int32_t group, int32_t K, const int32_t* pair
     }
   }
 
+  // ---- stage compaction for partial pairings ------------------------------------
+  // A pair with theta == 0 is an exact identity. When a plan has identities
+  // (a partial or sparse pairing), they are dropped, and every other rotation
+  // moves to the earliest activation stage after the last rotation on either
+  // of its channels: rotations keep their order on every channel, and
+  // rotations on disjoint pairs commute, so the product is unchanged. The
+  // activation kernel then executes KA <= K stages (the longest chain of
+  // rotations linked by shared channels); channels a stage leaves free get
+  // identity pairs chosen below. The weight transform above keeps the K
+  // stages in their canonical order.
+  std::vector<int> eff((size_t)K * half, -1);  // activation stage of each pair, -1: identity
+  int KA = K;
+  bool has_identity = false;
+  {
+    std::vector<int> last(d, -1);
+    int ka = 0;
+    bool identity = false;
+    for (int t = 0; t < K; ++t)
+      for (int64_t p = 0; p < half; ++p) {
+        const int64_t i = pairs[(t * half + p) * 2], j = pairs[(t * half + p) * 2 + 1];
+        if (theta[t * half + p] == 0.0f) {
+          identity = true;
+          continue;
+        }
+        const int e = std::max(last[i], last[j]) + 1;
+        eff[(size_t)t * half + p] = e;
+        last[i] = last[j] = e;
+        ka = std::max(ka, e + 1);
+      }
+    has_identity = identity;
+    if (identity) {
+      KA = ka;
+    } else {
+      for (int t = 0; t < K; ++t)
+        for (int64_t p = 0; p < half; ++p) eff[(size_t)t * half + p] = t;
+    }
+  }
+
   // ---- activation schedule ------------------------------------------------------
   for (int attempt = 0; attempt < 2; ++attempt) {
     const bool fast = attempt == 0;
@@ -213,7 +395,8 @@ int build_rotation_plan(int64_t d, int32_t group, int32_t K, const int32_t* pair
     lay.nv = nv;
     lay.fast = fast;
     lay.coef = fast ? 2 : 4;
-    lay.words = rot_words(K, lay.coef);
+    lay.words = rot_words(KA, lay.coef);
+    lay.stages = KA;
     std::vector<uint32_t> table((size_t)segs * lay.words * nv, 0);
     bool ok = true;
 
@@ -221,27 +404,67 @@ int build_rotation_plan(int64_t d, int32_t group, int32_t K, const int32_t* pair
       const int64_t base = (int64_t)sg * seg_ch;
       SegPairings S;
       S.C = seg_ch;
-      S.partner.assign(K + 2, std::vector<int>(seg_ch));
-      S.first.assign(K + 2, std::vector<uint8_t>(seg_ch, 0));
-      S.c.assign(K + 2, std::vector<double>(seg_ch, 1.0));
-      S.s.assign(K + 2, std::vector<double>(seg_ch, 0.0));
+      S.partner.assign(KA + 2, std::vector<int>(seg_ch, -1));
+      S.first.assign(KA + 2, std::vector<uint8_t>(seg_ch, 0));
+      S.c.assign(KA + 2, std::vector<double>(seg_ch, 1.0));
+      S.s.assign(KA + 2, std::vector<double>(seg_ch, 0.0));
       for (int ch = 0; ch < seg_ch; ++ch) {
-        S.partner[0][ch] = S.partner[K + 1][ch] = ch ^ 1;
-        S.first[0][ch] = S.first[K + 1][ch] = (ch & 1) == 0;
+        S.partner[0][ch] = S.partner[KA + 1][ch] = ch ^ 1;
+        S.first[0][ch] = S.first[KA + 1][ch] = (ch & 1) == 0;
       }
       for (int t = 0; t < K; ++t) {
         for (int64_t p = 0; p < half; ++p) {
+          const int e = eff[(size_t)t * half + p];
+          if (e < 0) continue;  // identity
           int64_t i = pairs[(t * half + p) * 2], j = pairs[(t * half + p) * 2 + 1];
           if (i < base || i >= base + seg_ch) continue;
           int li = (int)(i - base), lj = (int)(j - base);
           double th = (double)theta[t * half + p];
-          S.partner[t + 1][li] = lj;
-          S.partner[t + 1][lj] = li;
-          S.first[t + 1][li] = 1;
-          S.first[t + 1][lj] = 0;
-          S.c[t + 1][li] = S.c[t + 1][lj] = std::cos(th);
-          S.s[t + 1][li] = S.s[t + 1][lj] = std::sin(th);
+          S.partner[e + 1][li] = lj;
+          S.partner[e + 1][lj] = li;
+          S.first[e + 1][li] = 1;
+          S.first[e + 1][lj] = 0;
+          S.c[e + 1][li] = S.c[e + 1][lj] = std::cos(th);
+          S.s[e + 1][li] = S.s[e + 1][lj] = std::sin(th);
         }
+      }
+      // Channels no rotation of a stage touches get identity pairs (c = 1,
+      // s = 0). The factored form cannot swap the two members of an identity
+      // pair (one of its coefficients would be zero), so the lane that holds
+      // one must keep the channel already in its register. fill_kept() picks
+      // the identity pairs so that this always holds: see there. The general
+      // form takes any identity pairs: a free channel is paired with its
+      // partner of the previous stage where both are free, the rest in
+      // channel order.
+      // Coefficient bounds. A factored stage computes c*a + s*b as
+      // c*(a + (s/c)*b): one fp32 fma whose rounding error is relative to the
+      // result, so a small leading coefficient costs no accuracy (a quarter
+      // turn, |cos| ~ 4e-8 for a float angle, is fine). Only a leading
+      // coefficient below `tiny` (in practice an exact zero) is refused, and the
+      // deferred scales and ratios stay within [lo, hi] so that the registers
+      // keep far from the fp32 range limits.
+      const double lo = std::ldexp(1.0, -60), hi = std::ldexp(1.0, 60), tiny = std::ldexp(1.0, -40);
+      std::vector<std::vector<uint8_t>> kset;  // kset[tau][ch]: ch stays in its lane at exchange tau
+      if (fast && has_identity) {
+        if (!fill_kept(S, KA, tiny, kset)) { ok = false; break; }
+      } else {
+      for (int tt = 1; tt <= KA; ++tt) {
+        auto pair_id = [&](int a2, int b2) {
+          S.partner[tt][a2] = b2;
+          S.partner[tt][b2] = a2;
+          S.first[tt][std::min(a2, b2)] = 1;
+        };
+        for (int ch = 0; ch < seg_ch; ++ch) {
+          const int q = S.partner[tt - 1][ch];
+          if (S.partner[tt][ch] < 0 && q >= 0 && q != ch && S.partner[tt][q] < 0) pair_id(ch, q);
+        }
+        int pending = -1;
+        for (int ch = 0; ch < seg_ch; ++ch) {
+          if (S.partner[tt][ch] >= 0) continue;
+          if (pending < 0) pending = ch;
+          else { pair_id(pending, ch); pending = -1; }
+        }
+      }
       }
 
       // mu(out <- in) of the pairing tt's 2x2 update, for two members of one pair
@@ -252,17 +475,18 @@ int build_rotation_plan(int64_t d, int32_t group, int32_t K, const int32_t* pair
         return ii ? s : c;
       };
 
+
       LaneState L;
-      L.kept.assign(K + 1, std::vector<int>(nv));
-      L.fetched.assign(K + 1, std::vector<int>(nv));
-      L.src.assign(K + 1, std::vector<int>(nv));
+      L.kept.assign(KA + 1, std::vector<int>(nv));
+      L.fetched.assign(KA + 1, std::vector<int>(nv));
+      L.src.assign(KA + 1, std::vector<int>(nv));
       std::vector<int> ch_a(nv), ch_b(nv), lane_of(seg_ch);
       for (int v = 0; v < nv; ++v) {
         ch_a[v] = 2 * v;
         ch_b[v] = 2 * v + 1;
       }
 
-      for (int tau = 0; tau <= K; ++tau) {
+      for (int tau = 0; tau <= KA; ++tau) {
         for (int v = 0; v < nv; ++v) lane_of[ch_a[v]] = lane_of[ch_b[v]] = v;
         const std::vector<int>& nxt = S.partner[tau + 1];
         std::vector<char> done(nv, 0);
@@ -292,7 +516,9 @@ int build_rotation_plan(int64_t d, int32_t group, int32_t K, const int32_t* pair
             }
           }
           int o = score[1] > score[0] ? 1 : 0;
+          if (!kset.empty()) o = kset[tau][ch_a[L0]] ? 0 : 1;
           for (const auto& rc : orient[o]) {
+            if (!kset.empty() && !kset[tau][rc.keep]) ok = false;
             L.kept[tau][rc.lane] = rc.keep;
             L.fetched[tau][rc.lane] = rc.fetch;
             L.src[tau][rc.lane] = rc.from;
@@ -310,9 +536,8 @@ int build_rotation_plan(int64_t d, int32_t group, int32_t K, const int32_t* pair
       for (int ch = 0; ch < seg_ch; ++ch) lam[ch] = 1.0 / (double)alpha[base + ch];
       uint32_t* T = &table[(size_t)sg * lay.words * nv];
       auto put = [&](int field, int v, uint32_t w) { T[((size_t)(field >> 2) * nv + v) * 4 + (field & 3)] = w; };
-      const double lo = std::ldexp(1.0, -60), hi = std::ldexp(1.0, 60), tiny = std::ldexp(1.0, -20);
       auto in_range = [&](double x) { double a = std::fabs(x); return a >= lo && a <= hi; };
-      for (int t = 0; t < K && ok; ++t) {
+      for (int t = 0; t < KA && ok; ++t) {
         const int tt = t + 1;
         std::vector<double> new_lam = lam;
         for (int v = 0; v < nv; ++v) {
@@ -320,7 +545,7 @@ int build_rotation_plan(int64_t d, int32_t group, int32_t K, const int32_t* pair
           int p = L.kept[t + 1][v];
           int q = (p == a) ? b : a;
           double mpa = mu(tt, p, a), mpb = mu(tt, p, b), mqa = mu(tt, q, a), mqb = mu(tt, q, b);
-          const int f0 = 3 + 2 * K + lay.coef * t;
+          const int f0 = 3 + 2 * KA + lay.coef * t;
           if (fast) {
             if (std::fabs(mpa) < tiny || std::fabs(mqb) < tiny) { ok = false; break; }
             double lp = mpa * lam[a], lq = mqb * lam[b];
@@ -350,7 +575,7 @@ int build_rotation_plan(int64_t d, int32_t group, int32_t K, const int32_t* pair
       for (int v = 0; v < nv; ++v) {
         put(0, v, L.kept[0][v] == 2 * v ? kSelLoadKeep : kSelLoadSwap);
       }
-      for (int tau = 0; tau <= K; ++tau) {
+      for (int tau = 0; tau <= KA; ++tau) {
         std::vector<int> slot = plan_lds_slots(L.src[tau]);
         if (slot.empty()) { ok = false; break; }
         for (int v = 0; v < nv; ++v) {
@@ -359,9 +584,9 @@ int build_rotation_plan(int64_t d, int32_t group, int32_t K, const int32_t* pair
         }
       }
       if (!ok) break;
-      const int ff = 3 + 2 * K + lay.coef * K;
+      const int ff = 3 + 2 * KA + lay.coef * KA;
       for (int v = 0; v < nv; ++v) {
-        int kx = L.kept[K][v], kb = L.fetched[K][v];
+        int kx = L.kept[KA][v], kb = L.fetched[KA][v];
         int q = kx / 2;  // natural pair index the lane stores
         put(ff + 0, v, fbits((float)lam[kx]));
         put(ff + 1, v, fbits((float)lam[kb]));

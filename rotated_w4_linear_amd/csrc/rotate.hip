@@ -121,7 +121,7 @@ hipError_t launch_t(const paro_rotation* r, const uint16_t* x, uint16_t* y, int6
   const int64_t waves = chunks * segs;
   const int64_t blocks = (waves + 3) / 4;
   hipLaunchKernelGGL((rotate_kernel<PPL, KMAX, KEXACT, FAST, T>), dim3((unsigned)blocks),
-                     dim3(256), 0, stream, x, y, r->d_table, (int)M, r->d, segs, r->K, (int)tpw);
+                     dim3(256), 0, stream, x, y, r->d_table, (int)M, r->d, segs, r->lay.stages, (int)tpw);
   return hipGetLastError();
 }
 
@@ -133,7 +133,7 @@ template <int PPL>
 hipError_t launch_ppl(const paro_rotation* r, const uint16_t* x, uint16_t* y, int64_t M,
                       hipStream_t stream) {
   constexpr int T = PPL == 1 ? 8 : 4;
-  const int K = r->K;
+  const int K = r->lay.stages;  // stages the schedule executes
   const int64_t tw = kTargetWaves;
   if (K == 0) return launch_t<PPL, 0, true, true, T>(r, x, y, M, stream, tw);
   if (r->lay.fast) {

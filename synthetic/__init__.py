@@ -190,6 +190,18 @@ def rotation_case(seed: int, M: int, d: int, group: int, K: int, x_dist="normal"
     return x, Layer(None, pairs, theta, alpha, group)
 
 
+def sparse_rotation_case(seed: int, M: int, d: int, group: int, K: int, keep: float):
+    """A rotation case where each pair carries its angle with probability
+    ``keep`` and is otherwise an exact identity (theta = 0): a sparse pairing
+    in which only a fraction of the channel pairs rotate (a random stand-in for
+    keeping only the most useful pairs)."""
+    x, layer = rotation_case(seed, M, d, group, K)
+    rng = rng_for(1500, seed)
+    drop = rng.random(layer.theta.shape) >= keep
+    layer.theta[drop] = 0.0
+    return x, layer
+
+
 def linear_case(seed: int, M: int, d: int, N: int, group: int = 128, K: int = 8, bias=True):
     """A free-form linear-layer case for tests (seeded by ``seed``)."""
     rng = rng_for(2000, seed)

@@ -89,17 +89,50 @@ def test_rotate_shapes(paro, G, K, d, M):
 
 
 def test_rotate_general_form_and_identity_angles(paro):
-    log("rotate with theta=0 pairs (general 2x2 form)")
+    log("rotate with theta=1e-7 pairs (general 2x2 form)")
     x, layer = synthetic.rotation_case(seed=11, M=33, d=512, group=128, K=8)
-    layer.theta[:, ::3] = 0.0
+    theta0 = layer.theta.copy()
+    layer.theta[:, ::3] = 1e-7
     img, lay = paro.paro_rotation_plan_host(layer.pairs, layer.theta, layer.alpha, 128)
     assert not lay["fast"]
+    check_rotation(paro, x, layer)
+    log("rotate with theta=0 pairs (identity pairs, factored form)")
+    layer.theta[:] = theta0
+    layer.theta[:, ::3] = 0.0
+    img, lay = paro.paro_rotation_plan_host(layer.pairs, layer.theta, layer.alpha, 128)
+    assert lay["fast"]
     check_rotation(paro, x, layer)
     # all angles zero: X' = X / alpha exactly up to the fp16 rounding
     layer.theta[:] = 0.0
     _, got = check_rotation(paro, x, layer)
     want = (x.astype(np.float64) / layer.alpha.astype(np.float64)).astype(np.float16)
     assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
+@pytest.mark.parametrize("keep,G,K,d,M", [(0.1, 128, 8, 4096, 300), (0.1, 128, 8, 4096, 1),
+                                           (0.05, 128, 8, 14336, 70), (0.1, 64, 8, 512, 37),
+                                           (0.1, 256, 8, 1024, 19), (0.02, 128, 16, 512, 9)])
+def test_rotate_sparse_pairing(paro, keep, G, K, d, M):
+    """Sparse pairings (most theta = 0): the kernel runs the compacted schedule
+    of fewer stages than K."""
+    log(f"rotate sparse keep={keep} G={G} K={K} d={d} M={M}")
+    x, layer = synthetic.sparse_rotation_case(seed=int(keep * 1000) + d + M, M=M, d=d, group=G,
+                                              K=K, keep=keep)
+    _, lay = paro.paro_rotation_plan_host(layer.pairs, layer.theta, layer.alpha, G)
+    assert lay["stages"] < K and lay["fast"]
+    check_rotation(paro, x, layer)
+
+
+@pytest.mark.parametrize("keep", [1.0, 0.1])
+def test_rotate_quarter_turns(paro, keep):
+    """Quarter turns (cos ~ 4e-8 for the float angle) in dense and sparse
+    pairings: the factored form carries them with large coefficient ratios."""
+    log(f"rotate quarter turns keep={keep}")
+    x, layer = synthetic.sparse_rotation_case(seed=23, M=45, d=2048, group=128, K=8, keep=keep)
+    nz = np.argwhere(layer.theta != 0.0)
+    for t, p in nz[::50 if keep == 1.0 else 16]:
+        layer.theta[t, p] = np.float32(np.pi / 2)
+    check_rotation(paro, x, layer)
 
 
 def test_rotate_inplace_and_empty(paro):
@@ -364,11 +397,26 @@ def test_linear_rejects_other_rotation_groups(paro, group):
 
 
 def test_decode_general_form(paro):
-    log("decode with theta=0 pairs (general 2x2 form, fused)")
+    log("decode with theta=1e-7 pairs (general 2x2 form, fused)")
     x, layer, b = synthetic.linear_case(seed=71, M=6, d=768, N=144)
-    layer.theta[:, ::3] = 0.0
+    layer.theta[:, ::3] = 1e-7
     _, lay = paro.paro_rotation_plan_host(layer.pairs, layer.theta, layer.alpha, 128)
     assert not lay["fast"]
+    check_linear(paro, x, layer, bias=b)
+
+
+@pytest.mark.parametrize("M,d,N", [(1, 4096, 4096), (16, 4096, 1024), (300, 4096, 512)])
+def test_linear_sparse_pairing(paro, M, d, N):
+    """A sparse pairing (10 % of the pairs rotate): compacted activation
+    schedule in the fused small-batch kernel and in the prefill path, weights
+    transformed with all K canonical stages."""
+    log(f"linear sparse pairing M={M} d={d} N={N}")
+    x, layer, b = synthetic.linear_case(seed=90 + M, M=M, d=d, N=N)
+    rng = np.random.default_rng(91 + M)
+    layer.theta[rng.random(layer.theta.shape) >= 0.1] = 0.0
+    _, lay = paro.paro_rotation_plan_host(layer.pairs, layer.theta, layer.alpha, 128)
+    assert lay["stages"] < 8 and lay["fast"]
+    check_quantize(paro, layer)
     check_linear(paro, x, layer, bias=b)
 
 

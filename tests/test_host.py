@@ -158,6 +158,10 @@ def field_major(img, lay, segs):
 
 
 def emulate_rotate(img, lay, x, K, d):
+    """Runs the plan image the way the activation kernel does: the kernel executes
+    lay["stages"] stages, at most the K stages of the layer."""
+    assert 0 <= lay["stages"] <= K
+    K = lay["stages"]
     nv = lay["seg_ch"] // 2
     W = lay["words"]
     C = 2 if lay["fast"] else 4
@@ -212,6 +216,8 @@ def check_slots_conflict_free(img, lay, K, d):
     """gfx950 16-byte LDS accesses: writes conflict-free when every 8 consecutive
     lanes hit slots distinct mod 8, reads when every 16 consecutive lanes hit
     slots distinct mod 16."""
+    assert 0 <= lay["stages"] <= K
+    K = lay["stages"]
     nv = lay["seg_ch"] // 2
     tab = field_major(img, lay, d // lay["seg_ch"])
     for s in range(tab.shape[0]):
@@ -239,17 +245,79 @@ def test_schedule_emulation_matches_oracle(paro, G, K, d, M):
     metrics.assert_rotated_close(emulate_rotate(img, lay, x, K, d), ref, G)
 
 
-def test_schedule_general_form_with_identity_pairs(paro):
-    """theta = 0 (exact identities) defeat the factored form; the general 2x2 form is used."""
+def test_schedule_general_form_with_near_identity_pairs(paro):
+    """Rotations with |sin theta| below the factored form's threshold (theta =
+    1e-7, not an exact identity) pin lane orientations that cannot all hold:
+    the general 2x2 form is used."""
     d, G, K, M = 256, 128, 6, 4
     x, layer = synthetic.rotation_case(seed=5, M=M, d=d, group=G, K=K)
     theta = layer.theta.copy()
-    theta[:, ::3] = 0.0
+    theta[:, ::3] = 1e-7
     img, lay = paro.paro_rotation_plan_host(layer.pairs, theta, layer.alpha, G)
-    assert not lay["fast"]
+    assert not lay["fast"] and lay["stages"] == K
     check_slots_conflict_free(img, lay, K, d)
     ref = oracle.rotate_activations(x, layer.pairs, theta, layer.alpha)
     metrics.assert_rotated_close(emulate_rotate(img, lay, x, K, d), ref, G)
+
+
+@pytest.mark.parametrize("keep,d,K,M", [(0.1, 4096, 8, 3), (0.1, 512, 8, 5), (0.2, 256, 8, 4),
+                                         (0.05, 1024, 16, 3), (0.1, 256, 4, 2)])
+def test_schedule_sparse_pairing_compacts_stages(paro, keep, d, K, M):
+    """Sparse pairings (most theta = 0): the activation schedule runs fewer
+    stages than K, with every rotation after the earlier ones on its channels,
+    and still equals the oracle's K-stage product."""
+    x, layer = synthetic.sparse_rotation_case(seed=int(keep * 100) + d + K, M=M, d=d, group=128,
+                                              K=K, keep=keep)
+    img, lay = paro.paro_rotation_plan_host(layer.pairs, layer.theta, layer.alpha, 128)
+    # the least number of stages that keeps the order on every channel: the
+    # longest chain of non-identity rotations linked by shared channels
+    depth = np.zeros(d, np.int64)
+    for t in range(K):
+        for p in range(d // 2):
+            if layer.theta[t, p] != 0.0:
+                i, j = layer.pairs[t, p]
+                depth[i] = depth[j] = max(depth[i], depth[j]) + 1
+    want = int(depth.max())
+    assert lay["stages"] == want < K
+    assert lay["fast"]
+    check_slots_conflict_free(img, lay, K, d)
+    ref = oracle.rotate_activations(x, layer.pairs, layer.theta, layer.alpha)
+    metrics.assert_rotated_close(emulate_rotate(img, lay, x, K, d), ref, 128)
+
+
+@pytest.mark.parametrize("angle,step,seed,fast", [(np.pi / 2, 16, 18, True), (np.pi / 2, 64, 17, True),
+                                                  (1e-13, 64, 17, True), (1e-13, 4, 17, False)])
+def test_schedule_sparse_pairing_with_pinned_rotations(paro, angle, step, seed, fast):
+    """Sparse pairings where some rotations are quarter turns (cos ~ 4e-8: the
+    factored form carries them with a large coefficient ratio) or nearly
+    identities (sin ~ 1e-13: their lanes must keep their registers, which ties
+    the identity pairs around them; many such ties can contradict each other,
+    and the plan then takes the general form)."""
+    d, K = 1024, 8
+    x, layer = synthetic.sparse_rotation_case(seed=seed, M=3, d=d, group=128, K=K, keep=0.1)
+    nz = np.argwhere(layer.theta != 0.0)
+    for t, p in nz[::step]:
+        layer.theta[t, p] = np.float32(angle)
+    img, lay = paro.paro_rotation_plan_host(layer.pairs, layer.theta, layer.alpha, 128)
+    assert lay["fast"] == fast and lay["stages"] < K
+    check_slots_conflict_free(img, lay, K, d)
+    ref = oracle.rotate_activations(x, layer.pairs, layer.theta, layer.alpha)
+    metrics.assert_rotated_close(emulate_rotate(img, lay, x, K, d), ref, 128)
+
+
+def test_schedule_dense_pairing_keeps_all_stages(paro):
+    """No identities, or identities that do not shorten the longest chain: K stages."""
+    x, layer = synthetic.rotation_case(seed=9, M=2, d=512, group=128, K=6)
+    _, lay = paro.paro_rotation_plan_host(layer.pairs, layer.theta, layer.alpha, 128)
+    assert lay["stages"] == 6
+    theta = layer.theta.copy()
+    theta[:, ::3] = 0.0
+    img, lay = paro.paro_rotation_plan_host(layer.pairs, theta, layer.alpha, 128)
+    # exact identities become identity pairs that the factored form can carry
+    assert lay["stages"] == 6 and lay["fast"]
+    check_slots_conflict_free(img, lay, 6, 512)
+    ref = oracle.rotate_activations(x, layer.pairs, theta, layer.alpha)
+    metrics.assert_rotated_close(emulate_rotate(img, lay, x, 6, 512), ref, 128)
 
 
 def test_schedule_full_decode_layer(paro):
