@@ -165,18 +165,21 @@ int paro_quantize_weights(const paro_rotation* r, const uint16_t* w, int64_t N, 
 size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t N, int64_t d);
 
 /*
- * The W4G128 linear layer on rotated activations:
- *   Y[m][n] = sum_k X'[m][k] * (q[n][k] - z[n][k/128]) * s[n][k/128] + bias[n]
+ * The W4 linear layer on rotated activations (W4G128 in the paper notes'
+ * main experiments; groups of 64 and 256 as well, the sizes the CSDN
+ * article's section 5.2 compares):
+ *   Y[m][n] = sum_k X'[m][k] * (q[n][k] - z[n][k/G]) * s[n][k/G] + bias[n]
  * with X' = X T^-1 when r != NULL (rotated inside the call) and X' = X when
  * r == NULL (plain W4, or activations the caller rotated already).
  *
  *   x        device fp16 [M][d]; qweight/scales/zeros as produced by
- *            paro_quantize_weights with group 128; bias device fp16 [N] or NULL;
+ *            paro_quantize_weights with the same group; bias device fp16 [N]
+ *            or NULL;
  *   y        device fp16 [M][N] (must not overlap x).
- *   group    must be 128 (W4G128); other values return PARO_ERR_UNSUPPORTED.
+ *   group    G = 64, 128 or 256; other values return PARO_ERR_UNSUPPORTED.
  *            A plan r must have the same d and group (the pairs stay inside
  *            quantization groups), else PARO_ERR_SHAPE.
- *   N % 16 == 0, d % 128 == 0, M >= 0 (M == 0 is a no-op); N <= 2^30,
+ *   N % 16 == 0, d % 128 == 0, d % G == 0, M >= 0 (M == 0 is a no-op); N <= 2^30,
  *   d <= 2^22, M < 2^30, else PARO_ERR_UNSUPPORTED.
  *   workspace, workspace_bytes: device memory of at least
  *            paro_w4_linear_workspace_size(r, M, N, d) bytes, 256-byte
@@ -188,8 +191,9 @@ size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t 
  *            workspaces.
  *
  * Execution: M <= 16 runs one kernel that streams the packed weights and, for
- * plans with K <= 8, applies the transform to the activations inside the same
- * kernel; plans with more stages rotate into the workspace first. M > 16 rotates into the workspace and then runs
+ * plans of group 64 or 128 that execute at most 8 stages, applies the
+ * transform to the activations inside the same kernel; other plans rotate
+ * into the workspace first. M > 16 rotates into the workspace and then runs
  * the matrix-core kernel.
  *
  * Arithmetic: X' exactly as paro_rotate computes it (fp16); fp32 accumulation

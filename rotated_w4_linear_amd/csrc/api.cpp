@@ -230,12 +230,12 @@ int paro_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qwe
     set_error("paro_w4_linear: bad sizes");
     return PARO_ERR_SHAPE;
   }
-  if (group != 128) {
-    set_error("paro_w4_linear: only group 128 (W4G128) is implemented");
+  if (group != 64 && group != 128 && group != 256) {
+    set_error("paro_w4_linear: group must be 64, 128 or 256");
     return PARO_ERR_UNSUPPORTED;
   }
-  if (N % 16 || d % 128) {
-    set_error("paro_w4_linear: N must be a multiple of 16 and d of 128");
+  if (N % 16 || d % 128 || d % group) {
+    set_error("paro_w4_linear: N must be a multiple of 16, d of 128 and of group");
     return PARO_ERR_SHAPE;
   }
   // (the kernels address one tile of rows with 32-bit byte offsets)
@@ -284,7 +284,7 @@ int paro_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qwe
       xin = xr;
       fused = nullptr;
     }
-    e = launch_w4_decode(xin, qweight, scales, zeros, bias, y, M, N, d, fused, ws, stream);
+    e = launch_w4_decode(xin, qweight, scales, zeros, bias, y, M, N, d, group, fused, ws, stream);
   } else {
     const uint16_t* xin = x;
     if (r) {
@@ -293,7 +293,7 @@ int paro_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qwe
       if (e != hipSuccess) return hip_fail(e, "paro_w4_linear rotate launch");
       xin = xr;
     }
-    e = launch_w4_gemm(xin, qweight, scales, zeros, bias, y, M, N, d, stream);
+    e = launch_w4_gemm(xin, qweight, scales, zeros, bias, y, M, N, d, group, stream);
   }
   if (e != hipSuccess) return hip_fail(e, "paro_w4_linear launch");
   return PARO_OK;

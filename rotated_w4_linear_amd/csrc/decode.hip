@@ -1,7 +1,9 @@
 // gfx950 kernel for the W4G128 linear layer with few tokens (decode, M <= 16),
 // with the online activation transform fused in:
-//   Y[m][n] = sum_k X'[m][k] (q[n][k] - z[n][k/128]) s[n][k/128] + b[n],
+//   Y[m][n] = sum_k X'[m][k] (q[n][k] - z[n][k/G]) s[n][k/G] + b[n],
 //   X' = X T^-1
+// (G = 128; 64 and 256 as well: each lane's 32 codes of a segment lie in one
+// group)
 // (CSDN article section 2.1: Y = (X T^-1)(T W) + b; paper notes "关键设计"
 // for the rotation and "主实验" for the 4-bit, group-128 weights).
 //
@@ -95,7 +97,7 @@ __global__ __launch_bounds__(256) void w4_decode_kernel(
     const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zr,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N, int d,
     const uint32_t* __restrict__ tab, int K, float* part, uint32_t* cnt, int ksl, int nbl,
-    int nb_base, int sys) {
+    int nb_base, int sys, int gsh) {
   // X' tile: [16 tokens][64 chunks of 16 bytes]; chunk c of token m is stored
   // at position c ^ m, so the 16 tokens of one MFMA operand read land on 16
   // distinct 16-byte positions.
@@ -111,7 +113,8 @@ __global__ __launch_bounds__(256) void w4_decode_kernel(
   const int ks = j8 % ksl;              // k-slice
   if (nb >= nbl) return;
   const int nbg = nb_base + nb;
-  const int groups = d >> 7;
+  const int groups = d >> 7;            // 128-channel segments
+  const int sgr = d >> (6 + gsh);       // quantization groups (64 << gsh channels) per row
   const int g0 = ks * DK_SEGS;
   const int nq = min(DK_SEGS, groups - g0);
   const int r = lane & 15, kq = lane >> 4;
@@ -151,9 +154,9 @@ __global__ __launch_bounds__(256) void w4_decode_kernel(
   for (int j = 0; j < TJ; ++j) {
     const int nc = min(rb + 16 * j + r, N - 1);  // rows past N are never stored
     wrow[j] = qw + (size_t)nc * (size_t)(d >> 1) + 16 * kq;
-    grow[j] = (size_t)nc * groups;
+    grow[j] = (size_t)nc * sgr;
   }
-  if constexpr (SZV) {
+  if constexpr (SZV) {  // (group 128: sgr == groups)
     uint2 s4[TJ];
     uint32_t z4[TJ];
 #pragma unroll
@@ -176,11 +179,12 @@ __global__ __launch_bounds__(256) void w4_decode_kernel(
 #pragma unroll
     for (int q = 0; q < DK_SEGS; ++q) {
       const int g = min(g0 + q, groups - 1);
+      const int gq = ((g << 7) + 32 * kq) >> (6 + gsh);  // this lane's 32 codes share one group
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         wv[j][q] = *(const u4*)(wrow[j] + 64 * g);
-        sraw[j][q] = sc[grow[j] + g];
-        zraw[j][q] = zr[grow[j] + g];
+        sraw[j][q] = sc[grow[j] + gq];
+        zraw[j][q] = zr[grow[j] + gq];
       }
     }
   }
@@ -389,7 +393,7 @@ bool xcd_dispatch_is_round_robin() {
 
 template <bool ROT, int KMAX, bool KEXACT, bool FAST, int T, int TJ, bool SZV>
 hipError_t launch_t(const uint16_t* x, const uint8_t* qw, const uint16_t* sc, const uint8_t* zr,
-                    const uint16_t* bias, uint16_t* y, int M, int N, int d,
+                    const uint16_t* bias, uint16_t* y, int M, int N, int d, int gsh,
                     const paro_rotation* r, void* ws, hipStream_t stream) {
   const int ksl = (d / 128 + DK_SEGS - 1) / DK_SEGS;
   const int nbl_all = (N + 64 * TJ - 1) / (64 * TJ);
@@ -404,7 +408,7 @@ hipError_t launch_t(const uint16_t* x, const uint8_t* qw, const uint16_t* sc, co
     const unsigned blocks = 8u * (unsigned)ksl * (unsigned)((nbl + 7) / 8);
     hipLaunchKernelGGL((w4_decode_kernel<ROT, KMAX, KEXACT, FAST, T, TJ, SZV>), dim3(blocks), dim3(256), 0,
                        stream, x, qw, sc, zr, bias, y, M, N, d, tab, K, part, cnt, ksl, nbl, nb0,
-                       sys);
+                       sys, gsh);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -413,15 +417,15 @@ hipError_t launch_t(const uint16_t* x, const uint8_t* qw, const uint16_t* sc, co
 
 template <int T, int TJ, bool SZV>
 hipError_t launch_plan(const uint16_t* x, const uint8_t* qw, const uint16_t* sc, const uint8_t* zr,
-                       const uint16_t* bias, uint16_t* y, int m, int n, int k,
+                       const uint16_t* bias, uint16_t* y, int m, int n, int k, int gsh,
                        const paro_rotation* r, void* ws, hipStream_t stream) {
-  if (!r) return launch_t<false, 0, true, true, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
-  if (r->lay.stages == 0) return launch_t<true, 0, true, true, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
+  if (!r) return launch_t<false, 0, true, true, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, gsh, r, ws, stream);
+  if (r->lay.stages == 0) return launch_t<true, 0, true, true, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, gsh, r, ws, stream);
   if (r->lay.fast) {
-    if (r->lay.stages == 8) return launch_t<true, 8, true, true, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
-    return launch_t<true, 8, false, true, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
+    if (r->lay.stages == 8) return launch_t<true, 8, true, true, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, gsh, r, ws, stream);
+    return launch_t<true, 8, false, true, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, gsh, r, ws, stream);
   }
-  return launch_t<true, 8, false, false, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, r, ws, stream);
+  return launch_t<true, 8, false, false, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, gsh, r, ws, stream);
 }
 
 }  // namespace
@@ -432,24 +436,26 @@ bool decode_fuses_rotation(const paro_rotation* r) {
 
 hipError_t launch_w4_decode(const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
                             const uint8_t* zeros, const uint16_t* bias, uint16_t* y, int64_t M,
-                            int64_t N, int64_t d, const paro_rotation* r, void* ws,
+                            int64_t N, int64_t d, int group, const paro_rotation* r, void* ws,
                             hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const int m = (int)M, n = (int)N, k = (int)d;
+  const int gsh = group == 64 ? 0 : group == 128 ? 1 : 2;
   // 64-channel workgroups when 128-channel ones would not give two per CU
   const int64_t wg128 = ((N + 127) / 128) * ((d / 128 + DK_SEGS - 1) / DK_SEGS);
   const bool tj1 = wg128 < 384, small = M <= 4;
   // full slices and aligned bases: vector scale / zero loads
-  if ((d / 128) % DK_SEGS == 0 && ((uintptr_t)scales & 7) == 0 && ((uintptr_t)zeros & 3) == 0) {
-    if (tj1) return small ? launch_plan<4, 1, true>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream)
-                          : launch_plan<16, 1, true>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream);
-    return small ? launch_plan<4, 2, true>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream)
-                 : launch_plan<16, 2, true>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream);
+  if (group == 128 && (d / 128) % DK_SEGS == 0 && ((uintptr_t)scales & 7) == 0 &&
+      ((uintptr_t)zeros & 3) == 0) {
+    if (tj1) return small ? launch_plan<4, 1, true>(x, qweight, scales, zeros, bias, y, m, n, k, gsh, r, ws, stream)
+                          : launch_plan<16, 1, true>(x, qweight, scales, zeros, bias, y, m, n, k, gsh, r, ws, stream);
+    return small ? launch_plan<4, 2, true>(x, qweight, scales, zeros, bias, y, m, n, k, gsh, r, ws, stream)
+                 : launch_plan<16, 2, true>(x, qweight, scales, zeros, bias, y, m, n, k, gsh, r, ws, stream);
   }
-  if (tj1) return small ? launch_plan<4, 1, false>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream)
-                        : launch_plan<16, 1, false>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream);
-  return small ? launch_plan<4, 2, false>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream)
-               : launch_plan<16, 2, false>(x, qweight, scales, zeros, bias, y, m, n, k, r, ws, stream);
+  if (tj1) return small ? launch_plan<4, 1, false>(x, qweight, scales, zeros, bias, y, m, n, k, gsh, r, ws, stream)
+                        : launch_plan<16, 1, false>(x, qweight, scales, zeros, bias, y, m, n, k, gsh, r, ws, stream);
+  return small ? launch_plan<4, 2, false>(x, qweight, scales, zeros, bias, y, m, n, k, gsh, r, ws, stream)
+               : launch_plan<16, 2, false>(x, qweight, scales, zeros, bias, y, m, n, k, gsh, r, ws, stream);
 }
 
 }  // namespace paro

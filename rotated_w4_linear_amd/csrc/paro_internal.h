@@ -97,7 +97,7 @@ hipError_t launch_quantize(const paro_rotation* r, const uint16_t* w, int64_t N,
 // Large-batch linear (M > 16) on already transformed activations.
 hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
                           const uint8_t* zeros, const uint16_t* bias, uint16_t* y, int64_t M,
-                          int64_t N, int64_t d, hipStream_t stream);
+                          int64_t N, int64_t d, int group, hipStream_t stream);
 
 // Small-batch linear (M <= 16). With r != NULL the activation transform runs
 // inside the kernel (requires decode_fuses_rotation(r)); ws is the workspace:
@@ -108,6 +108,6 @@ constexpr int64_t kDecodeMaxM = 16;
 bool decode_fuses_rotation(const paro_rotation* r);
 hipError_t launch_w4_decode(const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
                             const uint8_t* zeros, const uint16_t* bias, uint16_t* y, int64_t M,
-                            int64_t N, int64_t d, const paro_rotation* r, void* ws,
+                            int64_t N, int64_t d, int group, const paro_rotation* r, void* ws,
                             hipStream_t stream);
 }  // namespace paro

@@ -1,8 +1,9 @@
 // gfx950 kernel for the W4G128 linear layer on rotated activations with
 // many tokens (prefill, M > 16):
-//   Y[m][n] = sum_k X'[m][k] (q[n][k] - z[n][k/128]) s[n][k/128] + b[n]
+//   Y[m][n] = sum_k X'[m][k] (q[n][k] - z[n][k/G]) s[n][k/G] + b[n]
 // (CSDN article section 2.1: Y = (X T^-1)(T W) + b; paper notes "主实验":
-// 4-bit weights, group 128). Here the layer is a dense contraction and runs
+// 4-bit weights, group G = 128; 64 and 256 are taken as well, each 64-channel
+// k-tile reading the one group it lies in). Here the layer is a dense contraction and runs
 // on the matrix cores. Dequantization: two nibbles are spread into the
 // mantissas of two fp16 1024.0 values with v_perm, (1024 + q) - (1024 + z) =
 // q - z is exact in packed fp16, and one packed multiply by the fp16 scale
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(2)))
 void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ qw,
                     const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zr,
                     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N,
-                    int d, int mblk, int nblk) {
+                    int d, int gsh, int mblk, int nblk) {
   constexpr int GB_M = 32 * MT;           // tokens per workgroup tile
   constexpr int GB_XSTAGE = GB_M * GB_K;  // halfs per X' stage (16 KB at MT = 4)
   __shared__ __attribute__((aligned(1024))) _Float16 X0[KS][GB_XSTAGE], X1[KS][GB_XSTAGE];
@@ -97,7 +98,7 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
   const int m0 = mb * GB_M;
   const int nw0 = nb * GB_N;       // workgroup's first output channel
   const int n0 = nw0 + 64 * w;     // this wavefront's first output channel
-  const int groups = d >> 7;
+  const int groups = d >> (6 + gsh);  // quantization groups of 64 << gsh channels per row
   const int KT = (d / GB_K) / KS;  // k-tiles per group of wavefronts
   const int kt0 = kg * KT;
   const int l32 = lane & 31, g = lane >> 5;
@@ -138,7 +139,7 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
   // the DMA of one k-tile: ten load-to-LDS instructions per lane
   auto dma = [&](int kt, _Float16* xs, u4* ws, uint32_t* ss_l, uint32_t* zs_l) {
     const int kglob = kt0 + kt;
-    const uint32_t gi = (uint32_t)(kglob >> 1);
+    const uint32_t gi = (uint32_t)(kglob >> gsh);  // the k-tile's group (64-channel k-tiles)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)&ss_l[64 * w], 2, (szrow + gi) * 2u, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_void*)&zs_l[64 * w], 1, szrow + gi, 0, 0, 0);
 #pragma unroll
@@ -265,17 +266,18 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
 template <int KS, int MT>
 void launch_gemm(unsigned blocks, hipStream_t stream, const uint16_t* x, const uint8_t* qweight,
                  const uint16_t* scales, const uint8_t* zeros, const uint16_t* bias, uint16_t* y,
-                 int64_t M, int64_t N, int64_t d, int mblk, int nblk) {
+                 int64_t M, int64_t N, int64_t d, int gsh, int mblk, int nblk) {
   hipLaunchKernelGGL((w4_gemm_kernel<KS, MT>), dim3(blocks), dim3(256 * KS), 0, stream, x, qweight,
-                     scales, zeros, bias, y, (int)M, (int)N, (int)d, mblk, nblk);
+                     scales, zeros, bias, y, (int)M, (int)N, (int)d, gsh, mblk, nblk);
 }
 
 }  // namespace
 
 hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
                           const uint8_t* zeros, const uint16_t* bias, uint16_t* y, int64_t M,
-                          int64_t N, int64_t d, hipStream_t stream) {
+                          int64_t N, int64_t d, int group, hipStream_t stream) {
   if (M == 0) return hipSuccess;
+  const int gsh = group == 64 ? 0 : group == 128 ? 1 : 2;
   const int nblk = (int)((N + GB_N - 1) / GB_N);
   // 64-token tiles when 128-token ones would leave most SIMDs without work
   const bool half = (int64_t)nblk * ((M + 127) / 128) < kHalfTileBelow;
@@ -288,10 +290,10 @@ hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint1
   // too few tiles to give every SIMD two wavefronts: split k inside the workgroup
   const bool ks2 = tiles < 512 && (d / GB_K) % 2 == 0 && d / GB_K >= 4;
   const unsigned g = (unsigned)blocks;
-  if (half && ks2) launch_gemm<2, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, mblk, nblk);
-  else if (half) launch_gemm<1, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, mblk, nblk);
-  else if (ks2) launch_gemm<2, 4>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, mblk, nblk);
-  else launch_gemm<1, 4>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, mblk, nblk);
+  if (half && ks2) launch_gemm<2, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
+  else if (half) launch_gemm<1, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
+  else if (ks2) launch_gemm<2, 4>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
+  else launch_gemm<1, 4>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
   return hipGetLastError();
 }
 

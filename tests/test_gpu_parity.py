@@ -253,15 +253,16 @@ def test_quantize_nonfinite_weight_is_an_error(paro):
 # ----------------------------------------------------------------------------
 
 def check_linear(paro, x, layer, bias=None, rotated=True, rows=None):
-    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, layer.group) if rotated else None
-    qw, s, z = paro.paro_quantize_weights(r, dev(layer.w), 128)
-    y = host(paro.paro_w4_linear(r, dev(x), qw, s, z, dev(bias) if bias is not None else None))
+    G = layer.group
+    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, G) if rotated else None
+    qw, s, z = paro.paro_quantize_weights(r, dev(layer.w), G)
+    y = host(paro.paro_w4_linear(r, dev(x), qw, s, z, dev(bias) if bias is not None else None, group=G))
     qw, s, z = host(qw), host(s), host(z)
     idx = np.arange(x.shape[0]) if rows is None else rows
     if rotated:
-        ref = oracle.rotated_w4_linear(x[idx], qw, s, z, 128, layer.pairs, layer.theta, layer.alpha, bias)
+        ref = oracle.rotated_w4_linear(x[idx], qw, s, z, G, layer.pairs, layer.theta, layer.alpha, bias)
     else:
-        ref = oracle.rotated_w4_linear(x[idx], qw, s, z, 128, bias=bias)
+        ref = oracle.rotated_w4_linear(x[idx], qw, s, z, G, bias=bias)
     assert np.all(np.isfinite(y[idx].astype(np.float32)))
     return metrics.assert_linear_close(y[idx], ref)
 
@@ -394,6 +395,22 @@ def test_linear_rejects_other_rotation_groups(paro, group):
     with pytest.raises(paro.ParoError) as e:
         paro.paro_w4_linear(r, dev(x), qw, s, z)
     assert e.value.status == -2
+
+
+@pytest.mark.parametrize("G", [64, 256])
+@pytest.mark.parametrize("M,d,N", [(1, 1024, 256), (5, 768, 144), (16, 2048, 128), (130, 1024, 272),
+                                   (300, 512, 128), (1, 4096, 1024)])
+def test_linear_other_groups(paro, G, M, d, N):
+    """W4G64 and W4G256: rotation and quantization groups of 64 or 256 channels
+    (the small-batch kernel fuses the transform for G = 64; G = 256 rotates
+    into the workspace first)."""
+    if d % G:
+        pytest.skip("d is not a multiple of the group")
+    log(f"linear group {G} M={M} d={d} N={N}")
+    x, layer, b = synthetic.linear_case(seed=300 + G + M, M=M, d=d, N=N, group=G)
+    check_quantize(paro, layer, group=G)
+    check_linear(paro, x, layer, bias=b)
+    check_linear(paro, x, layer, rotated=False)
 
 
 def test_decode_general_form(paro):

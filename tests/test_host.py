@@ -101,9 +101,12 @@ def test_hot_calls_validate_before_any_launch(paro):
     bad = ctypes.c_void_p(16 * 1024 + 2)
     # null handle
     assert lib.paro_rotate(None, dummy, dummy, 4, None) == -1
-    # w4_linear: group other than 128 is unsupported; N % 16, d % 128 are shape errors
+    # w4_linear: groups other than 64, 128, 256 are unsupported; N % 16, d % 128,
+    # d % group are shape errors
     args = [None, dummy, dummy, dummy, dummy, None, dummy]
-    assert lib.paro_w4_linear(*args, 4, 64, 256, 64, None, 0, None) == -6
+    assert lib.paro_w4_linear(*args, 4, 64, 256, 32, None, 0, None) == -6
+    assert lib.paro_w4_linear(*args, 4, 64, 256, 512, None, 0, None) == -6
+    assert lib.paro_w4_linear(*args, 4, 64, 384, 256, None, 0, None) == -2
     assert lib.paro_w4_linear(*args, 4, 60, 256, 128, None, 0, None) == -2
     assert lib.paro_w4_linear(*args, 4, 64, 200, 128, None, 0, None) == -2
     assert lib.paro_w4_linear(*args, -1, 64, 256, 128, None, 0, None) == -2
