@@ -46,7 +46,8 @@ notes of the repository):
     canonical fp32 weight transform; plain fp64 cos/sin for the fp64 parts.
 
 Precision:
-  * ``rotate_activations``, ``transform_weights_f64``, ``linear``: fp64.
+  * ``rotate_activations``, ``transform_weights_f64``, ``linear``,
+    ``rotation_backward``: fp64.
   * ``transform_weights_f32`` and ``quantize_groups``: the canonical fp32
     order of operations (every product and sum rounded to fp32 on its own,
     no fused multiply-add), because the int4 codes must be reproduced bit for
@@ -61,7 +62,7 @@ __all__ = [
     "check_rotation_params", "cos_sin_f32", "rotate_activations",
     "transform_weights_f32", "transform_weights_f64", "quantize_groups",
     "pack_codes", "unpack_codes", "dequantize", "quantize_weights", "linear",
-    "rotated_w4_linear", "QuantizeError",
+    "rotated_w4_linear", "rotation_backward", "QuantizeError",
 ]
 
 
@@ -143,6 +144,70 @@ def rotate_activations(x, pairs, theta, alpha):
     v = np.asarray(x).astype(np.float64) / np.asarray(alpha, dtype=np.float32).astype(np.float64)
     t64 = np.asarray(theta, dtype=np.float32).astype(np.float64)
     return _apply_stages(v, np.asarray(pairs), np.cos(t64), np.sin(t64))
+
+
+# ----------------------------------------------------------------------------
+# Gradients of the transform (transform learning)
+# ----------------------------------------------------------------------------
+
+def rotation_backward(x, g, pairs, theta, alpha, side="activation"):
+    """Gradients of the transform with respect to its input, angles and scales (fp64).
+
+    [Notes] "损失函数 / 训练策略": the angles and channel scales are learned by
+    minimising the layer-wise output loss, which needs these gradients.
+
+    The transform of one row r (a token of X, or a row of W in the [N][d]
+    layout): v_0 = r / alpha (side "activation", X' = X T^-1) or r * alpha
+    (side "weight", T W), then each stage t in order applies the pair update
+    (v_i, v_j) <- (c v_i - s v_j, s v_i + c v_j). Given g = dL/d(output) for
+    every row ([M][d]), returns, by the chain rule:
+      dr      [M][d]    g walked back through every stage's transpose
+                        (g_i, g_j) <- (c g_i + s g_j, -s g_i + c g_j), then
+                        through the scaling (/ alpha or * alpha);
+      dtheta  [K][d/2]  summed over rows: g'_j v'_i - g'_i v'_j, with v' the
+                        stage's outputs and g' their gradient, because
+                        d v'_i / d theta = -v'_j and d v'_j / d theta = v'_i;
+      dalpha  [d]       summed over rows: g_0 * d v_0 / d alpha, which is
+                        -v_0 / alpha for activations and r for weights.
+    The forward values of every stage are kept (fp64), then the stages are
+    walked back in reverse order.
+    """
+    if side not in ("activation", "weight"):
+        raise ValueError("side is 'activation' or 'weight'")
+    r = np.asarray(x).astype(np.float64)
+    gy = np.asarray(g).astype(np.float64)
+    a = np.asarray(alpha, dtype=np.float32).astype(np.float64)
+    t64 = np.asarray(theta, dtype=np.float32).astype(np.float64)
+    c, s = np.cos(t64), np.sin(t64)
+    pairs = np.asarray(pairs)
+    K = pairs.shape[0]
+    d = a.shape[0]
+    v0 = r / a if side == "activation" else r * a
+    outs = []
+    v = v0
+    for t in range(K):
+        i, j = pairs[t, :, 0], pairs[t, :, 1]
+        vi, vj = v[..., i], v[..., j]
+        v = v.copy()
+        v[..., i] = c[t] * vi - s[t] * vj
+        v[..., j] = s[t] * vi + c[t] * vj
+        outs.append(v)
+    gc = gy.copy()
+    dtheta = np.zeros((K, d // 2))
+    for t in reversed(range(K)):
+        i, j = pairs[t, :, 0], pairs[t, :, 1]
+        gi, gj = gc[..., i], gc[..., j]
+        dtheta[t] = (gj * outs[t][..., i] - gi * outs[t][..., j]).reshape(-1, d // 2).sum(axis=0)
+        gc = gc.copy()
+        gc[..., i] = c[t] * gi + s[t] * gj
+        gc[..., j] = -s[t] * gi + c[t] * gj
+    if side == "activation":
+        dr = gc / a
+        dalpha = -(gc * v0 / a).reshape(-1, d).sum(axis=0)
+    else:
+        dr = gc * a
+        dalpha = (gc * r).reshape(-1, d).sum(axis=0)
+    return dr, dtheta, dalpha
 
 
 # ----------------------------------------------------------------------------

@@ -386,3 +386,122 @@ def test_metrics_floor():
     got = ref + np.array([[1e-4, 1e-6, 0, 0]])
     fl, raw, n = metrics.rotated_error(got, ref, 4)
     assert raw > 1 and fl < 2e-3
+
+
+# ----------------------------------------------------------------------------
+# B1-B4: gradients of the transform (transform learning)
+# ----------------------------------------------------------------------------
+
+def grid_params(seed, d, G, K):
+    """Rotation parameters on coarse binary grids (theta = k / 64, alpha =
+    1 + m / 64), so that theta +- 2^-9 and alpha +- 2^-9 stay exact in fp32,
+    where the forward transforms round the parameters."""
+    rng = synthetic.rng_for(98, seed)
+    pairs = synthetic.draw_pairs(rng, d, G, K)
+    theta = (rng.integers(-200, 201, size=(K, d // 2)) / 64.0).astype(np.float32)
+    alpha = (1.0 + rng.integers(-16, 33, size=d) / 64.0).astype(np.float32)
+    return pairs, theta, alpha
+
+
+def forward(side, x, pairs, theta, alpha):
+    if side == "activation":
+        return oracle.rotate_activations(x, pairs, theta, alpha)
+    return oracle.transform_weights_f64(x, pairs, theta, alpha)
+
+
+def richardson(f, h):
+    """Central difference extrapolated from steps h and h/2 (error O(h^4))."""
+    d1 = (f(h) - f(-h)) / (2 * h)
+    d2 = (f(h / 2) - f(-h / 2)) / h
+    return (4 * d2 - d1) / 3
+
+
+@pytest.mark.parametrize("side", ["activation", "weight"])
+def test_b1_gradients_match_finite_differences(side):
+    """d theta and d alpha against finite differences of the forward transform
+    (the scalar loss L = sum g * F), d input against the dense-matrix closed form
+    (X' = X T^-1 gives dX = g T^-T; rows of T W give dW = g T)."""
+    d, G, K, M = 16, 8, 3, 3
+    pairs, theta, alpha = grid_params(1 if side == "activation" else 2, d, G, K)
+    rng = synthetic.rng_for(97, 0)
+    x = synthetic.draw_x(rng, M, d, 1, 5.0)
+    g = rng.standard_normal((M, d))
+    dr, dth, dal = oracle.rotation_backward(x, g, pairs, theta, alpha, side)
+
+    def loss(th, al):
+        return float(np.sum(g * forward(side, x, pairs, th, al)))
+
+    h = 2.0 ** -8
+    for t in range(K):
+        for p in range(d // 2):
+            def f(e, t=t, p=p):
+                th = theta.copy()
+                th[t, p] = np.float32(theta[t, p] + e)
+                assert th[t, p] == theta[t, p] + e
+                return loss(th, alpha)
+            assert abs(richardson(f, h) - dth[t, p]) <= 1e-9 * (1 + abs(dth[t, p]))
+    for k in range(d):
+        def f(e, k=k):
+            al = alpha.copy()
+            al[k] = np.float32(alpha[k] + e)
+            assert al[k] == alpha[k] + e
+            return loss(theta, al)
+        assert abs(richardson(f, h) - dal[k]) <= 1e-9 * (1 + abs(dal[k]))
+    T = dense_T(pairs, theta, alpha)
+    want = g @ np.linalg.inv(T).T if side == "activation" else g @ T
+    assert np.allclose(dr, want, rtol=1e-12, atol=1e-12)
+
+
+def test_b2_k0_is_the_scaling_gradient():
+    """K = 0: dX = g / alpha and d alpha = -sum g x / alpha^2 for activations;
+    dW = g alpha and d alpha = sum g w for weights."""
+    rng = synthetic.rng_for(97, 1)
+    d, M = 64, 4
+    x = synthetic.draw_x(rng, M, d, 1, 5.0)
+    g = rng.standard_normal((M, d))
+    alpha = synthetic.draw_alpha(rng, d)
+    pairs = np.zeros((0, d // 2, 2), np.int32)
+    theta = np.zeros((0, d // 2), np.float32)
+    a = alpha.astype(np.float64)
+    xf = x.astype(np.float64)
+    dr, dth, dal = oracle.rotation_backward(x, g, pairs, theta, alpha, "activation")
+    assert dth.shape == (0, d // 2)
+    assert np.allclose(dr, g / a, rtol=1e-15)
+    assert np.allclose(dal, -(g * xf).sum(0) / a ** 2, rtol=1e-12)
+    dr, _, dal = oracle.rotation_backward(x, g, pairs, theta, alpha, "weight")
+    assert np.allclose(dr, g * a, rtol=1e-15)
+    assert np.allclose(dal, (g * xf).sum(0), rtol=1e-12)
+
+
+def test_b3_single_pair_closed_form():
+    """One pair, one stage, alpha = 1: out = (c x1 - s x2, s x1 + c x2), so
+    dL/dtheta = g1 (-s x1 - c x2) + g2 (c x1 - s x2) and dx = R^T g."""
+    x = np.array([[0.75, -1.5]], np.float16)
+    g = np.array([[0.3, -2.0]])
+    th = np.float32(0.625)
+    c, s = np.cos(np.float64(th)), np.sin(np.float64(th))
+    pairs = np.array([[[0, 1]]], np.int32)
+    dr, dth, dal = oracle.rotation_backward(x, g, pairs, np.array([[th]]), np.ones(2, np.float32))
+    x1, x2 = 0.75, -1.5
+    assert np.isclose(dth[0, 0], 0.3 * (-s * x1 - c * x2) + (-2.0) * (c * x1 - s * x2), rtol=1e-14)
+    assert np.allclose(dr[0], [c * 0.3 + s * -2.0, -s * 0.3 + c * -2.0], rtol=1e-14)
+    # d alpha at alpha = 1: -g_0 * x with g_0 = R^T g
+    assert np.allclose(dal, -dr[0] * np.array([x1, x2]), rtol=1e-14)
+
+
+def test_b4_weight_side_is_activation_side_with_inverse_scales():
+    """r * alpha = r / (1 / alpha): with power-of-two scales (exact inverses),
+    the weight side's dW and d theta equal the activation side's at 1 / alpha,
+    and d alpha follows the chain rule d/d alpha = -(1 / alpha^2) d/d(1 / alpha)."""
+    rng = synthetic.rng_for(97, 2)
+    d, G, K, M = 128, 64, 4, 3
+    w = synthetic.draw_w(rng, M, d, 0.5)
+    g = rng.standard_normal((M, d))
+    pairs, theta, _ = synthetic.draw_rotation(rng, d, G, K)
+    alpha = (2.0 ** rng.integers(-2, 3, size=d)).astype(np.float32)
+    inv = (1.0 / alpha).astype(np.float32)
+    dw, dth_w, dal_w = oracle.rotation_backward(w, g, pairs, theta, alpha, "weight")
+    dx, dth_a, dal_a = oracle.rotation_backward(w, g, pairs, theta, inv, "activation")
+    assert np.allclose(dw, dx, rtol=1e-13, atol=1e-13)
+    assert np.allclose(dth_w, dth_a, rtol=1e-12, atol=1e-12)
+    assert np.allclose(dal_w, -dal_a / alpha.astype(np.float64) ** 2, rtol=1e-12, atol=1e-12)
