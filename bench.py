@@ -21,7 +21,8 @@ alternating blocks.
 Other workloads (``--workload``): prefill_down (2048 x 14336 -> 4096),
 decode (M = 1, 4, 16 tokens, 4096 -> 4096; weight streaming), sweep (the 27
 rotation-only points, 8192 x d), sparse (the transform with sparse pairings, in
-which only a fraction of the pairs rotate), chain (the seven linears of a Llama-3-8B
+which only a fraction of the pairs rotate), backward (the gradients of the
+transform with respect to its input, angles and scales), chain (the seven linears of a Llama-3-8B
 decoder layer as rotated W4, plain W4 and dense fp16 chains), copy (a plain
 device copy, for calibrating HBM byte counters).
 
@@ -526,6 +527,80 @@ def bench_sparse(args, paro, torch):
     }
 
 
+def bench_backward(args, paro, torch):
+    """Gradients of the transform (paro_rotation_backward) at the prefill shape,
+    8192 x 4096, K = 8: activation side and weight side with the input
+    gradient, and the activation side with angle and scale gradients only."""
+    import synthetic
+    T = Timer(torch)
+    M, d, K = 8192, 4096, 8
+    ring = args.ring or 4
+    x, layer = synthetic.rotation_case(seed=11, M=M, d=d, group=128, K=K)
+    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, 128)
+    g = synthetic.rng_for(4100, 11).standard_normal((M, d)).astype(np.float32)
+    xs = [torch.from_numpy(x).cuda()] + [None] * (ring - 1)
+    gs = [torch.from_numpy(g).cuda()] + [None] * (ring - 1)
+    for k in range(1, ring):
+        xs[k] = xs[0].clone()
+        gs[k] = gs[0].clone()
+    gx = torch.empty((M, d), dtype=torch.float32, device="cuda")
+    dth = torch.empty((K, d // 2), dtype=torch.float32, device="cuda")
+    dal = torch.empty((d,), dtype=torch.float32, device="cuda")
+    need = paro.paro_rotation_backward_workspace_size(r, M)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    lib = paro.load_library()
+    import ctypes
+
+    def call(i, side, with_gx):
+        k = i % ring
+        st = lib.paro_rotation_backward(
+            r.handle, paro.SIDES[side], ctypes.c_void_p(xs[k].data_ptr()),
+            ctypes.c_void_p(gs[k].data_ptr()), ctypes.c_void_p(gx.data_ptr()) if with_gx else None,
+            ctypes.c_void_p(dth.data_ptr()), ctypes.c_void_p(dal.data_ptr()), M,
+            ctypes.c_void_p(ws.data_ptr()), need, None)
+        assert st == 0, paro.STATUS.get(st, st)
+
+    ys = [torch.empty_like(xs[0]) for _ in range(ring)]
+    cases = [("activation", True), ("weight", True), ("activation", False)]
+    fns = [lambda i, c=c: call(i, *c) for c in cases]
+    fns.append(lambda i: paro.paro_rotate(r, xs[i % ring], ys[i % ring]))
+    settle(torch, fns, args.warmup + 2)
+    n = max(args.steps, 20)
+    times = [[] for _ in fns]
+    for _ in range(2):
+        for f, tl in zip(fns, times):
+            s = T.event()
+            for i in range(n):
+                f(i)
+            e = T.event()
+            torch.cuda.synchronize()
+            tl.append(s.elapsed_time(e) / n)
+    ms = [float(np.mean(t)) for t in times]
+    part = need  # partial sums: written once, read once
+    pts = []
+    for (side, with_gx), t in zip(cases, ms):
+        alg = (2 + 4 + (4 if with_gx else 0)) * M * d
+        gbps = alg / (t * 1e-3) / 1e9
+        pts.append({"side": side, "input_gradient": with_gx, "us": round(t * 1e3, 2),
+                    "algorithmic_bytes": alg, "partial_sum_bytes": 2 * part, "gbps": round(gbps, 1),
+                    "frac": round(gbps / HBM_PEAK_GBPS, 4)})
+        log(f"[backward] {side} gx={with_gx}: {t*1e3:.1f} us, {gbps:.0f} GB/s")
+    fwd_us = ms[-1] * 1e3
+    log(f"[backward] forward transform for reference: {fwd_us:.1f} us")
+    head = pts[0]
+    return {
+        "metric": "transform gradient HBM GB/s (paro_rotation_backward, 8192 x 4096, K = 8)",
+        "value": head["gbps"], "unit": "GB/s", "n_gpus": 1, "steps": n, "warmup": args.warmup,
+        "ms_per_step": round(head["us"] / 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "rotation_backward_8192x4096_K8", "group": 128, "K": K},
+        "points": pts, "forward_transform_us": round(fwd_us, 2),
+        "roofline": {"bound": "hbm", "achieved": head["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": head["frac"], "traffic": None,
+                     "note": "whole call (gradient kernel + chunk reduction)"},
+    }
+
+
 def bench_chain(args, paro, torch):
     """The seven linears of one Llama-3-8B decoder layer in sequence (q, k, v, o,
     gate, up, down; attention and activations left out), as rotated W4G128,
@@ -646,8 +721,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill_mlp",
-                    choices=["prefill_mlp", "prefill_down", "decode", "sweep", "sparse", "tiny", "copy",
-                             "chain"])
+                    choices=["prefill_mlp", "prefill_down", "decode", "sweep", "sparse", "backward",
+                             "tiny", "copy", "chain"])
     ap.add_argument("--ring", type=int, default=0, help="distinct input copies cycled (0 = auto)")
     ap.add_argument("--decode-m", default="1,4,16", help="token counts of the decode workload")
     ap.add_argument("--chain-m", default="1,16,2048", help="token counts of the layer-chain workload")
@@ -684,6 +759,8 @@ def main():
         out = bench_chain(args, paro, torch)
     elif args.workload == "sparse":
         out = bench_sparse(args, paro, torch)
+    elif args.workload == "backward":
+        out = bench_backward(args, paro, torch)
     else:
         out = bench_copy(args, torch)
     print(json.dumps(out), flush=True)

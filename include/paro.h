@@ -207,6 +207,59 @@ int paro_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qwe
                    uint16_t* y, int64_t M, int64_t N, int64_t d, int32_t group,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Which transform paro_rotation_backward differentiates. */
+typedef enum {
+  PARO_SIDE_ACTIVATION = 0, /* X' = X T^-1, as paro_rotate computes it */
+  PARO_SIDE_WEIGHT = 1      /* the rows of T W in the [N][d] layout, as the quantizer transforms them */
+} paro_side;
+
+/* Bytes of device scratch paro_rotation_backward needs for M rows (0 when
+ * M <= 0). */
+size_t paro_rotation_backward_workspace_size(const paro_rotation* r, int64_t M);
+
+/*
+ * Gradients of the transform with respect to its input, its angles and its
+ * channel scales: the step that learns theta and alpha by minimising the
+ * layer-wise output loss (paper notes, "损失函数 / 训练策略"). For every row r
+ * of x (a token for PARO_SIDE_ACTIVATION; a weight row, [N][d] layout, for
+ * PARO_SIDE_WEIGHT) the transform is v_0 = r / alpha (activation) or
+ * r * alpha (weight), then the K stages in order with the pair update
+ * (v_i, v_j) <- (c v_i - s v_j, s v_i + c v_j) (CSDN article, section 2.2).
+ * Given gy = dL/d(output):
+ *   gx[m][k]     = dL/dr: gy walked back through the transposed stages, then
+ *                  divided (activation) or multiplied (weight) by alpha;
+ *   dtheta[t][p] = sum over rows of g'_j v'_i - g'_i v'_j, with (i, j) the
+ *                  stored pair p of stage t, v' that stage's outputs and g'
+ *                  their gradient (d v'_i / d theta = -v'_j,
+ *                  d v'_j / d theta = v'_i); pairs with theta = 0 included;
+ *   dalpha[k]    = sum over rows of g_0[k] * d v_0[k] / d alpha[k], i.e.
+ *                  -g_0 r / alpha^2 (activation) or g_0 r (weight),
+ * with g_0 the gradient of v_0.
+ *
+ *   side     PARO_SIDE_ACTIVATION or PARO_SIDE_WEIGHT, else PARO_ERR_VALUE.
+ *   x        device fp16 [M][d] (4-byte aligned): the transform's input.
+ *   gy       device fp32 [M][d] (8-byte aligned): gradient of its output.
+ *   gx       device fp32 [M][d] (8-byte aligned) or NULL (not computed); may
+ *            be gy itself (in place).
+ *   dtheta   device fp32 [K][d/2] (may be NULL when K == 0), overwritten.
+ *   dalpha   device fp32 [d], overwritten.
+ *   M        rows, 0 <= M < 2^31 (M == 0 writes zero gradients).
+ *   workspace, workspace_bytes: device scratch of at least
+ *            paro_rotation_backward_workspace_size(r, M) bytes, 256-byte
+ *            aligned (NULL when that size is 0); calls that may overlap need
+ *            different workspaces.
+ *
+ * Arithmetic: fp32. The stages' inputs are recovered from their outputs by
+ * the transposed update instead of being stored. The sums over rows are taken
+ * per chunk of rows and the chunks added in a fixed order: the result does
+ * not depend on scheduling.
+ * Errors: PARO_ERR_NULL, PARO_ERR_VALUE, PARO_ERR_SHAPE, PARO_ERR_ALIGN,
+ * PARO_ERR_WORKSPACE, PARO_ERR_HIP.
+ */
+int paro_rotation_backward(const paro_rotation* r, int32_t side, const uint16_t* x,
+                           const float* gy, float* gx, float* dtheta, float* dalpha, int64_t M,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /*
  * Host-only view of the per-segment rotation schedule that
  * paro_rotation_create uploads (for testing the plan logic without a GPU).

@@ -7,7 +7,8 @@ fallback: if the library is missing or no GPU is visible the calls raise.
 
 Names follow the C ABI: ``paro_rotation_create`` / ``Rotation``,
 ``paro_rotate``, ``paro_quantize_weights``, ``paro_w4_linear``,
-``paro_w4_linear_workspace_size``.
+``paro_w4_linear_workspace_size``, ``paro_rotation_backward``,
+``paro_rotation_backward_workspace_size``.
 """
 from __future__ import annotations
 
@@ -65,6 +66,10 @@ def load_library() -> ctypes.CDLL:
     lib.paro_w4_linear.restype = ctypes.c_int
     lib.paro_w4_linear.argtypes = [vp, vp, vp, vp, vp, vp, vp, c_i64, c_i64, c_i64, c_i32, vp,
                                    c_size, vp]
+    lib.paro_rotation_backward_workspace_size.restype = c_size
+    lib.paro_rotation_backward_workspace_size.argtypes = [vp, c_i64]
+    lib.paro_rotation_backward.restype = ctypes.c_int
+    lib.paro_rotation_backward.argtypes = [vp, c_i32, vp, vp, vp, vp, vp, c_i64, vp, c_size, vp]
     lib.paro_rotation_plan_host.restype = ctypes.c_int
     lib.paro_rotation_plan_host.argtypes = [c_i64, c_i32, c_i32, vp, vp, vp, vp, c_size,
                                             ctypes.POINTER(c_size), ctypes.POINTER(c_i32)]
@@ -196,6 +201,37 @@ def paro_w4_linear(r: Optional[Rotation], x, qweight, scales, zeros, bias=None, 
         _dptr(bias, "bias", torch.float16) if bias is not None else None,
         _dptr(y, "y", torch.float16), M, N, d, group, ws_ptr, ws_bytes, _stream(stream)))
     return y
+
+
+SIDES = {"activation": 0, "weight": 1}
+
+
+def paro_rotation_backward_workspace_size(r: Rotation, M: int) -> int:
+    return int(load_library().paro_rotation_backward_workspace_size(r.handle, M))
+
+
+def paro_rotation_backward(r: Rotation, x, gy, side: str = "activation", gx=None,
+                           want_gx: bool = True, workspace=None, stream=None):
+    """Gradients of the transform: returns (gx fp32 [M][d] or None, dtheta fp32
+    [K][d/2], dalpha fp32 [d]) for x fp16 [M][d] and gy = dL/d(output) fp32."""
+    import torch
+    M, d = x.shape
+    info_K = r.K
+    if gx is None and want_gx:
+        gx = torch.empty((M, d), dtype=torch.float32, device=x.device)
+    dtheta = torch.empty((info_K, d // 2), dtype=torch.float32, device=x.device)
+    dalpha = torch.empty((d,), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        need = paro_rotation_backward_workspace_size(r, M)
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
+    ws_ptr = _dptr(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load_library().paro_rotation_backward(
+        r.handle, SIDES[side], _dptr(x, "x", torch.float16), _dptr(gy, "gy", torch.float32),
+        _dptr(gx, "gx", torch.float32) if gx is not None else None,
+        _dptr(dtheta, "dtheta", torch.float32) if info_K else None,
+        _dptr(dalpha, "dalpha", torch.float32), M, ws_ptr, ws_bytes, _stream(stream)))
+    return gx, dtheta, dalpha
 
 
 def paro_rotation_plan_host(pairs, theta, alpha, group: int) -> Tuple[np.ndarray, dict]:

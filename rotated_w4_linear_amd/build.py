@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libparo.so")
 
-SOURCES = ["api.cpp", "plan.cpp", "rotate.hip", "quantize.hip", "w4_linear.hip", "decode.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "rotate.hip", "quantize.hip", "w4_linear.hip", "decode.hip",
+           "backward.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -41,6 +41,7 @@ void free_rotation(paro_rotation* r) {
   if (r->d_wt_c) (void)hipFree(r->d_wt_c);
   if (r->d_wt_s) (void)hipFree(r->d_wt_s);
   if (r->d_alpha) (void)hipFree(r->d_alpha);
+  if (r->d_bw) (void)hipFree(r->d_bw);
   delete r;
 }
 
@@ -118,7 +119,8 @@ int paro_rotation_create(int64_t d, int32_t group, int32_t K, const int32_t* pai
       (st = upload(&r->d_wt_pairs, plan.wt_pairs)) != PARO_OK ||
       (st = upload(&r->d_wt_c, plan.wt_c)) != PARO_OK ||
       (st = upload(&r->d_wt_s, plan.wt_s)) != PARO_OK ||
-      (st = upload(&r->d_alpha, plan.alpha)) != PARO_OK) {
+      (st = upload(&r->d_alpha, plan.alpha)) != PARO_OK ||
+      (st = upload(&r->d_bw, plan.bw)) != PARO_OK) {
     free_rotation(r);
     return st;
   }
@@ -296,6 +298,52 @@ int paro_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qwe
     e = launch_w4_gemm(xin, qweight, scales, zeros, bias, y, M, N, d, group, stream);
   }
   if (e != hipSuccess) return hip_fail(e, "paro_w4_linear launch");
+  return PARO_OK;
+}
+
+size_t paro_rotation_backward_workspace_size(const paro_rotation* r, int64_t M) {
+  if (!r || M <= 0) return 0;
+  return (paro::rotate_backward_scratch_bytes(r, M) + 255) & ~(size_t)255;
+}
+
+int paro_rotation_backward(const paro_rotation* r, int32_t side, const uint16_t* x,
+                           const float* gy, float* gx, float* dtheta, float* dalpha, int64_t M,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  using namespace paro;
+  if (!r) {
+    set_error("paro_rotation_backward: NULL rotation");
+    return PARO_ERR_NULL;
+  }
+  if (side != PARO_SIDE_ACTIVATION && side != PARO_SIDE_WEIGHT) {
+    set_error("paro_rotation_backward: side must be PARO_SIDE_ACTIVATION or PARO_SIDE_WEIGHT");
+    return PARO_ERR_VALUE;
+  }
+  if (M < 0 || M >= (int64_t(1) << 31)) {
+    set_error("paro_rotation_backward: M must be in [0, 2^31)");
+    return PARO_ERR_SHAPE;
+  }
+  if (!dalpha || (r->K > 0 && !dtheta) || (M > 0 && (!x || !gy))) {
+    set_error("paro_rotation_backward: NULL tensor");
+    return PARO_ERR_NULL;
+  }
+  if (((uintptr_t)x & 3) || ((uintptr_t)gy & 7) || ((uintptr_t)gx & 7) || ((uintptr_t)dtheta & 3) ||
+      ((uintptr_t)dalpha & 3)) {
+    set_error("paro_rotation_backward: x must be 4-byte aligned, gy and gx 8-byte aligned");
+    return PARO_ERR_ALIGN;
+  }
+  const size_t need = paro_rotation_backward_workspace_size(r, M);
+  if (need && (!workspace || workspace_bytes < need)) {
+    set_error("paro_rotation_backward: workspace missing or smaller than "
+              "paro_rotation_backward_workspace_size");
+    return PARO_ERR_WORKSPACE;
+  }
+  if (need && ((uintptr_t)workspace & 255)) {
+    set_error("paro_rotation_backward: workspace must be 256-byte aligned");
+    return PARO_ERR_ALIGN;
+  }
+  hipError_t e = launch_rotate_backward(r, side == PARO_SIDE_WEIGHT, x, gy, gx, dtheta, dalpha, M,
+                                        workspace, stream);
+  if (e != hipSuccess) return hip_fail(e, "paro_rotation_backward launch");
   return PARO_OK;
 }
 

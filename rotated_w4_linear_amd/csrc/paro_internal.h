@@ -64,6 +64,9 @@ struct RotPlanHost {
   std::vector<uint32_t> wt_pairs;  // [groups][K][G/2]
   std::vector<float> wt_c, wt_s;   // [groups][K][G/2]
   std::vector<float> alpha;        // [d]
+  // gradient kernel: per segment, stage, lane slot: (i | j << 16, c bits,
+  // s bits, flat pair index)
+  std::vector<uint32_t> bw;        // [segs][K][seg_ch / 2][4]
 };
 
 // Validates arguments and builds the schedule. Returns a paro_status.
@@ -71,6 +74,13 @@ int build_rotation_plan(int64_t d, int32_t group, int32_t K, const int32_t* pair
                         const float* theta, const float* alpha, RotPlanHost* out);
 
 void set_error(const std::string& msg);
+
+// Gradients of the transform (activation side: X' = X T^-1; weight side:
+// rows of T W). part is scratch of rotate_backward_scratch_bytes(r, M).
+size_t rotate_backward_scratch_bytes(const paro_rotation* r, int64_t M);
+hipError_t launch_rotate_backward(const paro_rotation* r, int weight_side, const uint16_t* x,
+                                  const float* gy, float* gx, float* dtheta, float* dalpha,
+                                  int64_t M, void* part, hipStream_t stream);
 
 }  // namespace paro
 
@@ -85,6 +95,7 @@ struct paro_rotation {
   float* d_wt_c;
   float* d_wt_s;
   float* d_alpha;
+  uint32_t* d_bw;       // device copy of RotPlanHost::bw
 };
 
 namespace paro {

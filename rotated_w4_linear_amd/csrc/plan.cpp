@@ -252,6 +252,106 @@ struct LaneState {
   std::vector<std::vector<int>> kept, fetched, src;  // [tau][v]
 };
 
+// Lane slots of one stage for the gradient kernel, which keeps a batch in LDS
+// channel-major with channel c's rows in 16-byte slot c and reads (writes) the
+// rows of a slot's two channels with one 16-byte access per channel. gfx950
+// serves such reads without bank conflicts when every 16 consecutive lanes hit
+// slots distinct modulo 16, i.e. channels distinct modulo 16, and writes when
+// every 8 consecutive lanes hit channels distinct modulo 8. The pairs of a stage are placed as follows:
+//  * each pair is oriented (its first channel a, second b) so that every
+//    residue modulo 16 is first as often as it is second: an Eulerian
+//    orientation of the multigraph on the 16 residues whose edges are the
+//    pairs (every residue has even degree, two per channel); a pair stored
+//    the other way round is the same rotation with the sine negated and its
+//    angle gradient negated;
+//  * the oriented pairs form a regular bipartite multigraph (first residue
+//    -> second residue) that splits into perfect matchings of 16 pairs, one
+//    per 16-lane block and slot;
+//  * inside a block, the two halves of 8 lanes take the two perfect matchings
+//    of the 2-regular graph of residues modulo 8.
+// pr[k] = (i, j) segment-local; returns pos[k] (the slot index lane * ppl + q)
+// and flip[k]; an empty result if a step fails (it cannot for valid input).
+bool plan_backward_slots(const std::vector<std::pair<int, int>>& pr, int ppl, std::vector<int>& pos,
+                         std::vector<char>& flip) {
+  const int np = (int)pr.size();  // 64 ppl
+  // Eulerian orientation by closed trails
+  std::vector<std::vector<std::pair<int, int>>> g(16);
+  for (int k = 0; k < np; ++k) {
+    g[pr[k].first & 15].push_back({pr[k].second & 15, k});
+    g[pr[k].second & 15].push_back({pr[k].first & 15, k});
+  }
+  std::vector<char> used(np, 0);
+  std::vector<size_t> it(16, 0);
+  flip.assign(np, 0);
+  std::vector<int> tail(np), head(np);
+  for (int s0 = 0; s0 < 16; ++s0) {
+    for (;;) {
+      int u = s0;
+      bool moved = false;
+      for (;;) {
+        while (it[u] < g[u].size() && used[g[u][it[u]].second]) ++it[u];
+        if (it[u] == g[u].size()) break;
+        const auto [w, k] = g[u][it[u]];
+        used[k] = 1;
+        // orient k as u -> w
+        if ((pr[k].first & 15) == u) {
+          flip[k] = 0;
+        } else {
+          flip[k] = 1;
+        }
+        tail[k] = u;
+        head[k] = w;
+        u = w;
+        moved = true;
+      }
+      if (!moved) break;
+    }
+  }
+  // perfect matchings of the bipartite multigraph tail -> head
+  std::vector<std::vector<std::pair<int, int>>> adj(16);
+  for (int k = 0; k < np; ++k) adj[tail[k]].push_back({head[k], k});
+  std::vector<char> taken(np, 0);
+  std::vector<int> match_of(np, -1);
+  const int nm = np / 16;
+  for (int m = 0; m < nm; ++m) {
+    std::vector<int> mr(16, -1), me(16, -1);
+    for (int u = 0; u < 16; ++u) {
+      std::vector<char> seen(16, 0);
+      augment(u, adj, mr, me, seen, taken);
+    }
+    for (int v = 0; v < 16; ++v) {
+      if (me[v] < 0) return false;
+      taken[me[v]] = 1;
+      match_of[me[v]] = m;
+    }
+  }
+  // halves of each matching, and positions
+  pos.assign(np, -1);
+  for (int m = 0; m < nm; ++m) {
+    std::vector<int> ks;
+    for (int k = 0; k < np; ++k)
+      if (match_of[k] == m) ks.push_back(k);
+    std::vector<std::vector<std::pair<int, int>>> a8(8);
+    std::vector<char> t8(np, 0);
+    for (int k : ks) a8[tail[k] & 7].push_back({head[k] & 7, k});
+    int fill[2] = {0, 0};
+    for (int h = 0; h < 2; ++h) {
+      std::vector<int> mr(8, -1), me(8, -1);
+      for (int u = 0; u < 8; ++u) {
+        std::vector<char> seen(8, 0);
+        augment(u, a8, mr, me, seen, t8);
+      }
+      for (int v = 0; v < 8; ++v) {
+        if (me[v] < 0) return false;
+        t8[me[v]] = 1;
+        const int lane = 16 * (m % 4) + 8 * h + fill[h]++;
+        pos[me[v]] = lane * ppl + m / 4;
+      }
+    }
+  }
+  return true;
+}
+
 }  // namespace
 
 int build_rotation_plan(int64_t d, int32_t group, int32_t K, const int32_t* pairs,
@@ -344,6 +444,48 @@ int build_rotation_plan(int64_t d, int32_t group, int32_t K, const int32_t* pair
         double th = (double)theta[t * half + p];
         P.wt_c[at] = (float)std::cos(th);
         P.wt_s[at] = (float)std::sin(th);
+      }
+    }
+  }
+
+  // ---- table of the gradient kernel --------------------------------------------
+  // Per segment, stage and lane slot k (lane k / ppl, sub-slot k % ppl): the
+  // pair's segment-local channels (i | j << 16), fp32 cos and sin (the same
+  // roundings as the weight transform), and the pair's flat index t * d/2 + p
+  // in the caller's theta. Identities (theta = 0) are kept: their angle
+  // gradient is not zero.
+  // Slots are placed by plan_backward_slots; a pair stored the other way
+  // round has its sine negated and bit 31 of the index set (its angle
+  // gradient is negated when written out).
+  {
+    const int ppl = seg_ch / 128;
+    P.bw.assign((size_t)segs * K * nv * 4, 0);
+    std::vector<std::vector<int64_t>> members(segs);
+    for (int t = 0; t < K; ++t) {
+      for (auto& m : members) m.clear();
+      for (int64_t p = 0; p < half; ++p) members[pairs[(t * half + p) * 2] / seg_ch].push_back(p);
+      for (int sg = 0; sg < segs; ++sg) {
+        std::vector<std::pair<int, int>> pr;
+        for (int64_t p : members[sg])
+          pr.push_back({(int)(pairs[(t * half + p) * 2] - (int64_t)sg * seg_ch),
+                        (int)(pairs[(t * half + p) * 2 + 1] - (int64_t)sg * seg_ch)});
+        std::vector<int> pos;
+        std::vector<char> flip;
+        if ((int)pr.size() != nv || !plan_backward_slots(pr, ppl, pos, flip)) {
+          set_error("internal: could not place the gradient kernel's pairs");
+          return PARO_ERR_HIP;
+        }
+        for (int k = 0; k < nv; ++k) {
+          const int64_t p = members[sg][k];
+          uint32_t* e = &P.bw[(((size_t)sg * K + t) * nv + (size_t)pos[k]) * 4];
+          const int a = flip[k] ? pr[k].second : pr[k].first, b = flip[k] ? pr[k].first : pr[k].second;
+          e[0] = (uint32_t)a | ((uint32_t)b << 16);
+          const double th = (double)theta[t * half + p];
+          const float sn = (float)std::sin(th);
+          e[1] = fbits((float)std::cos(th));
+          e[2] = fbits(flip[k] ? -sn : sn);
+          e[3] = (uint32_t)(t * half + p) | (flip[k] ? 0x80000000u : 0u);
+        }
       }
     }
   }

@@ -502,3 +502,98 @@ def test_linear_prefill_down_sampled(paro):
     rows = np.sort(synthetic.rng_for(3500, 1).choice(x.shape[0], 48, replace=False))
     rows[-1] = x.shape[0] - 1
     check_linear(paro, x, layer, rows=rows)
+
+
+# ----------------------------------------------------------------------------
+# gradients of the transform
+# ----------------------------------------------------------------------------
+
+def backward_ref(x, g, layer, side, block=1024):
+    """The oracle's gradients, its row sums taken over blocks of rows (each row
+    is independent, so the block sums add up to the same sums)."""
+    M, d = x.shape
+    K = layer.pairs.shape[0]
+    gx = np.zeros((M, d))
+    dth = np.zeros((K, d // 2))
+    dal = np.zeros(d)
+    for m0 in range(0, max(M, 1), block):
+        sl = slice(m0, min(M, m0 + block))
+        a, b, c = oracle.rotation_backward(x[sl], g[sl], layer.pairs, layer.theta, layer.alpha, side)
+        gx[sl] = a
+        dth += b
+        dal += c
+    return gx, dth, dal
+
+
+def check_backward(paro, x, g, layer, side, rows=None, want_gx=True):
+    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, layer.group)
+    gx, dth, dal = paro.paro_rotation_backward(r, dev(x), dev(g), side, want_gx=want_gx)
+    rgx, rdth, rdal = backward_ref(x, g, layer, side)
+    errs = {"dtheta": metrics.assert_grad_close(host(dth), rdth, "dtheta"),
+            "dalpha": metrics.assert_grad_close(host(dal), rdal, "dalpha")}
+    if want_gx:
+        idx = np.arange(x.shape[0]) if rows is None else rows
+        errs["gx"] = metrics.assert_grad_close(host(gx)[idx], rgx[idx], "gx")
+    r.close()
+    return errs
+
+
+def grad_case(seed, M, d, G, K, side, keep=1.0):
+    x, layer = synthetic.sparse_rotation_case(seed, M, d, G, K, keep) if keep < 1.0 else \
+        synthetic.rotation_case(seed, M, d, G, K)
+    if side == "weight":
+        x = synthetic.draw_w(synthetic.rng_for(4000, seed), M, d, 0.02, n_outlier_cols=2)
+    g = synthetic.rng_for(4100, seed).standard_normal((M, d)).astype(np.float32)
+    return x, g, layer
+
+
+@pytest.mark.parametrize("side", ["activation", "weight"])
+@pytest.mark.parametrize("G,K,d,M", [(128, 8, 256, 5), (128, 8, 512, 37), (64, 8, 512, 9),
+                                     (256, 8, 512, 21), (128, 1, 128, 3), (128, 0, 256, 4),
+                                     (128, 32, 256, 11), (256, 3, 768, 1), (64, 5, 384, 300)])
+def test_backward_shapes(paro, side, G, K, d, M):
+    log(f"backward {side} G={G} K={K} d={d} M={M}")
+    x, g, layer = grad_case(G + K + d + M, M, d, G, K, side)
+    check_backward(paro, x, g, layer, side)
+
+
+def test_backward_sparse_pairing_and_no_input_gradient(paro):
+    """Identities (theta = 0) still get angle gradients; gx = NULL skips the input gradient."""
+    log("backward sparse pairing, gx = NULL")
+    x, g, layer = grad_case(5, 40, 1024, 128, 8, "activation", keep=0.1)
+    check_backward(paro, x, g, layer, "activation", want_gx=False)
+
+
+def test_backward_in_place_and_empty(paro):
+    log("backward in place / M = 0")
+    x, g, layer = grad_case(6, 19, 512, 128, 8, "activation")
+    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, 128)
+    gd = dev(g)
+    gx, dth, dal = paro.paro_rotation_backward(r, dev(x), gd, "activation", gx=gd)
+    rgx, rdth, rdal = backward_ref(x, g, layer, "activation")
+    metrics.assert_grad_close(host(gd), rgx, "gx in place")
+    metrics.assert_grad_close(host(dth), rdth, "dtheta")
+    e = torch.empty((0, 512), dtype=torch.float16, device="cuda")
+    ge = torch.empty((0, 512), dtype=torch.float32, device="cuda")
+    _, dth, dal = paro.paro_rotation_backward(r, e, ge, "activation")
+    assert not host(dth).any() and not host(dal).any()
+
+
+def test_backward_deterministic(paro):
+    x, g, layer = grad_case(7, 300, 1024, 128, 8, "activation")
+    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, 128)
+    a = [host(t) for t in paro.paro_rotation_backward(r, dev(x), dev(g), "activation")]
+    b = [host(t) for t in paro.paro_rotation_backward(r, dev(x), dev(g), "activation")]
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+@pytest.mark.parametrize("side", ["activation", "weight"])
+def test_backward_prefill_layer(paro, side):
+    """The benchmark's shape (8192 x 4096, K = 8): angle and scale gradients in
+    full, input gradients on sampled rows."""
+    M, d = 8192, 4096
+    log(f"backward {side} {M}x{d}")
+    x, g, layer = grad_case(8 if side == "activation" else 9, M, d, 128, 8, side)
+    rows = np.sort(synthetic.rng_for(4200, 0).choice(M, 256, replace=False))
+    check_backward(paro, x, g, layer, side, rows=rows)

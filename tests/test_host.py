@@ -95,6 +95,10 @@ def test_create_validation_errors(paro):
 
 def test_hot_calls_validate_before_any_launch(paro):
     lib = paro.load_library()
+    # gradients of the transform: the handle comes first
+    d4 = ctypes.c_void_p(16 * 1024)
+    assert lib.paro_rotation_backward(None, 0, d4, d4, d4, d4, d4, 4, None, 0, None) == -1
+    assert lib.paro_rotation_backward_workspace_size(None, 4) == 0
     assert lib.paro_rotate(None, None, None, 4, None) == -1
     assert lib.paro_rotate(None, None, None, 0, None) == -1  # handle still required
     dummy = ctypes.c_void_p(16 * 1024)

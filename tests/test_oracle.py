@@ -386,6 +386,12 @@ def test_metrics_floor():
     got = ref + np.array([[1e-4, 1e-6, 0, 0]])
     fl, raw, n = metrics.rotated_error(got, ref, 4)
     assert raw > 1 and fl < 2e-3
+    # gradients: relative to each entry, floored at the rms of the output
+    ref = np.array([300.0, 1.0, -1.0, 1e-12])
+    rms = np.sqrt(np.mean(ref * ref))
+    assert np.isclose(metrics.grad_error(ref + [3e-3, 0, 0, 0], ref), 1e-5)
+    assert np.isclose(metrics.grad_error(ref + [0, 0, 0, 1e-3 * rms], ref), 1e-3)
+    assert metrics.grad_error(np.zeros(0), np.zeros(0)) == 0.0
 
 
 # ----------------------------------------------------------------------------
