@@ -596,8 +596,10 @@ def bench_backward(args, paro, torch):
         "config": {"workload": "rotation_backward_8192x4096_K8", "group": 128, "K": K},
         "points": pts, "forward_transform_us": round(fwd_us, 2),
         "roofline": {"bound": "hbm", "achieved": head["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": head["frac"], "traffic": None,
-                     "note": "whole call (gradient kernel + chunk reduction)"},
+                     "frac": head["frac"],
+                     "traffic": traffic_for("rotate_backward:8192x4096_K8"),
+                     "note": "achieved over the whole call (gradient kernel + chunk reduction); "
+                             "traffic is the gradient kernel's"},
     }
 
 
