@@ -62,7 +62,7 @@ __all__ = [
     "check_rotation_params", "cos_sin_f32", "rotate_activations",
     "transform_weights_f32", "transform_weights_f64", "quantize_groups",
     "pack_codes", "unpack_codes", "dequantize", "quantize_weights", "linear",
-    "rotated_w4_linear", "rotation_backward", "QuantizeError",
+    "rotated_w4_linear", "rotation_backward", "layer_loss", "QuantizeError",
 ]
 
 
@@ -341,3 +341,44 @@ def rotated_w4_linear(x, qweight, scales, zeros, group, pairs=None, theta=None, 
     else:
         xr = rotate_activations(x, pairs, theta, alpha)
     return linear(xr, qweight, scales, zeros, group, bias)
+
+
+# ----------------------------------------------------------------------------
+# Layer-wise output loss (transform learning)
+# ----------------------------------------------------------------------------
+
+def layer_loss(x, w, qweight, scales, zeros, group, pairs, theta, alpha, grad=False, round16=True):
+    """Layer-wise output loss of the quantized, transformed layer, and its
+    gradients with respect to the angles and scales (fp64).
+
+    [Notes] "损失函数 / 训练策略": L = ||Q(D)(X') - D(X)||, here the squared
+    Frobenius norm L = sum (Y_q - Y)^2 with D(X) = X W^T the layer in its
+    original fp16 weights and Q(D)(X') = X' W_hat^T the 4-bit layer on the
+    transformed activations (W_hat the dequantized Q(T W)). With round16 the
+    intermediate results are rounded to fp16 where the product path stores
+    them (X' and Y_q).
+
+    Gradients (grad=True) pass through the quantizer unchanged (the
+    straight-through reading of training through Q): dL/dY_q = 2 (Y_q - Y),
+    dL/dX' = dY W_hat, dL/dW_hat = dY^T X' taken as dL/d(T W), then each
+    transform's own gradients (``rotation_backward``, activation side for X',
+    weight side for T W), summed. Returns L, or (L, dtheta [K][d/2], dalpha [d]).
+    """
+    xr = rotate_activations(x, pairs, theta, alpha)
+    if round16:
+        xr = xr.astype(np.float16).astype(np.float64)
+    what = dequantize(qweight, scales, zeros, group)
+    yq = xr @ what.T
+    if round16:
+        yq = yq.astype(np.float16).astype(np.float64)
+    y = np.asarray(x).astype(np.float64) @ np.asarray(w).astype(np.float64).T
+    diff = yq - y
+    loss = float(np.sum(diff * diff))
+    if not grad:
+        return loss
+    dy = 2.0 * diff
+    dxr = dy @ what
+    dw = dy.T @ xr
+    _, dth_a, dal_a = rotation_backward(x, dxr, pairs, theta, alpha, "activation")
+    _, dth_w, dal_w = rotation_backward(w, dw, pairs, theta, alpha, "weight")
+    return loss, dth_a + dth_w, dal_a + dal_w

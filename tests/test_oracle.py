@@ -511,3 +511,61 @@ def test_b4_weight_side_is_activation_side_with_inverse_scales():
     assert np.allclose(dw, dx, rtol=1e-13, atol=1e-13)
     assert np.allclose(dth_w, dth_a, rtol=1e-12, atol=1e-12)
     assert np.allclose(dal_w, -dal_a / alpha.astype(np.float64) ** 2, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# L1-L2: the layer-wise output loss and its straight-through gradients
+# ----------------------------------------------------------------------------
+
+def test_l_loss_is_the_output_error_of_the_quantized_layer():
+    """L = ||X' W_hat^T - X W^T||_F^2, and with K = 0 and alpha = 1 it is the
+    plain W4 layer's squared output error."""
+    rng = synthetic.rng_for(96, 0)
+    d, N, M, G = 128, 16, 5, 64
+    x = synthetic.draw_x(rng, M, d, 1, 5.0)
+    w = synthetic.draw_w(rng, N, d, 0.05)
+    pairs = np.zeros((0, d // 2, 2), np.int32)
+    theta = np.zeros((0, d // 2), np.float32)
+    alpha = np.ones(d, np.float32)
+    q, s, z = oracle.quantize_weights(w, G)
+    what = oracle.dequantize(q, s, z, G)
+    want = np.sum((x.astype(np.float64) @ what.T - x.astype(np.float64) @ w.astype(np.float64).T) ** 2)
+    got = oracle.layer_loss(x, w, q, s, z, G, pairs, theta, alpha, round16=False)
+    assert np.isclose(got, want, rtol=1e-12)
+
+
+def test_l_gradients_match_finite_differences_with_frozen_quantization_error():
+    """The straight-through gradients equal the exact gradients of the smooth
+    surrogate L~(theta, alpha) = ||X'(theta, alpha) (T W + E0)^T - X W^T||^2,
+    in which the quantization error E0 = W_hat - T W is frozen at the base
+    point: checked against finite differences of L~ built from the forward
+    transforms alone."""
+    d, N, M, G, K = 16, 6, 4, 8, 2
+    pairs, theta, alpha = grid_params(3, d, G, K)
+    rng = synthetic.rng_for(96, 1)
+    x = synthetic.draw_x(rng, M, d, 1, 5.0)
+    w = synthetic.draw_w(rng, N, d, 0.3)
+    q, s, z = oracle.quantize_weights(w, G, pairs, theta, alpha)
+    e0 = oracle.dequantize(q, s, z, G) - oracle.transform_weights_f64(w, pairs, theta, alpha)
+    y = x.astype(np.float64) @ w.astype(np.float64).T
+    _, dth, dal = oracle.layer_loss(x, w, q, s, z, G, pairs, theta, alpha, grad=True, round16=False)
+
+    def surrogate(th, al):
+        xr = oracle.rotate_activations(x, pairs, th, al)
+        u = oracle.transform_weights_f64(w, pairs, th, al) + e0
+        return float(np.sum((xr @ u.T - y) ** 2))
+
+    h = 2.0 ** -8
+    for t in range(K):
+        for p in range(d // 2):
+            def f(e, t=t, p=p):
+                th = theta.copy()
+                th[t, p] = np.float32(theta[t, p] + e)
+                return surrogate(th, alpha)
+            assert abs(richardson(f, h) - dth[t, p]) <= 1e-8 * (1 + abs(dth[t, p]))
+    for k in range(d):
+        def f(e, k=k):
+            al = alpha.copy()
+            al[k] = np.float32(alpha[k] + e)
+            return surrogate(theta, al)
+        assert abs(richardson(f, h) - dal[k]) <= 1e-8 * (1 + abs(dal[k]))
