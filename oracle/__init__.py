@@ -356,7 +356,8 @@ def layer_loss(x, w, qweight, scales, zeros, group, pairs, theta, alpha, grad=Fa
     original fp16 weights and Q(D)(X') = X' W_hat^T the 4-bit layer on the
     transformed activations (W_hat the dequantized Q(T W)). With round16 the
     intermediate results are rounded to fp16 where the product path stores
-    them (X' and Y_q).
+    them (X' and Y_q) for the loss; the gradients treat those roundings, like
+    the quantizer, as the identity.
 
     Gradients (grad=True) pass through the quantizer unchanged (the
     straight-through reading of training through Q): dL/dY_q = 2 (Y_q - Y),
@@ -364,9 +365,8 @@ def layer_loss(x, w, qweight, scales, zeros, group, pairs, theta, alpha, grad=Fa
     transform's own gradients (``rotation_backward``, activation side for X',
     weight side for T W), summed. Returns L, or (L, dtheta [K][d/2], dalpha [d]).
     """
-    xr = rotate_activations(x, pairs, theta, alpha)
-    if round16:
-        xr = xr.astype(np.float16).astype(np.float64)
+    xr_exact = rotate_activations(x, pairs, theta, alpha)
+    xr = xr_exact.astype(np.float16).astype(np.float64) if round16 else xr_exact
     what = dequantize(qweight, scales, zeros, group)
     yq = xr @ what.T
     if round16:
@@ -378,7 +378,7 @@ def layer_loss(x, w, qweight, scales, zeros, group, pairs, theta, alpha, grad=Fa
         return loss
     dy = 2.0 * diff
     dxr = dy @ what
-    dw = dy.T @ xr
+    dw = dy.T @ xr_exact  # the fp16 rounding of X' passes gradients unchanged too
     _, dth_a, dal_a = rotation_backward(x, dxr, pairs, theta, alpha, "activation")
     _, dth_w, dal_w = rotation_backward(w, dw, pairs, theta, alpha, "weight")
     return loss, dth_a + dth_w, dal_a + dal_w

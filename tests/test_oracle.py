@@ -569,3 +569,21 @@ def test_l_gradients_match_finite_differences_with_frozen_quantization_error():
             al[k] = np.float32(alpha[k] + e)
             return surrogate(theta, al)
         assert abs(richardson(f, h) - dal[k]) <= 1e-8 * (1 + abs(dal[k]))
+
+
+def test_l_gradient_is_the_activation_side_through_the_quantization_error():
+    """X' (T W)^T = X W^T for every angle and scale, so the two sides' terms
+    through T W cancel: the straight-through gradient equals the activation
+    side's gradient for dX' = dY E, E = W_hat - T W."""
+    x, layer, _ = synthetic.linear_case(seed=2, M=9, d=256, N=32, group=128, K=4, bias=False)
+    q, s, z = oracle.quantize_weights(layer.w, 128, layer.pairs, layer.theta, layer.alpha)
+    _, dth, dal = oracle.layer_loss(x, layer.w, q, s, z, 128, layer.pairs, layer.theta, layer.alpha,
+                                    grad=True)
+    xr16 = oracle.rotate_activations(x, layer.pairs, layer.theta, layer.alpha).astype(np.float16)
+    what = oracle.dequantize(q, s, z, 128)
+    yq = (xr16.astype(np.float64) @ what.T).astype(np.float16).astype(np.float64)
+    dy = 2.0 * (yq - x.astype(np.float64) @ layer.w.astype(np.float64).T)
+    e = what - oracle.transform_weights_f64(layer.w, layer.pairs, layer.theta, layer.alpha)
+    _, dth2, dal2 = oracle.rotation_backward(x, dy @ e, layer.pairs, layer.theta, layer.alpha)
+    assert np.allclose(dth, dth2, rtol=1e-9, atol=1e-9 * np.abs(dth).max())
+    assert np.allclose(dal, dal2, rtol=1e-9, atol=1e-9 * np.abs(dal).max())
