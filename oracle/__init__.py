@@ -355,9 +355,9 @@ def layer_loss(x, w, qweight, scales, zeros, group, pairs, theta, alpha, grad=Fa
     Frobenius norm L = sum (Y_q - Y)^2 with D(X) = X W^T the layer in its
     original fp16 weights and Q(D)(X') = X' W_hat^T the 4-bit layer on the
     transformed activations (W_hat the dequantized Q(T W)). With round16 the
-    intermediate results are rounded to fp16 where the product path stores
-    them (X' and Y_q) for the loss; the gradients treat those roundings, like
-    the quantizer, as the identity.
+    loss rounds to fp16 where the product path does (X', each dequantized
+    weight as the W4 linear multiplies it, and Y_q); the gradients treat those
+    roundings, like the quantizer, as the identity.
 
     Gradients (grad=True) pass through the quantizer unchanged (the
     straight-through reading of training through Q): dL/dY_q = 2 (Y_q - Y),
@@ -368,7 +368,8 @@ def layer_loss(x, w, qweight, scales, zeros, group, pairs, theta, alpha, grad=Fa
     xr_exact = rotate_activations(x, pairs, theta, alpha)
     xr = xr_exact.astype(np.float16).astype(np.float64) if round16 else xr_exact
     what = dequantize(qweight, scales, zeros, group)
-    yq = xr @ what.T
+    # the layer multiplies the fp16 rounding of each dequantized weight
+    yq = xr @ (what.astype(np.float16).astype(np.float64) if round16 else what).T
     if round16:
         yq = yq.astype(np.float16).astype(np.float64)
     y = np.asarray(x).astype(np.float64) @ np.asarray(w).astype(np.float64).T

@@ -581,7 +581,8 @@ def test_l_gradient_is_the_activation_side_through_the_quantization_error():
                                     grad=True)
     xr16 = oracle.rotate_activations(x, layer.pairs, layer.theta, layer.alpha).astype(np.float16)
     what = oracle.dequantize(q, s, z, 128)
-    yq = (xr16.astype(np.float64) @ what.T).astype(np.float16).astype(np.float64)
+    w16 = what.astype(np.float16).astype(np.float64)  # as the W4 layer multiplies them
+    yq = (xr16.astype(np.float64) @ w16.T).astype(np.float16).astype(np.float64)
     dy = 2.0 * (yq - x.astype(np.float64) @ layer.w.astype(np.float64).T)
     e = what - oracle.transform_weights_f64(layer.w, layer.pairs, layer.theta, layer.alpha)
     _, dth2, dal2 = oracle.rotation_backward(x, dy @ e, layer.pairs, layer.theta, layer.alpha)
