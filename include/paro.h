@@ -260,6 +260,49 @@ int paro_rotation_backward(const paro_rotation* r, int32_t side, const uint16_t*
                            const float* gy, float* gx, float* dtheta, float* dalpha, int64_t M,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of device workspace paro_layer_loss needs (0 for M <= 0, or d not the plan's). */
+size_t paro_layer_loss_workspace_size(const paro_rotation* r, int64_t M, int64_t N, int64_t d,
+                                      int32_t with_gradients);
+
+/*
+ * Layer-wise output loss of the quantized, transformed layer (paper notes,
+ * "损失函数 / 训练策略": L = ||Q(D)(X') - D(X)||, minimised per layer to learn
+ * the angles and scales), as the squared Frobenius norm
+ *   L = sum_{m,n} (Y_q[m][n] - Y[m][n])^2,
+ *   Y_q = paro_w4_linear's output (fp16) on X' = paro_rotate(x) with the
+ *         4-bit weights (qweight, scales, zeros: Q(T W) from
+ *         paro_quantize_weights with this plan), i.e. fp32 sums of X' times
+ *         the fp16 rounding of each dequantized weight,
+ *   Y   = x w^T with w the original fp16 weights [N][d] (fp32 accumulation).
+ * With dtheta and/or dalpha non-NULL also the gradients, passing through the
+ * quantizer and the fp16 roundings unchanged (straight-through):
+ * dY = 2 (Y_q - Y), dL/dX' = dY W_hat, dL/d(T W) = dY^T X', then both
+ * transforms' gradients as paro_rotation_backward computes them (activation
+ * side with x, weight side with w), summed. Since X' (T W)^T = X W^T for all
+ * angles and scales, that sum equals the activation side's gradient for
+ * dL/dX' = dY E, E = W_hat - T W (T W in the quantizer's fp32), which is how
+ * it is computed: the two sides' other terms cancel and are each tens of
+ * times larger than the result.
+ *
+ *   x        device fp16 [M][d], w device fp16 [N][d] (16-byte aligned);
+ *   qweight, scales, zeros: as for paro_w4_linear, with the plan's group;
+ *   loss     device fp32 [1] (the sum is taken in a fixed order, fp64 at the end);
+ *   dtheta   device fp32 [K][d/2] or NULL; dalpha device fp32 [d] or NULL;
+ *   N % 16 == 0, 0 <= M, N < 2^30; M == 0 writes zeros.
+ *   workspace: at least paro_layer_loss_workspace_size(r, M, N, d, dtheta ||
+ *            dalpha) bytes, 256-byte aligned, zero-filled once after
+ *            allocation (it holds paro_w4_linear's arrival counters for
+ *            M <= 16, which every call leaves zero).
+ * The three dense products go to rocBLAS (a handle per device, created on
+ * first use); everything else runs in this library's kernels.
+ * Errors: PARO_ERR_NULL, PARO_ERR_SHAPE, PARO_ERR_ALIGN, PARO_ERR_WORKSPACE,
+ * PARO_ERR_HIP, and those of paro_w4_linear.
+ */
+int paro_layer_loss(const paro_rotation* r, const uint16_t* x, const uint16_t* w,
+                    const uint8_t* qweight, const uint16_t* scales, const uint8_t* zeros, int64_t M,
+                    int64_t N, int64_t d, int32_t group, float* loss, float* dtheta, float* dalpha,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /*
  * Host-only view of the per-segment rotation schedule that
  * paro_rotation_create uploads (for testing the plan logic without a GPU).

@@ -8,7 +8,8 @@ fallback: if the library is missing or no GPU is visible the calls raise.
 Names follow the C ABI: ``paro_rotation_create`` / ``Rotation``,
 ``paro_rotate``, ``paro_quantize_weights``, ``paro_w4_linear``,
 ``paro_w4_linear_workspace_size``, ``paro_rotation_backward``,
-``paro_rotation_backward_workspace_size``.
+``paro_rotation_backward_workspace_size``, ``paro_layer_loss``,
+``paro_layer_loss_workspace_size``.
 """
 from __future__ import annotations
 
@@ -70,6 +71,11 @@ def load_library() -> ctypes.CDLL:
     lib.paro_rotation_backward_workspace_size.argtypes = [vp, c_i64]
     lib.paro_rotation_backward.restype = ctypes.c_int
     lib.paro_rotation_backward.argtypes = [vp, c_i32, vp, vp, vp, vp, vp, c_i64, vp, c_size, vp]
+    lib.paro_layer_loss_workspace_size.restype = c_size
+    lib.paro_layer_loss_workspace_size.argtypes = [vp, c_i64, c_i64, c_i64, c_i32]
+    lib.paro_layer_loss.restype = ctypes.c_int
+    lib.paro_layer_loss.argtypes = [vp, vp, vp, vp, vp, vp, c_i64, c_i64, c_i64, c_i32, vp, vp, vp,
+                                    vp, c_size, vp]
     lib.paro_rotation_plan_host.restype = ctypes.c_int
     lib.paro_rotation_plan_host.argtypes = [c_i64, c_i32, c_i32, vp, vp, vp, vp, c_size,
                                             ctypes.POINTER(c_size), ctypes.POINTER(c_i32)]
@@ -232,6 +238,32 @@ def paro_rotation_backward(r: Rotation, x, gy, side: str = "activation", gx=None
         _dptr(dtheta, "dtheta", torch.float32) if info_K else None,
         _dptr(dalpha, "dalpha", torch.float32), M, ws_ptr, ws_bytes, _stream(stream)))
     return gx, dtheta, dalpha
+
+
+def paro_layer_loss(r: Rotation, x, w, qweight, scales, zeros, gradients: bool = True,
+                    workspace=None, stream=None):
+    """Layer-wise output loss sum (Y_q - X W^T)^2 (fp32 device scalar) and, with
+    ``gradients``, its straight-through dtheta [K][d/2] and dalpha [d]."""
+    import torch
+    M, d = x.shape
+    N = w.shape[0]
+    dev_ = x.device
+    loss = torch.empty((1,), dtype=torch.float32, device=dev_)
+    dth = torch.empty((r.K, d // 2), dtype=torch.float32, device=dev_) if gradients else None
+    dal = torch.empty((d,), dtype=torch.float32, device=dev_) if gradients else None
+    if workspace is None:
+        need = int(load_library().paro_layer_loss_workspace_size(r.handle, M, N, d, int(gradients)))
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev_) if need else None
+    ws_ptr = _dptr(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load_library().paro_layer_loss(
+        r.handle, _dptr(x, "x", torch.float16), _dptr(w, "w", torch.float16),
+        _dptr(qweight, "qweight", torch.uint8), _dptr(scales, "scales", torch.float16),
+        _dptr(zeros, "zeros", torch.uint8), M, N, d, r.group, _dptr(loss, "loss", torch.float32),
+        _dptr(dth, "dtheta", torch.float32) if (gradients and r.K) else None,
+        _dptr(dal, "dalpha", torch.float32) if gradients else None, ws_ptr, ws_bytes,
+        _stream(stream)))
+    return loss, dth, dal
 
 
 def paro_rotation_plan_host(pairs, theta, alpha, group: int) -> Tuple[np.ndarray, dict]:

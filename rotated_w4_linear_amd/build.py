@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libparo.so")
 
 SOURCES = ["api.cpp", "plan.cpp", "rotate.hip", "quantize.hip", "w4_linear.hip", "decode.hip",
-           "backward.hip"]
+           "backward.hip", "layer_loss.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -23,6 +23,8 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     "-Wl,-z,defs",                                # no undefined symbols (e.g. a kernel stub) in the library
+    "-L/opt/rocm/lib", "-lrocblas",               # the layer loss's dense products
+    "-Wl,-rpath,/opt/rocm/lib",
 ]
 
 

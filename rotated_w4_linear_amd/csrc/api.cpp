@@ -347,4 +347,53 @@ int paro_rotation_backward(const paro_rotation* r, int32_t side, const uint16_t*
   return PARO_OK;
 }
 
+size_t paro_layer_loss_workspace_size(const paro_rotation* r, int64_t M, int64_t N, int64_t d,
+                                      int32_t with_gradients) {
+  if (!r || M <= 0 || N <= 0 || d != r->d) return 0;
+  return paro::layer_loss_scratch_bytes(r, M, N, d, with_gradients != 0);
+}
+
+int paro_layer_loss(const paro_rotation* r, const uint16_t* x, const uint16_t* w,
+                    const uint8_t* qweight, const uint16_t* scales, const uint8_t* zeros, int64_t M,
+                    int64_t N, int64_t d, int32_t group, float* loss, float* dtheta, float* dalpha,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  using namespace paro;
+  if (!r || !loss) {
+    set_error("paro_layer_loss: NULL rotation or loss");
+    return PARO_ERR_NULL;
+  }
+  if (M < 0 || N <= 0 || d != r->d || group != r->group || N % 16 || M >= (int64_t(1) << 30) ||
+      N >= (int64_t(1) << 30)) {
+    set_error("paro_layer_loss: sizes (d and group of the plan, N % 16 == 0, 0 <= M, N < 2^30)");
+    return PARO_ERR_SHAPE;
+  }
+  const bool grad = dtheta || dalpha;
+  if (M == 0) {  // no rows: zero loss and gradients
+    hipError_t e = launch_fill_zero(loss, 1, stream);
+    if (e == hipSuccess && dtheta) e = launch_fill_zero(dtheta, (int64_t)r->K * (d / 2), stream);
+    if (e == hipSuccess && dalpha) e = launch_fill_zero(dalpha, d, stream);
+    return e == hipSuccess ? PARO_OK : hip_fail(e, "paro_layer_loss");
+  }
+  if (!x || !w || !qweight || !scales || !zeros) {
+    set_error("paro_layer_loss: NULL tensor");
+    return PARO_ERR_NULL;
+  }
+  if (!aligned16(x) || !aligned16(w) || !aligned16(qweight) || ((uintptr_t)loss & 3) ||
+      ((uintptr_t)dtheta & 3) || ((uintptr_t)dalpha & 3)) {
+    set_error("paro_layer_loss: x, w, qweight must be 16-byte aligned");
+    return PARO_ERR_ALIGN;
+  }
+  const size_t need = layer_loss_scratch_bytes(r, M, N, d, grad);
+  if (!workspace || workspace_bytes < need) {
+    set_error("paro_layer_loss: workspace missing or smaller than paro_layer_loss_workspace_size");
+    return PARO_ERR_WORKSPACE;
+  }
+  if ((uintptr_t)workspace & 255) {
+    set_error("paro_layer_loss: workspace must be 256-byte aligned");
+    return PARO_ERR_ALIGN;
+  }
+  return run_layer_loss(r, x, w, qweight, scales, zeros, M, N, d, group, loss, dtheta, dalpha,
+                        workspace, stream);
+}
+
 }  // extern "C"

@@ -1,0 +1,227 @@
+// Layer-wise output loss of the quantized, transformed layer and its
+// straight-through gradients with respect to the angles and channel scales:
+// the objective the paper notes minimise to learn the transform ("损失函数 /
+// 训练策略": L = ||Q(D)(X') - D(X)||, per layer, with the angles and scales
+// optimised first). Here L is the squared Frobenius norm
+//   L = sum_{m,n} (Y_q[m][n] - Y[m][n])^2,
+//   Y_q = the 4-bit layer on X' = X T^-1 (paro_rotate, then the W4 linear;
+//         fp16 as the product stores them),
+//   Y   = X W^T, the layer in its original fp16 weights.
+// Gradients pass through the quantizer unchanged (training through Q reads
+// as straight-through): dY = 2 (Y_q - Y), dX' = dY W_hat, dW_hat = dY^T X'
+// taken as the gradient of T W, then both transforms' own gradients, summed.
+// Because X' (T W)^T = X W^T for every angle and scale, the two sides'
+// contributions through T W itself cancel exactly, and the sum equals the
+// activation side's gradient for dX' = dY E with E = W_hat - T W the
+// quantization error. That form is what is computed: the two cancelling
+// terms are each some 30-50 times larger than their sum, so adding them in
+// fp32 would lose that much accuracy.
+//
+// The two dense products (X W^T and dY E) are plain GEMMs and go to rocBLAS;
+// the rest runs in this library's kernels: the transform, the W4 linear, the
+// fp32 transform of W (the quantizer's own pass), the exact dequantization,
+// the loss with its deterministic reduction, and the activation side's
+// gradients.
+#include <rocblas/rocblas.h>
+
+#include <mutex>
+
+#include "paro_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace paro {
+namespace {
+
+constexpr int kLossBlocks = 1024;  // partial sums of the loss (fixed: the order never changes)
+
+// E[n][k] = (q - z) s - u[n][k] in fp32 ((q - z) s is exact: |q - z| <= 15
+// and s is fp16; one rounding for the difference); out may be u
+__global__ __launch_bounds__(256) void quant_error_kernel(const uint8_t* __restrict__ qw,
+                                                          const uint16_t* __restrict__ sc,
+                                                          const uint8_t* __restrict__ zr,
+                                                          const float* u, float* out, int64_t N,
+                                                          int64_t d, int gshift) {
+  const int64_t total = N * (d / 2);
+  const int64_t groups = d >> gshift;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t n = i / (d / 2), b = i % (d / 2);
+    const int64_t k = 2 * b;
+    const uint8_t byte = qw[i];
+    const int64_t g = n * groups + (k >> gshift);
+    const float s = (float)__builtin_bit_cast(_Float16, sc[g]);
+    const float z = (float)zr[g];
+    out[n * d + k] = ((float)(byte & 15) - z) * s - u[n * d + k];
+    out[n * d + k + 1] = ((float)(byte >> 4) - z) * s - u[n * d + k + 1];
+  }
+}
+
+// Block b sums (y_q - y)^2 over elements b, b + B, b + 2B, ... (grid-stride
+// by thread, then a fixed tree over the block) into part[b]; with dy != NULL
+// it also writes dy = 2 (y_q - y) (dy may be y).
+__global__ __launch_bounds__(256) void loss_partial_kernel(const uint16_t* __restrict__ yq,
+                                                           const float* y, float* dy, int64_t n,
+                                                           float* __restrict__ part) {
+  __shared__ float red[256];
+  float acc = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const float diff = (float)__builtin_bit_cast(_Float16, yq[i]) - y[i];
+    acc += diff * diff;
+    if (dy) dy[i] = 2.0f * diff;
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+}
+
+// loss = sum of the partial sums in block order (fp64), one thread
+__global__ void loss_final_kernel(const float* __restrict__ part, int nb, float* __restrict__ loss) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    double s = 0.0;
+    for (int b = 0; b < nb; ++b) s += (double)part[b];
+    loss[0] = (float)s;
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ a, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    a[i] = 0.f;
+}
+
+unsigned grid_for(int64_t n) {
+  const int64_t b = (n + 255) / 256;
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(b, 16384));
+}
+
+size_t a256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+int fail(hipError_t e, const char* what) {
+  set_error(std::string(what) + ": " + hipGetErrorString(e));
+  return PARO_ERR_HIP;
+}
+
+// rocBLAS handle per device, created on first use and kept for the process
+rocblas_handle blas_handle(int device) {
+  static std::mutex mu;
+  static rocblas_handle handles[64] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (device < 0 || device >= 64) return nullptr;
+  if (!handles[device] && rocblas_create_handle(&handles[device]) != rocblas_status_success) {
+    handles[device] = nullptr;
+  }
+  return handles[device];
+}
+
+struct LossLayout {
+  size_t xr, yq, y, w4, part, e, dxr, qw, sc, zr, flag, bw, dth, dal, total;
+};
+
+LossLayout loss_layout(const paro_rotation* r, int64_t M, int64_t N, int64_t d, bool grad) {
+  LossLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += a256(bytes);
+    return o;
+  };
+  L.xr = take((size_t)M * d * 2);
+  L.yq = take((size_t)M * N * 2);
+  L.y = take((size_t)M * N * 4);
+  L.w4 = take(paro_w4_linear_workspace_size(nullptr, M, N, d));
+  L.part = take((size_t)kLossBlocks * 4);
+  if (grad) {
+    L.e = take((size_t)N * d * 4);
+    L.dxr = take((size_t)M * d * 4);
+    L.qw = take((size_t)N * (d / 2));
+    L.sc = take((size_t)N * (d / r->group) * 2);
+    L.zr = take((size_t)N * (d / r->group));
+    L.flag = take(4);
+    L.bw = take(rotate_backward_scratch_bytes(r, M));
+    L.dth = take((size_t)r->K * (size_t)(d / 2) * 4);
+    L.dal = take((size_t)d * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+size_t layer_loss_scratch_bytes(const paro_rotation* r, int64_t M, int64_t N, int64_t d, bool grad) {
+  return loss_layout(r, M, N, d, grad).total;
+}
+
+int run_layer_loss(const paro_rotation* r, const uint16_t* x, const uint16_t* w, const uint8_t* qw,
+                   const uint16_t* sc, const uint8_t* zr, int64_t M, int64_t N, int64_t d, int group,
+                   float* loss, float* dtheta, float* dalpha, void* ws, hipStream_t stream) {
+  const bool grad = dtheta != nullptr || dalpha != nullptr;
+  const LossLayout L = loss_layout(r, M, N, d, grad);
+  char* base = (char*)ws;
+  uint16_t* xr = (uint16_t*)(base + L.xr);
+  uint16_t* yq = (uint16_t*)(base + L.yq);
+  float* y = (float*)(base + L.y);
+  float* part = (float*)(base + L.part);
+  hipError_t e = launch_rotate(r, x, xr, M, stream);
+  if (e != hipSuccess) return fail(e, "paro_layer_loss: transform");
+  int st = paro_w4_linear(nullptr, xr, qw, sc, zr, nullptr, yq, M, N, d, group, base + L.w4,
+                          paro_w4_linear_workspace_size(nullptr, M, N, d), stream);
+  if (st != PARO_OK) return st;
+  int dev = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return fail(e, "paro_layer_loss: hipGetDevice");
+  rocblas_handle h = blas_handle(dev);
+  if (!h || rocblas_set_stream(h, stream) != rocblas_status_success) {
+    set_error("paro_layer_loss: rocBLAS handle");
+    return PARO_ERR_HIP;
+  }
+  const float one = 1.0f, zero = 0.0f;
+  // Y (column-major N x M, ld N) = W (stored [N][d]: column-major d x N, transposed) * X^T
+  if (rocblas_gemm_ex(h, rocblas_operation_transpose, rocblas_operation_none, (rocblas_int)N,
+                      (rocblas_int)M, (rocblas_int)d, &one, w, rocblas_datatype_f16_r, (rocblas_int)d, x,
+                      rocblas_datatype_f16_r, (rocblas_int)d, &zero, y, rocblas_datatype_f32_r,
+                      (rocblas_int)N, y, rocblas_datatype_f32_r, (rocblas_int)N, rocblas_datatype_f32_r,
+                      rocblas_gemm_algo_standard, 0, 0) != rocblas_status_success) {
+    set_error("paro_layer_loss: rocBLAS X W^T");
+    return PARO_ERR_HIP;
+  }
+  hipLaunchKernelGGL(loss_partial_kernel, dim3(kLossBlocks), dim3(256), 0, stream, yq, y,
+                     grad ? y : nullptr, M * N, part);
+  hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(64), 0, stream, part, kLossBlocks, loss);
+  if ((e = hipGetLastError()) != hipSuccess) return fail(e, "paro_layer_loss: loss");
+  if (!grad) return PARO_OK;
+
+  float* dy = y;
+  float* err = (float*)(base + L.e);
+  float* dxr = (float*)(base + L.dxr);
+  const int gshift = group == 64 ? 6 : group == 128 ? 7 : 8;
+  // T W in fp32 (the quantizer's pass; its codes go to scratch), then E = W_hat - T W
+  if ((e = launch_quantize(r, w, N, d, group, (uint8_t*)(base + L.qw), (uint16_t*)(base + L.sc),
+                           (uint8_t*)(base + L.zr), (int*)(base + L.flag), stream, err)) != hipSuccess)
+    return fail(e, "paro_layer_loss: weight transform");
+  hipLaunchKernelGGL(quant_error_kernel, dim3(grid_for(N * d / 2)), dim3(256), 0, stream, qw, sc, zr,
+                     err, err, N, d, gshift);
+  if ((e = hipGetLastError()) != hipSuccess) return fail(e, "paro_layer_loss: quantization error");
+  // dX' (column-major d x M, ld d) = E (column-major d x N) * dY^T (column-major N x M)
+  if (rocblas_sgemm(h, rocblas_operation_none, rocblas_operation_none, (rocblas_int)d, (rocblas_int)M,
+                    (rocblas_int)N, &one, err, (rocblas_int)d, dy, (rocblas_int)N, &zero, dxr,
+                    (rocblas_int)d) != rocblas_status_success) {
+    set_error("paro_layer_loss: rocBLAS dY E");
+    return PARO_ERR_HIP;
+  }
+  float* dth = dtheta ? dtheta : (float*)(base + L.dth);  // a NULL output still needs a place
+  float* dal = dalpha ? dalpha : (float*)(base + L.dal);
+  if ((e = launch_rotate_backward(r, 0, x, dxr, nullptr, dth, dal, M, base + L.bw, stream)) !=
+      hipSuccess)
+    return fail(e, "paro_layer_loss: transform gradients");
+  return PARO_OK;
+}
+
+hipError_t launch_fill_zero(float* a, int64_t n, hipStream_t stream) {
+  if (n <= 0 || !a) return hipSuccess;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n)), dim3(256), 0, stream, a, n);
+  return hipGetLastError();
+}
+
+}  // namespace paro

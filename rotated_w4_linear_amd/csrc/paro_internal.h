@@ -82,6 +82,14 @@ hipError_t launch_rotate_backward(const paro_rotation* r, int weight_side, const
                                   const float* gy, float* gx, float* dtheta, float* dalpha,
                                   int64_t M, void* part, hipStream_t stream);
 
+// Layer-wise output loss and its straight-through angle/scale gradients
+// (layer_loss.hip): scratch bytes, the whole computation, and a zero fill.
+size_t layer_loss_scratch_bytes(const paro_rotation* r, int64_t M, int64_t N, int64_t d, bool grad);
+int run_layer_loss(const paro_rotation* r, const uint16_t* x, const uint16_t* w, const uint8_t* qw,
+                   const uint16_t* sc, const uint8_t* zr, int64_t M, int64_t N, int64_t d, int group,
+                   float* loss, float* dtheta, float* dalpha, void* ws, hipStream_t stream);
+hipError_t launch_fill_zero(float* a, int64_t n, hipStream_t stream);
+
 }  // namespace paro
 
 struct paro_rotation {
@@ -102,9 +110,10 @@ namespace paro {
 // Kernel launchers (defined in the .hip files). Return hipError_t of the launch.
 hipError_t launch_rotate(const paro_rotation* r, const uint16_t* x, uint16_t* y, int64_t M,
                          hipStream_t stream);
+// uout (may be NULL): also writes the transformed rows T W in fp32 [N][d]
 hipError_t launch_quantize(const paro_rotation* r, const uint16_t* w, int64_t N, int64_t d,
                            int group, uint8_t* qweight, uint16_t* scales, uint8_t* zeros,
-                           int* d_flag, hipStream_t stream);
+                           int* d_flag, hipStream_t stream, float* uout = nullptr);
 // Large-batch linear (M > 16) on already transformed activations.
 hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
                           const uint8_t* zeros, const uint16_t* bias, uint16_t* y, int64_t M,

@@ -28,7 +28,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     const uint16_t* __restrict__ w, int64_t N, int64_t d, int G, int K,
     const uint32_t* __restrict__ wt_pairs, const float* __restrict__ wt_c,
     const float* __restrict__ wt_s, const float* __restrict__ alpha, uint8_t* __restrict__ qweight,
-    uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros, int* __restrict__ flag) {
+    uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros, int* __restrict__ flag,
+    float* __restrict__ uout) {
   __shared__ float buf[4][256];
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -60,6 +61,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    if (uout) {  // the transformed row itself (fp32), for the layer loss's gradients
+      for (int k = lane; k < G; k += 64) uout[n * d + g * G + k] = u[k];
     }
     float mn = 0.0f, mx = 0.0f;
     int bad = 0;
@@ -107,7 +111,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(
 
 hipError_t launch_quantize(const paro_rotation* r, const uint16_t* w, int64_t N, int64_t d,
                            int group, uint8_t* qweight, uint16_t* scales, uint8_t* zeros,
-                           int* d_flag, hipStream_t stream) {
+                           int* d_flag, hipStream_t stream, float* uout) {
   const int64_t total = N * (d / group);
   if (total == 0) return hipSuccess;
   int64_t blocks = (total + 3) / 4;
@@ -115,7 +119,7 @@ hipError_t launch_quantize(const paro_rotation* r, const uint16_t* w, int64_t N,
   hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w, N, d, group,
                      r ? r->K : 0, r ? r->d_wt_pairs : nullptr, r ? r->d_wt_c : nullptr,
                      r ? r->d_wt_s : nullptr, r ? r->d_alpha : nullptr, qweight, scales, zeros,
-                     d_flag);
+                     d_flag, uout);
   return hipGetLastError();
 }
 

@@ -99,6 +99,10 @@ def test_hot_calls_validate_before_any_launch(paro):
     d4 = ctypes.c_void_p(16 * 1024)
     assert lib.paro_rotation_backward(None, 0, d4, d4, d4, d4, d4, 4, None, 0, None) == -1
     assert lib.paro_rotation_backward_workspace_size(None, 4) == 0
+    # layer loss: the handle and the loss pointer come first
+    assert lib.paro_layer_loss(None, d4, d4, d4, d4, d4, 4, 16, 256, 128, d4, None, None, None, 0,
+                               None) == -1
+    assert lib.paro_layer_loss_workspace_size(None, 4, 16, 256, 1) == 0
     assert lib.paro_rotate(None, None, None, 4, None) == -1
     assert lib.paro_rotate(None, None, None, 0, None) == -1  # handle still required
     dummy = ctypes.c_void_p(16 * 1024)
