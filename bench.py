@@ -22,7 +22,8 @@ Other workloads (``--workload``): prefill_down (2048 x 14336 -> 4096),
 decode (M = 1, 4, 16 tokens, 4096 -> 4096; weight streaming), sweep (the 27
 rotation-only points, 8192 x d), sparse (the transform with sparse pairings, in
 which only a fraction of the pairs rotate), backward (the gradients of the
-transform with respect to its input, angles and scales), chain (the seven linears of a Llama-3-8B
+transform with respect to its input, angles and scales), calib (the layer-wise
+loss with its angle and scale gradients: one transform-learning step), chain (the seven linears of a Llama-3-8B
 decoder layer as rotated W4, plain W4 and dense fp16 chains), copy (a plain
 device copy, for calibrating HBM byte counters).
 
@@ -603,6 +604,53 @@ def bench_backward(args, paro, torch):
     }
 
 
+def bench_calib(args, paro, torch):
+    """The layer-wise loss and its straight-through angle/scale gradients
+    (paro_layer_loss) for a Llama-3-8B q_proj-shaped layer (4096 -> 4096,
+    K = 8, G = 128) on a batch of 2048 calibration tokens: one step of the
+    transform-learning loop, without the optimizer update."""
+    import synthetic
+    T = Timer(torch)
+    M, d, N = 2048, 4096, 4096
+    x, layer, _ = synthetic.linear_case(seed=21, M=M, d=d, N=N, bias=False)
+    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, 128)
+    xd = torch.from_numpy(x).cuda()
+    wd = torch.from_numpy(layer.w).cuda()
+    qw, sc, zr = paro.paro_quantize_weights(r, wd, 128)
+    lib = paro.load_library()
+    out = {}
+    for grads in (True, False):
+        need = int(lib.paro_layer_loss_workspace_size(r.handle, M, N, d, int(grads)))
+        ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+
+        def step(i, grads=grads, ws=ws):
+            return paro.paro_layer_loss(r, xd, wd, qw, sc, zr, gradients=grads, workspace=ws)
+        settle(torch, [step], args.warmup + 2, seconds=0.3)
+        n = max(args.steps, 10)
+        s = T.event()
+        for i in range(n):
+            res = step(i)
+        e = T.event()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / n
+        out[grads] = (ms, float(res[0].item()))
+        log(f"[calib] gradients={grads}: {ms:.3f} ms per step, loss {out[grads][1]:.6g}")
+    ms, loss = out[True]
+    flops = 2.0 * M * N * d * 2 + 2.0 * M * N * d  # X W^T, dY E (fp32), the W4 layer
+    return {
+        "metric": "transform-learning step: layer loss + angle/scale gradients (ms)", "value": round(ms, 4),
+        "unit": "ms", "n_gpus": 1, "steps": max(args.steps, 10), "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16/f32", "data": "synthetic",
+        "config": {"workload": "layer_loss_q_proj_2048x4096to4096_K8", "group": 128, "K": 8},
+        "loss_only_ms": round(out[False][0], 4), "loss": loss,
+        "calibration_tokens_per_s": round(M / (ms * 1e-3), 1),
+        "roofline": None,
+        "note": "three dense products per step (X W^T fp16, dY E fp32, the W4 layer); "
+                "per-kernel durations in the committed rocprofv3 summary",
+    }
+
+
 def bench_chain(args, paro, torch):
     """The seven linears of one Llama-3-8B decoder layer in sequence (q, k, v, o,
     gate, up, down; attention and activations left out), as rotated W4G128,
@@ -724,7 +772,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill_mlp",
                     choices=["prefill_mlp", "prefill_down", "decode", "sweep", "sparse", "backward",
-                             "tiny", "copy", "chain"])
+                             "calib", "tiny", "copy", "chain"])
     ap.add_argument("--ring", type=int, default=0, help="distinct input copies cycled (0 = auto)")
     ap.add_argument("--decode-m", default="1,4,16", help="token counts of the decode workload")
     ap.add_argument("--chain-m", default="1,16,2048", help="token counts of the layer-chain workload")
@@ -763,6 +811,8 @@ def main():
         out = bench_sparse(args, paro, torch)
     elif args.workload == "backward":
         out = bench_backward(args, paro, torch)
+    elif args.workload == "calib":
+        out = bench_calib(args, paro, torch)
     else:
         out = bench_copy(args, torch)
     print(json.dumps(out), flush=True)

@@ -78,13 +78,20 @@ __global__ __launch_bounds__(256) void loss_partial_kernel(const uint16_t* __res
   if (threadIdx.x == 0) part[blockIdx.x] = red[0];
 }
 
-// loss = sum of the partial sums in block order (fp64), one thread
-__global__ void loss_final_kernel(const float* __restrict__ part, int nb, float* __restrict__ loss) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) {
-    double s = 0.0;
-    for (int b = 0; b < nb; ++b) s += (double)part[b];
-    loss[0] = (float)s;
+// loss = sum of the partial sums (fp64): thread t adds partials t, t + 256,
+// ... in order, then a fixed tree over the block
+__global__ __launch_bounds__(256) void loss_final_kernel(const float* __restrict__ part, int nb,
+                                                         float* __restrict__ loss) {
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int b = threadIdx.x; b < nb; b += 256) s += (double)part[b];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
   }
+  if (threadIdx.x == 0) loss[0] = (float)red[0];
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ a, int64_t n) {
@@ -188,7 +195,7 @@ int run_layer_loss(const paro_rotation* r, const uint16_t* x, const uint16_t* w,
   }
   hipLaunchKernelGGL(loss_partial_kernel, dim3(kLossBlocks), dim3(256), 0, stream, yq, y,
                      grad ? y : nullptr, M * N, part);
-  hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(64), 0, stream, part, kLossBlocks, loss);
+  hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(256), 0, stream, part, kLossBlocks, loss);
   if ((e = hipGetLastError()) != hipSuccess) return fail(e, "paro_layer_loss: loss");
   if (!grad) return PARO_OK;
 
