@@ -17,7 +17,8 @@
 // terms are each some 30-50 times larger than their sum, so adding them in
 // fp32 would lose that much accuracy.
 //
-// The two dense products (X W^T and dY E) are plain GEMMs and go to rocBLAS;
+// The two dense products (X W^T, and dY E as three bf16 products of split
+// operands) are plain GEMMs and go to rocBLAS;
 // the rest runs in this library's kernels: the transform, the W4 linear, the
 // fp32 transform of W (the quantizer's own pass), the exact dequantization,
 // the loss with its deterministic reduction, and the activation side's
@@ -94,6 +95,24 @@ __global__ __launch_bounds__(256) void loss_final_kernel(const float* __restrict
   if (threadIdx.x == 0) loss[0] = (float)red[0];
 }
 
+// x = hi + lo + (a remainder of about 2^-16 |x|): hi = bf16(x), lo = bf16(x - hi),
+// both rounded to nearest even
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__global__ __launch_bounds__(256) void split_bf16_kernel(const float* __restrict__ a,
+                                                         uint16_t* __restrict__ hi,
+                                                         uint16_t* __restrict__ lo, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const float v = a[i];
+    const uint16_t h = bf16_rne(v);
+    hi[i] = h;
+    lo[i] = bf16_rne(v - __builtin_bit_cast(float, (uint32_t)h << 16));
+  }
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ a, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
     a[i] = 0.f;
@@ -124,7 +143,7 @@ rocblas_handle blas_handle(int device) {
 }
 
 struct LossLayout {
-  size_t xr, yq, y, w4, part, e, dxr, qw, sc, zr, flag, bw, dth, dal, total;
+  size_t xr, yq, y, w4, part, e, dxr, qw, sc, zr, flag, bw, dth, dal, yh, yl, eh, el, total;
 };
 
 LossLayout loss_layout(const paro_rotation* r, int64_t M, int64_t N, int64_t d, bool grad) {
@@ -150,6 +169,10 @@ LossLayout loss_layout(const paro_rotation* r, int64_t M, int64_t N, int64_t d, 
     L.bw = take(rotate_backward_scratch_bytes(r, M));
     L.dth = take((size_t)r->K * (size_t)(d / 2) * 4);
     L.dal = take((size_t)d * 4);
+    L.yh = take((size_t)M * N * 2);
+    L.yl = take((size_t)M * N * 2);
+    L.eh = take((size_t)N * d * 2);
+    L.el = take((size_t)N * d * 2);
   }
   L.total = off;
   return L;
@@ -210,12 +233,29 @@ int run_layer_loss(const paro_rotation* r, const uint16_t* x, const uint16_t* w,
   hipLaunchKernelGGL(quant_error_kernel, dim3(grid_for(N * d / 2)), dim3(256), 0, stream, qw, sc, zr,
                      err, err, N, d, gshift);
   if ((e = hipGetLastError()) != hipSuccess) return fail(e, "paro_layer_loss: quantization error");
-  // dX' (column-major d x M, ld d) = E (column-major d x N) * dY^T (column-major N x M)
-  if (rocblas_sgemm(h, rocblas_operation_none, rocblas_operation_none, (rocblas_int)d, (rocblas_int)M,
-                    (rocblas_int)N, &one, err, (rocblas_int)d, dy, (rocblas_int)N, &zero, dxr,
-                    (rocblas_int)d) != rocblas_status_success) {
-    set_error("paro_layer_loss: rocBLAS dY E");
-    return PARO_ERR_HIP;
+  // dX' (column-major d x M, ld d) = E (column-major d x N) * dY^T (column-major N x M),
+  // as three bf16 products with fp32 accumulation: E_hi dY_hi + E_hi dY_lo +
+  // E_lo dY_hi carries about 16 bits of each operand (relative error ~2^-16),
+  // at a fraction of an fp32 GEMM's time, with fp32's range
+  uint16_t* yh = (uint16_t*)(base + L.yh);
+  uint16_t* yl = (uint16_t*)(base + L.yl);
+  uint16_t* eh = (uint16_t*)(base + L.eh);
+  uint16_t* el = (uint16_t*)(base + L.el);
+  hipLaunchKernelGGL(split_bf16_kernel, dim3(grid_for(M * N)), dim3(256), 0, stream, dy, yh, yl, M * N);
+  hipLaunchKernelGGL(split_bf16_kernel, dim3(grid_for(N * d)), dim3(256), 0, stream, err, eh, el, N * d);
+  if ((e = hipGetLastError()) != hipSuccess) return fail(e, "paro_layer_loss: split");
+  const uint16_t* ea[3] = {eh, eh, el};
+  const uint16_t* yb[3] = {yh, yl, yh};
+  for (int t = 0; t < 3; ++t) {
+    if (rocblas_gemm_ex(h, rocblas_operation_none, rocblas_operation_none, (rocblas_int)d, (rocblas_int)M,
+                        (rocblas_int)N, &one, ea[t], rocblas_datatype_bf16_r, (rocblas_int)d, yb[t],
+                        rocblas_datatype_bf16_r, (rocblas_int)N, t ? &one : &zero, dxr,
+                        rocblas_datatype_f32_r, (rocblas_int)d, dxr, rocblas_datatype_f32_r,
+                        (rocblas_int)d, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0,
+                        0) != rocblas_status_success) {
+      set_error("paro_layer_loss: rocBLAS dY E");
+      return PARO_ERR_HIP;
+    }
   }
   float* dth = dtheta ? dtheta : (float*)(base + L.dth);  // a NULL output still needs a place
   float* dal = dalpha ? dalpha : (float*)(base + L.dal);
