@@ -293,8 +293,10 @@ size_t paro_layer_loss_workspace_size(const paro_rotation* r, int64_t M, int64_t
  *            dalpha) bytes, 256-byte aligned, zero-filled once after
  *            allocation (it holds paro_w4_linear's arrival counters for
  *            M <= 16, which every call leaves zero).
- * The three dense products go to rocBLAS (a handle per device, created on
- * first use); everything else runs in this library's kernels.
+ * The dense products go to rocBLAS, through one handle per device created on
+ * first use and kept for the process; calls on one device from several host
+ * threads at the same time are not supported (rocBLAS handles are not
+ * thread-safe). Everything else runs in this library's kernels.
  * Errors: PARO_ERR_NULL, PARO_ERR_SHAPE, PARO_ERR_ALIGN, PARO_ERR_WORKSPACE,
  * PARO_ERR_HIP, and those of paro_w4_linear.
  */
