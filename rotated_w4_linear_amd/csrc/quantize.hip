@@ -37,14 +37,37 @@ __global__ __launch_bounds__(256) void quantize_kernel(
   const int64_t total = N * groups;
   float* u = buf[wid];
   const int half = G / 2;
-  for (int64_t item = (int64_t)blockIdx.x * 4 + wid; item < total; item += (int64_t)gridDim.x * 4) {
+  // Each lane reads its weights as dwords (two consecutive fp16), and the
+  // next item's are requested before the current one is transformed.
+  const int64_t stride = (int64_t)gridDim.x * 4;
+  uint32_t nxt[2] = {0u, 0u};
+  auto fetch = [&](int64_t item) {
+    if (item >= total) return;
+    const int64_t n = item / groups, g = item - n * groups;
+    const uint32_t* wr = (const uint32_t*)(w + n * d + g * G);
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      if (lane + 64 * r < half) nxt[r] = wr[lane + 64 * r];
+  };
+  fetch((int64_t)blockIdx.x * 4 + wid);
+  for (int64_t item = (int64_t)blockIdx.x * 4 + wid; item < total; item += stride) {
     const int64_t n = item / groups;
     const int64_t g = item - n * groups;
-    const uint16_t* wr = w + n * d + g * G;
-    for (int k = lane; k < G; k += 64) {
-      float v = (float)__builtin_bit_cast(_Float16, wr[k]);
-      if (alpha) v = v * alpha[g * G + k];
-      u[k] = v;
+    const uint32_t cur[2] = {nxt[0], nxt[1]};
+    fetch(item + stride);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int k2 = lane + 64 * r;
+      if (k2 < half) {
+        float v0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(cur[r] & 0xffffu));
+        float v1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(cur[r] >> 16));
+        if (alpha) {
+          v0 = v0 * alpha[g * G + 2 * k2];
+          v1 = v1 * alpha[g * G + 2 * k2 + 1];
+        }
+        u[2 * k2] = v0;
+        u[2 * k2 + 1] = v1;
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
