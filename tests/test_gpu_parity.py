@@ -550,7 +550,8 @@ def grad_case(seed, M, d, G, K, side, keep=1.0):
 @pytest.mark.parametrize("side", ["activation", "weight"])
 @pytest.mark.parametrize("G,K,d,M", [(128, 8, 256, 5), (128, 8, 512, 37), (64, 8, 512, 9),
                                      (256, 8, 512, 21), (128, 1, 128, 3), (128, 0, 256, 4),
-                                     (128, 32, 256, 11), (256, 3, 768, 1), (64, 5, 384, 300)])
+                                     (128, 32, 256, 11), (256, 3, 768, 1), (64, 5, 384, 300),
+                                     (256, 8, 14336, 3), (128, 16, 2048, 70)])
 def test_backward_shapes(paro, side, G, K, d, M):
     log(f"backward {side} G={G} K={K} d={d} M={M}")
     x, g, layer = grad_case(G + K + d + M, M, d, G, K, side)
@@ -650,7 +651,8 @@ def check_layer_loss(paro, M, d, N, G, K, seed, gradients=True, keep=1.0, exact=
 
 
 @pytest.mark.parametrize("M,d,N,G,K", [(37, 256, 64, 128, 8), (5, 512, 96, 128, 8), (300, 512, 128, 64, 4),
-                                       (130, 768, 48, 128, 1), (64, 256, 32, 128, 0), (200, 1024, 256, 128, 8)])
+                                       (130, 768, 48, 128, 1), (64, 256, 32, 128, 0), (200, 1024, 256, 128, 8),
+                                       (40, 512, 64, 256, 8), (12, 512, 48, 64, 8)])
 def test_layer_loss_and_gradients(paro, M, d, N, G, K):
     log(f"layer loss M={M} d={d} N={N} G={G} K={K}")
     check_layer_loss(paro, M, d, N, G, K, seed=M + d + N + G + K)
