@@ -780,7 +780,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the rotated W4G128 layer is built and measured on a "
-              "single MI355X (multi-GPU sharding is described in DESIGN.md, not run).", file=sys.stderr)
+              "single MI355X; sharding across GPUs is not run.", file=sys.stderr)
         sys.exit(2)
 
     import torch

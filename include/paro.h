@@ -60,7 +60,7 @@ typedef enum {
   PARO_ERR_PAIRING = -3,     /* a stage is not a perfect pairing inside every group */
   PARO_ERR_VALUE = -4,       /* alpha <= 0 or non-finite, theta non-finite, non-finite weights */
   PARO_ERR_ALIGN = -5,       /* a tensor pointer is not 16-byte aligned */
-  PARO_ERR_UNSUPPORTED = -6, /* a valid request this build does not implement */
+  PARO_ERR_UNSUPPORTED = -6, /* a valid request the library does not implement */
   PARO_ERR_WORKSPACE = -7,   /* workspace missing or too small */
   PARO_ERR_HIP = -8          /* a HIP runtime call failed */
 } paro_status;
