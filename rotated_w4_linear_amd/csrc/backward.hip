@@ -17,19 +17,19 @@
 //
 // Work split: a wavefront (one per workgroup) owns one segment of 128
 // channels (256 for groups of 256) and one chunk of rows, which it walks in
-// batches of BT rows. Lane l owns the segment's pair slots l * PPL .. + PPL - 1
-// of every stage (the pairs of a stage lie inside the segment, so every
-// exchange stays inside the wavefront) and the natural channels
-// 2 (l + 64 q) + {0, 1}. A batch of four rows sits in LDS channel-major, the
-// rows of channel c in 16-byte slot c, values and gradients in two arrays. The
-// host places the pairs on the lanes so that every 16 consecutive lanes touch
-// channels distinct modulo 16 and every 8 distinct modulo 8, which makes the
-// 16-byte accesses free of bank conflicts. LDS accesses of one wavefront
-// complete in order, so a stage reads what the previous stage wrote without a
-// barrier. Angle sums stay in LDS per
-// wavefront, scale sums in registers; each chunk writes its partial sums to
-// scratch, and a second kernel adds the chunks in chunk order, so the result
-// does not depend on scheduling.
+// batches of BT rows (batch_rows). Lane l owns the segment's pair slots
+// l * PPL .. + PPL - 1 of every stage (the pairs of a stage lie inside the
+// segment, so every exchange stays inside the wavefront) and the natural
+// channels 2 (l + 64 q) + {0, 1}. A batch sits in LDS channel-major in planes
+// of four rows: the four rows of channel c in 16-byte slot c of a plane,
+// values and gradients in two arrays. The host places the pairs on the lanes
+// so that every 16 consecutive lanes touch channels distinct modulo 16 and
+// every 8 distinct modulo 8, which makes the 16-byte accesses free of bank
+// conflicts. LDS accesses of one wavefront complete in order, so a stage
+// reads what the previous stage wrote without a barrier. Angle sums stay in
+// LDS per wavefront, scale sums in registers; each chunk writes its partial
+// sums to scratch, and a second kernel adds the chunks in chunk order, so the
+// result does not depend on scheduling.
 #include <algorithm>
 
 #include "paro_internal.h"
@@ -39,8 +39,11 @@
 namespace paro {
 namespace {
 
-constexpr int BT = 4;             // rows per batch: one 16-byte LDS slot per channel
-constexpr int BSTR = BT;          // floats per channel in LDS
+// Rows per batch (a multiple of 4) for segments of 128 * PPL channels: eight
+// rows for 128-channel segments (measured 7% faster than four at 8192 x 4096,
+// K = 8: the table entries, addresses and angle sums of a stage serve twice
+// the rows), four for 256-channel segments (eight measured no faster there).
+__host__ __device__ constexpr int batch_rows(int ppl) { return ppl == 1 ? 8 : 4; }
 constexpr int64_t kTargetWaves = 4096;
 
 typedef float f4v __attribute__((ext_vector_type(4)));
@@ -52,18 +55,21 @@ __device__ __forceinline__ float h_hi(uint32_t v) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
 }
 
-// BT floats of one channel: BT / 4 16-byte LDS accesses
-__device__ __forceinline__ void lds_get(const float* p, float (&o)[BT]) {
+// BT floats of one channel: BT / 4 16-byte LDS accesses, one per plane of
+// four rows (planes qs floats apart)
+template <int BT>
+__device__ __forceinline__ void lds_get(const float* p, int qs, float (&o)[BT]) {
 #pragma unroll
   for (int k = 0; k < BT / 4; ++k) {
-    const f4v a = *(const f4v*)(p + 4 * k);
+    const f4v a = *(const f4v*)(p + qs * k);
 #pragma unroll
     for (int r = 0; r < 4; ++r) o[4 * k + r] = a[r];
   }
 }
-__device__ __forceinline__ void lds_put(float* p, const float (&o)[BT]) {
+template <int BT>
+__device__ __forceinline__ void lds_put(float* p, int qs, const float (&o)[BT]) {
 #pragma unroll
-  for (int k = 0; k < BT / 4; ++k) *(f4v*)(p + 4 * k) = f4v{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
+  for (int k = 0; k < BT / 4; ++k) *(f4v*)(p + qs * k) = f4v{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
 }
 
 template <int PPL>
@@ -75,9 +81,11 @@ __global__ __launch_bounds__(64) void rotate_backward_kernel(
   constexpr int S = 128 * PPL;  // channels per segment
   constexpr int NP = S / 2;     // pair slots per stage
   extern __shared__ float lds[];
-  float* v = lds;               // [S][BSTR] values
-  float* g = v + S * BSTR;      // [S][BSTR] gradients
-  float* th = g + S * BSTR;     // [K][NP] angle sums of this chunk
+  constexpr int BT = batch_rows(PPL);
+  constexpr int QS = 4 * S;     // floats per plane of four rows
+  float* v = lds;               // [BT / 4][S][4] values
+  float* g = v + S * BT;        // [BT / 4][S][4] gradients
+  float* th = g + S * BT;       // [K][NP] angle sums of this chunk
   const int lane = threadIdx.x;
   const int seg = blockIdx.x % segs, ch = blockIdx.x / segs;
   if (ch >= nchunks) return;
@@ -124,88 +132,96 @@ __global__ __launch_bounds__(64) void rotate_backward_kernel(
           vv[i] = (h ? h_hi(xr[i][q]) : h_lo(xr[i][q])) * sc[q][h];
           gg[i] = gr[i][q][h];
         }
-        lds_put(v + c * BSTR, vv);
-        lds_put(g + c * BSTR, gg);
+        lds_put(v + c * 4, QS, vv);
+        lds_put(g + c * 4, QS, gg);
       }
 
-    // ---- forward: the stages' outputs (each stage's table entries are
-    // requested one stage ahead)
-    // (K == 0: there is no table, and no entry may be read)
-    uint4 en[PPL];
+    // ---- forward: the stages' outputs, then backward: angle sums, gradients
+    // and inputs of each stage. The table entries of two consecutive stages
+    // are held in two register sets, each reloaded right after its use, so a
+    // stage's entries are requested two stages ahead (requests past the end
+    // are clamped to the last stage and unused). K == 0: there is no table,
+    // and no entry may be read.
+    auto fetch = [&](uint4 (&e)[PPL], int t) {
 #pragma unroll
-    for (int q = 0; q < PPL; ++q) en[q] = uint4{0u, 0u, 0u, 0u};
-    if (K > 0) {
-#pragma unroll
-      for (int q = 0; q < PPL; ++q) en[q] = tseg[lane * PPL + q];
-    }
-#pragma unroll 1
-    for (int t = 0; t < K; ++t) {
-      uint4 ec[PPL];
+      for (int q = 0; q < PPL; ++q) e[q] = tseg[(size_t)t * NP + lane * PPL + q];
+    };
+    auto fwd_stage = [&](const uint4 (&en)[PPL]) {
 #pragma unroll
       for (int q = 0; q < PPL; ++q) {
-        ec[q] = en[q];
-        en[q] = tseg[(size_t)min(t + 1, K - 1) * NP + lane * PPL + q];
-      }
-#pragma unroll
-      for (int q = 0; q < PPL; ++q) {
-        const uint4 e = ec[q];
+        const uint4 e = en[q];
         const int i = (int)(e.x & 0xffffu), j = (int)(e.x >> 16);
         const float c = __builtin_bit_cast(float, e.y), s = __builtin_bit_cast(float, e.z);
         float a[BT], b[BT], na[BT], nb[BT];
-        lds_get(v + i * BSTR, a);
-        lds_get(v + j * BSTR, b);
+        lds_get(v + i * 4, QS, a);
+        lds_get(v + j * 4, QS, b);
 #pragma unroll
         for (int r = 0; r < BT; ++r) {
-          na[r] = c * a[r] - s * b[r];
-          nb[r] = s * a[r] + c * b[r];
+          na[r] = __builtin_fmaf(c, a[r], -(s * b[r]));
+          nb[r] = __builtin_fmaf(s, a[r], c * b[r]);
         }
-        lds_put(v + i * BSTR, na);
-        lds_put(v + j * BSTR, nb);
+        lds_put(v + i * 4, QS, na);
+        lds_put(v + j * 4, QS, nb);
       }
-    }
-
-    // ---- backward: angle sums, gradients and inputs of each stage
-    if (K > 0) {
-#pragma unroll
-      for (int q = 0; q < PPL; ++q) en[q] = tseg[(size_t)(K - 1) * NP + lane * PPL + q];
-    }
-#pragma unroll 1
-    for (int t = K - 1; t >= 0; --t) {
-      uint4 ec[PPL];
+    };
+    auto bwd_stage = [&](int t, const uint4 (&en)[PPL]) {
 #pragma unroll
       for (int q = 0; q < PPL; ++q) {
-        ec[q] = en[q];
-        en[q] = tseg[(size_t)max(t - 1, 0) * NP + lane * PPL + q];
-      }
-#pragma unroll
-      for (int q = 0; q < PPL; ++q) {
-        const uint4 e = ec[q];
+        const uint4 e = en[q];
         const int i = (int)(e.x & 0xffffu), j = (int)(e.x >> 16);
         const float c = __builtin_bit_cast(float, e.y), s = __builtin_bit_cast(float, e.z);
         float vi[BT], vj[BT], gi[BT], gj[BT], o1[BT], o2[BT];
-        lds_get(v + i * BSTR, vi);
-        lds_get(v + j * BSTR, vj);
-        lds_get(g + i * BSTR, gi);
-        lds_get(g + j * BSTR, gj);
+        lds_get(v + i * 4, QS, vi);
+        lds_get(v + j * 4, QS, vj);
+        lds_get(g + i * 4, QS, gi);
+        lds_get(g + j * 4, QS, gj);
         float acc = th[t * NP + lane * PPL + q];
 #pragma unroll
-        for (int r = 0; r < BT; ++r) acc += gj[r] * vi[r] - gi[r] * vj[r];
+        for (int r = 0; r < BT; ++r) acc = __builtin_fmaf(-gi[r], vj[r], __builtin_fmaf(gj[r], vi[r], acc));
         th[t * NP + lane * PPL + q] = acc;
 #pragma unroll
         for (int r = 0; r < BT; ++r) {
-          o1[r] = c * gi[r] + s * gj[r];
-          o2[r] = c * gj[r] - s * gi[r];
+          o1[r] = __builtin_fmaf(c, gi[r], s * gj[r]);
+          o2[r] = __builtin_fmaf(c, gj[r], -(s * gi[r]));
         }
-        lds_put(g + i * BSTR, o1);
-        lds_put(g + j * BSTR, o2);
+        lds_put(g + i * 4, QS, o1);
+        lds_put(g + j * 4, QS, o2);
 #pragma unroll
         for (int r = 0; r < BT; ++r) {
-          o1[r] = c * vi[r] + s * vj[r];
-          o2[r] = c * vj[r] - s * vi[r];
+          o1[r] = __builtin_fmaf(c, vi[r], s * vj[r]);
+          o2[r] = __builtin_fmaf(c, vj[r], -(s * vi[r]));
         }
-        lds_put(v + i * BSTR, o1);
-        lds_put(v + j * BSTR, o2);
+        lds_put(v + i * 4, QS, o1);
+        lds_put(v + j * 4, QS, o2);
       }
+    };
+    if (K > 0) {
+      // stage pairs without a branch inside, so that the loads of the two
+      // sets stay in flight across the loop's back edge; an odd K ends with
+      // one more stage
+      uint4 ea[PPL], eb[PPL];
+      fetch(ea, 0);
+      fetch(eb, min(1, K - 1));
+      int t = 0;
+#pragma unroll 1
+      for (; t + 1 < K; t += 2) {
+        fwd_stage(ea);
+        fetch(ea, min(t + 2, K - 1));
+        fwd_stage(eb);
+        fetch(eb, min(t + 3, K - 1));
+      }
+      if (t < K) fwd_stage(ea);
+      fetch(ea, K - 1);
+      fetch(eb, max(K - 2, 0));
+      t = K - 1;
+#pragma unroll 1
+      for (; t >= 1; t -= 2) {
+        bwd_stage(t, ea);
+        fetch(ea, max(t - 2, 0));
+        bwd_stage(t - 1, eb);
+        fetch(eb, max(t - 3, 0));
+      }
+      if (t == 0) bwd_stage(0, ea);
     }
 
     // ---- input gradients and the scales' sums
@@ -213,8 +229,8 @@ __global__ __launch_bounds__(64) void rotate_backward_kernel(
     for (int q = 0; q < PPL; ++q) {
       const int c0 = 2 * (lane + 64 * q);
       float g0[BT], g1[BT];
-      lds_get(g + c0 * BSTR, g0);
-      lds_get(g + (c0 + 1) * BSTR, g1);
+      lds_get(g + c0 * 4, QS, g0);
+      lds_get(g + (c0 + 1) * 4, QS, g1);
 #pragma unroll
       for (int i = 0; i < BT; ++i) {
         if (i < nt) {
@@ -279,6 +295,7 @@ struct ChunkPlan {
 
 ChunkPlan chunk_plan(const paro_rotation* r, int64_t M) {
   const int S = r->lay.seg_ch;
+  const int BT = batch_rows(S / 128);
   ChunkPlan p;
   p.segs = (int)(r->d / S);
   if (M <= 0) {
@@ -312,7 +329,7 @@ hipError_t launch_rotate_backward(const paro_rotation* r, int weight_side, const
   float* part_th = (float*)part;
   float* part_al = part_th + (size_t)p.nchunks * nth;
   if (p.nchunks > 0) {
-    const size_t lds = ((size_t)2 * S * BSTR + (size_t)K * (S / 2)) * sizeof(float);
+    const size_t lds = ((size_t)2 * S * batch_rows(S / 128) + (size_t)K * (S / 2)) * sizeof(float);
     const unsigned blocks = (unsigned)((int64_t)p.segs * p.nchunks);
     if (S == 128)
       hipLaunchKernelGGL(rotate_backward_kernel<1>, dim3(blocks), dim3(64), lds, stream, x, gy, gx,
