@@ -558,6 +558,17 @@ def test_backward_shapes(paro, side, G, K, d, M):
     check_backward(paro, x, g, layer, side)
 
 
+@pytest.mark.parametrize("M,d", [(1, 512), (7, 512), (8, 512), (9, 512), (17, 512), (65, 128),
+                                 (1000, 4096)])
+def test_backward_batch_boundaries(paro, M, d):
+    """Row counts around the gradient kernel's batches (eight rows for
+    128-channel segments) and chunk ends: ragged last batches repeat the last
+    row with a zero gradient and must add nothing."""
+    log(f"backward batch boundaries M={M} d={d}")
+    x, g, layer = grad_case(5000 + M + d, M, d, 128, 8, "activation")
+    check_backward(paro, x, g, layer, "activation")
+
+
 def test_backward_sparse_pairing_and_no_input_gradient(paro):
     """Identities (theta = 0) still get angle gradients; gx = NULL skips the input gradient."""
     log("backward sparse pairing, gx = NULL")
