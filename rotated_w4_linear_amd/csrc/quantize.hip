@@ -32,29 +32,38 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     float* __restrict__ uout) {
   __shared__ float buf[4][256];
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  // wave-uniform: the item, row and group stay in scalar registers, and every
+  // table and row address is a scalar base plus the lane's offset
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t groups = d / G;
   const int64_t total = N * groups;
   float* u = buf[wid];
   const int half = G / 2;
   // Each lane reads its weights as dwords (two consecutive fp16), and the
   // next item's are requested before the current one is transformed.
+  // Items item0, item0 + stride, ...: (row, group) advances by (sn, sg) with
+  // a carry, so no item needs a division.
   const int64_t stride = (int64_t)gridDim.x * 4;
+  const int64_t sn = stride / groups, sg = stride - sn * groups;
   uint32_t nxt[2] = {0u, 0u};
-  auto fetch = [&](int64_t item) {
+  auto fetch = [&](int64_t item, int64_t n, int64_t g) {
     if (item >= total) return;
-    const int64_t n = item / groups, g = item - n * groups;
     const uint32_t* wr = (const uint32_t*)(w + n * d + g * G);
 #pragma unroll
     for (int r = 0; r < 2; ++r)
       if (lane + 64 * r < half) nxt[r] = wr[lane + 64 * r];
   };
-  fetch((int64_t)blockIdx.x * 4 + wid);
-  for (int64_t item = (int64_t)blockIdx.x * 4 + wid; item < total; item += stride) {
-    const int64_t n = item / groups;
-    const int64_t g = item - n * groups;
+  const int64_t item0 = (int64_t)blockIdx.x * 4 + wid;
+  int64_t n = item0 / groups, g = item0 - (item0 / groups) * groups;
+  fetch(item0, n, g);
+  for (int64_t item = item0; item < total; item += stride) {
     const uint32_t cur[2] = {nxt[0], nxt[1]};
-    fetch(item + stride);
+    int64_t nn = n + sn, ng = g + sg;
+    if (ng >= groups) {
+      ng -= groups;
+      ++nn;
+    }
+    fetch(item + stride, nn, ng);
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int k2 = lane + 64 * r;
@@ -127,6 +136,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    n = nn;
+    g = ng;
   }
 }
 
