@@ -24,6 +24,42 @@
 namespace paro {
 namespace {
 
+// Wave-wide min, max and or, exact in any order: within each row of 16 lanes
+// by DPP moves (lane i with i ^ 1, i ^ 2, its mirror in the half row and in
+// the row), then the four rows' values read from lanes 0, 16, 32 and 48.
+__device__ __forceinline__ int dpp_row(int v, int ctrl_step) {
+  switch (ctrl_step) {
+    case 0: return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);   // quad_perm [1, 0, 3, 2]
+    case 1: return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);   // quad_perm [2, 3, 0, 1]
+    case 2: return __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    default: return __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false); // row_mirror
+  }
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v = fminf(v, __builtin_bit_cast(float, dpp_row(__builtin_bit_cast(int, v), k)));
+  const int b = __builtin_bit_cast(int, v);
+  return fminf(fminf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)),
+                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))),
+               fminf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)),
+                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48))));
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v = fmaxf(v, __builtin_bit_cast(float, dpp_row(__builtin_bit_cast(int, v), k)));
+  const int b = __builtin_bit_cast(int, v);
+  return fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)),
+                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))),
+               fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)),
+                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48))));
+}
+__device__ __forceinline__ int wave_or(int v) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v |= dpp_row(v, k);
+  return __builtin_amdgcn_readlane(v, 0) | __builtin_amdgcn_readlane(v, 16) |
+         __builtin_amdgcn_readlane(v, 32) | __builtin_amdgcn_readlane(v, 48);
+}
+
 __global__ __launch_bounds__(256) void quantize_kernel(
     const uint16_t* __restrict__ w, int64_t N, int64_t d, int G, int K,
     const uint32_t* __restrict__ wt_pairs, const float* __restrict__ wt_c,
@@ -105,12 +141,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(
       mn = fminf(mn, v);
       mx = fmaxf(mx, v);
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      mn = fminf(mn, __shfl_xor(mn, off, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-      bad |= __shfl_xor(bad, off, 64);
-    }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    bad = wave_or(bad);
     const float range = mx - mn;
     const float s32 = range / 15.0f;
     _Float16 s16 = (_Float16)s32;
