@@ -12,9 +12,9 @@
 //   z = clamp(rint(fl(-mn / s16)), 0, 15); q = clamp(rint(fl(u / s16)) + z, 0, 15).
 // The file is compiled without floating-point contraction.
 //
-// One wavefront owns one (output row, group): the group lives in a
-// wave-private LDS slice, each lane updates its own pairs per stage, and
-// min/max are wave reductions (exact in any order).
+// One wavefront owns one or two (output row, group) items at a time: each
+// group lives in a wave-private LDS slice, each lane updates its own pairs per
+// stage, and min/max are wave reductions (exact in any order).
 #include <cmath>
 
 #include "paro_internal.h"
@@ -60,6 +60,12 @@ __device__ __forceinline__ int wave_or(int v) {
          __builtin_amdgcn_readlane(v, 32) | __builtin_amdgcn_readlane(v, 48);
 }
 
+// NI: items per wavefront step. Two for groups of up to 128 channels: the
+// two items' stage chains (dependent LDS round trips) then overlap. One for
+// groups of 256 channels, whose slice fills the wavefront's 256 floats.
+// Slot r (0, 1) of a lane is pair `lane` of item r (NI = 2; item r's slice at
+// u + 128 r) or pair lane + 64 r of the one item (NI = 1).
+template <int NI>
 __global__ __launch_bounds__(256) void quantize_kernel(
     const uint16_t* __restrict__ w, int64_t N, int64_t d, int G, int K,
     const uint32_t* __restrict__ wt_pairs, const float* __restrict__ wt_c,
@@ -67,29 +73,45 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros, int* __restrict__ flag,
     float* __restrict__ uout) {
   __shared__ float buf[4][256];
+  constexpr int SL = 128;  // floats between the two items' slices (NI = 2)
   const int lane = threadIdx.x & 63;
-  // wave-uniform: the item, row and group stay in scalar registers, and every
+  // wave-uniform: items, rows and groups stay in scalar registers, and every
   // table and row address is a scalar base plus the lane's offset
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t groups = d / G;
   const int64_t total = N * groups;
   float* u = buf[wid];
   const int half = G / 2;
+  auto item_of = [](int r) { return NI == 2 ? r : 0; };
+  auto pair_of = [&](int r) { return NI == 2 ? lane : lane + 64 * r; };
+  // A step takes items item, item + 1 (NI = 2): the second is the next group
+  // of the same row, or group 0 of the next row.
+  auto second = [&](int64_t n, int64_t g, int64_t& n1, int64_t& g1) {
+    g1 = g + 1;
+    n1 = n;
+    if (g1 == groups) {
+      g1 = 0;
+      ++n1;
+    }
+  };
   // Each lane reads its weights as dwords (two consecutive fp16), and the
-  // next item's are requested before the current one is transformed.
-  // Items item0, item0 + stride, ...: (row, group) advances by (sn, sg) with
-  // a carry, so no item needs a division.
-  const int64_t stride = (int64_t)gridDim.x * 4;
+  // next step's are requested before the current one is transformed. Steps
+  // item0, item0 + stride, ...: (row, group) advances by (sn, sg) with a
+  // carry, so no step needs a division.
+  const int64_t stride = (int64_t)gridDim.x * 4 * NI;
   const int64_t sn = stride / groups, sg = stride - sn * groups;
   uint32_t nxt[2] = {0u, 0u};
   auto fetch = [&](int64_t item, int64_t n, int64_t g) {
-    if (item >= total) return;
-    const uint32_t* wr = (const uint32_t*)(w + n * d + g * G);
+    int64_t n1, g1;
+    second(n, g, n1, g1);
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-      if (lane + 64 * r < half) nxt[r] = wr[lane + 64 * r];
+    for (int r = 0; r < 2; ++r) {
+      const int q = item_of(r), p = pair_of(r);
+      if (item + q < total && p < half)
+        nxt[r] = ((const uint32_t*)(w + (q ? n1 : n) * d + (q ? g1 : g) * G))[p];
+    }
   };
-  const int64_t item0 = (int64_t)blockIdx.x * 4 + wid;
+  const int64_t item0 = ((int64_t)blockIdx.x * 4 + wid) * NI;
   int64_t n = item0 / groups, g = item0 - (item0 / groups) * groups;
   fetch(item0, n, g);
   for (int64_t item = item0; item < total; item += stride) {
@@ -100,72 +122,98 @@ __global__ __launch_bounds__(256) void quantize_kernel(
       ++nn;
     }
     fetch(item + stride, nn, ng);
+    int64_t n1, g1;
+    second(n, g, n1, g1);
+    const int ni = (NI == 2 && item + 1 < total) ? 2 : 1;  // items of this step
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int k2 = lane + 64 * r;
-      if (k2 < half) {
+      const int q = item_of(r), p = pair_of(r);
+      if (p < half) {
+        const int64_t gq = q ? g1 : g;
         float v0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(cur[r] & 0xffffu));
         float v1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(cur[r] >> 16));
         if (alpha) {
-          v0 = v0 * alpha[g * G + 2 * k2];
-          v1 = v1 * alpha[g * G + 2 * k2 + 1];
+          v0 = v0 * alpha[gq * G + 2 * p];
+          v1 = v1 * alpha[gq * G + 2 * p + 1];
         }
-        u[2 * k2] = v0;
-        u[2 * k2 + 1] = v1;
+        u[SL * q + 2 * p] = v0;
+        u[SL * q + 2 * p + 1] = v1;
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     for (int t = 0; t < K; ++t) {
-      const size_t base = ((size_t)g * K + t) * half;
-      for (int p = lane; p < half; p += 64) {
-        const uint32_t ij = wt_pairs[base + p];
-        const int i = (int)(ij & 0xffffu), j = (int)(ij >> 16);
-        const float c = wt_c[base + p], s = wt_s[base + p];
-        const float a = u[i], b = u[j];
-        const float ca = c * a, sb = s * b, sa = s * a, cb = c * b;
-        u[i] = ca - sb;
-        u[j] = sa + cb;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int q = item_of(r), p = pair_of(r);
+        if (p < half) {
+          const size_t e = ((size_t)(q ? g1 : g) * K + t) * half + p;
+          const uint32_t ij = wt_pairs[e];
+          const int i = SL * q + (int)(ij & 0xffffu), j = SL * q + (int)(ij >> 16);
+          const float c = wt_c[e], s = wt_s[e];
+          const float a = u[i], b = u[j];
+          const float ca = c * a, sb = s * b, sa = s * a, cb = c * b;
+          u[i] = ca - sb;
+          u[j] = sa + cb;
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    if (uout) {  // the transformed row itself (fp32), for the layer loss's gradients
-      for (int k = lane; k < G; k += 64) uout[n * d + g * G + k] = u[k];
+    // per item: the transformed row itself (fp32, for the layer loss's
+    // gradients), min / max / non-finite over the wave, scale, zero, codes
+    float mn[NI], mx[NI];
+    int bad[NI];
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      mn[q] = 0.0f;
+      mx[q] = 0.0f;
+      bad[q] = 0;
+      if (q < ni) {
+        const int64_t nq = q ? n1 : n, gq = q ? g1 : g;
+        for (int k = lane; k < G; k += 64) {
+          const float v = u[SL * q + k];
+          if (uout) uout[nq * d + gq * G + k] = v;
+          bad[q] |= !__builtin_isfinite(v);
+          mn[q] = fminf(mn[q], v);
+          mx[q] = fmaxf(mx[q], v);
+        }
+      }
     }
-    float mn = 0.0f, mx = 0.0f;
-    int bad = 0;
-    for (int k = lane; k < G; k += 64) {
-      const float v = u[k];
-      bad |= !__builtin_isfinite(v);
-      mn = fminf(mn, v);
-      mx = fmaxf(mx, v);
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      mn[q] = wave_min(mn[q]);
+      mx[q] = wave_max(mx[q]);
+      bad[q] = wave_or(bad[q]);
     }
-    mn = wave_min(mn);
-    mx = wave_max(mx);
-    bad = wave_or(bad);
-    const float range = mx - mn;
-    const float s32 = range / 15.0f;
-    _Float16 s16 = (_Float16)s32;
-    float sq = (float)s16;
-    if (bad || !__builtin_isfinite(sq)) {
-      if (lane == 0) atomicOr(flag, 1);
-    }
-    if (sq == 0.0f) {
-      s16 = (_Float16)1.0f;
-      sq = 1.0f;
-    }
-    const float negmn = -mn;
-    const float zf = fminf(fmaxf(rintf(negmn / sq), 0.0f), 15.0f);
-    for (int b = lane; b < half; b += 64) {
-      const float q0f = fminf(fmaxf(rintf(u[2 * b] / sq) + zf, 0.0f), 15.0f);
-      const float q1f = fminf(fmaxf(rintf(u[2 * b + 1] / sq) + zf, 0.0f), 15.0f);
-      const uint32_t q0 = (uint32_t)q0f, q1 = (uint32_t)q1f;
-      qweight[n * (d / 2) + g * half + b] = (uint8_t)(q0 | (q1 << 4));
-    }
-    if (lane == 0) {
-      scales[n * groups + g] = __builtin_bit_cast(uint16_t, s16);
-      zeros[n * groups + g] = (uint8_t)zf;
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      if (q < ni) {
+        const int64_t nq = q ? n1 : n, gq = q ? g1 : g;
+        const float range = mx[q] - mn[q];
+        const float s32 = range / 15.0f;
+        _Float16 s16 = (_Float16)s32;
+        float sq = (float)s16;
+        if (bad[q] || !__builtin_isfinite(sq)) {
+          if (lane == 0) atomicOr(flag, 1);
+        }
+        if (sq == 0.0f) {
+          s16 = (_Float16)1.0f;
+          sq = 1.0f;
+        }
+        const float negmn = -mn[q];
+        const float zf = fminf(fmaxf(rintf(negmn / sq), 0.0f), 15.0f);
+        for (int b = lane; b < half; b += 64) {
+          const float q0f = fminf(fmaxf(rintf(u[SL * q + 2 * b] / sq) + zf, 0.0f), 15.0f);
+          const float q1f = fminf(fmaxf(rintf(u[SL * q + 2 * b + 1] / sq) + zf, 0.0f), 15.0f);
+          const uint32_t q0 = (uint32_t)q0f, q1 = (uint32_t)q1f;
+          qweight[nq * (d / 2) + gq * half + b] = (uint8_t)(q0 | (q1 << 4));
+        }
+        if (lane == 0) {
+          scales[nq * groups + gq] = __builtin_bit_cast(uint16_t, s16);
+          zeros[nq * groups + gq] = (uint8_t)zf;
+        }
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -181,9 +229,11 @@ hipError_t launch_quantize(const paro_rotation* r, const uint16_t* w, int64_t N,
                            int* d_flag, hipStream_t stream, float* uout) {
   const int64_t total = N * (d / group);
   if (total == 0) return hipSuccess;
-  int64_t blocks = (total + 3) / 4;
+  const int ni = group <= 128 ? 2 : 1;
+  int64_t blocks = (total + 4 * ni - 1) / (4 * ni);
   if (blocks > 16384) blocks = 16384;
-  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w, N, d, group,
+  auto kern = ni == 2 ? quantize_kernel<2> : quantize_kernel<1>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, stream, w, N, d, group,
                      r ? r->K : 0, r ? r->d_wt_pairs : nullptr, r ? r->d_wt_c : nullptr,
                      r ? r->d_wt_s : nullptr, r ? r->d_alpha : nullptr, qweight, scales, zeros,
                      d_flag, uout);
