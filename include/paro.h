@@ -282,7 +282,10 @@ size_t paro_layer_loss_workspace_size(const paro_rotation* r, int64_t M, int64_t
  * angles and scales, that sum equals the activation side's gradient for
  * dL/dX' = dY E, E = W_hat - T W (T W in the quantizer's fp32), which is how
  * it is computed: the two sides' other terms cancel and are each tens of
- * times larger than the result.
+ * times larger than the result. E comes from the quantizer's own pass over
+ * T W, with W_hat from the codes that pass produces; these equal qweight,
+ * scales and zeros bit for bit when those are Q(T W) of this plan, as
+ * required above.
  *
  *   x        device fp16 [M][d], w device fp16 [N][d] (16-byte aligned);
  *   qweight, scales, zeros: as for paro_w4_linear, with the plan's group;

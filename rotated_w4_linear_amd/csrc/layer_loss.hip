@@ -36,27 +36,6 @@ namespace {
 
 constexpr int kLossBlocks = 1024;  // partial sums of the loss (fixed: the order never changes)
 
-// E[n][k] = (q - z) s - u[n][k] in fp32 ((q - z) s is exact: |q - z| <= 15
-// and s is fp16; one rounding for the difference); out may be u
-__global__ __launch_bounds__(256) void quant_error_kernel(const uint8_t* __restrict__ qw,
-                                                          const uint16_t* __restrict__ sc,
-                                                          const uint8_t* __restrict__ zr,
-                                                          const float* u, float* out, int64_t N,
-                                                          int64_t d, int gshift) {
-  const int64_t total = N * (d / 2);
-  const int64_t groups = d >> gshift;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-    const int64_t n = i / (d / 2), b = i % (d / 2);
-    const int64_t k = 2 * b;
-    const uint8_t byte = qw[i];
-    const int64_t g = n * groups + (k >> gshift);
-    const float s = (float)__builtin_bit_cast(_Float16, sc[g]);
-    const float z = (float)zr[g];
-    out[n * d + k] = ((float)(byte & 15) - z) * s - u[n * d + k];
-    out[n * d + k + 1] = ((float)(byte >> 4) - z) * s - u[n * d + k + 1];
-  }
-}
-
 // Block b sums (y_q - y)^2 over elements b, b + B, b + 2B, ... (grid-stride
 // by thread, then a fixed tree over the block) into part[b]; with dy != NULL
 // it also writes dy = 2 (y_q - y) (dy may be y).
@@ -143,7 +122,7 @@ rocblas_handle blas_handle(int device) {
 }
 
 struct LossLayout {
-  size_t xr, yq, y, w4, part, e, dxr, qw, sc, zr, flag, bw, dth, dal, yh, yl, eh, el, total;
+  size_t xr, yq, y, w4, part, dxr, qw, sc, zr, flag, bw, dth, dal, yh, yl, eh, el, total;
 };
 
 LossLayout loss_layout(const paro_rotation* r, int64_t M, int64_t N, int64_t d, bool grad) {
@@ -160,7 +139,6 @@ LossLayout loss_layout(const paro_rotation* r, int64_t M, int64_t N, int64_t d, 
   L.w4 = take(paro_w4_linear_workspace_size(nullptr, M, N, d));
   L.part = take((size_t)kLossBlocks * 4);
   if (grad) {
-    L.e = take((size_t)N * d * 4);
     L.dxr = take((size_t)M * d * 4);
     L.qw = take((size_t)N * (d / 2));
     L.sc = take((size_t)N * (d / r->group) * 2);
@@ -223,26 +201,21 @@ int run_layer_loss(const paro_rotation* r, const uint16_t* x, const uint16_t* w,
   if (!grad) return PARO_OK;
 
   float* dy = y;
-  float* err = (float*)(base + L.e);
   float* dxr = (float*)(base + L.dxr);
-  const int gshift = group == 64 ? 6 : group == 128 ? 7 : 8;
-  // T W in fp32 (the quantizer's pass; its codes go to scratch), then E = W_hat - T W
+  uint16_t* eh = (uint16_t*)(base + L.eh);
+  uint16_t* el = (uint16_t*)(base + L.el);
+  // The quantizer's pass over T W (its codes go to scratch) writes the
+  // quantization error E = W_hat - T W, as bf16 high and low parts
   if ((e = launch_quantize(r, w, N, d, group, (uint8_t*)(base + L.qw), (uint16_t*)(base + L.sc),
-                           (uint8_t*)(base + L.zr), (int*)(base + L.flag), stream, err)) != hipSuccess)
+                           (uint8_t*)(base + L.zr), (int*)(base + L.flag), stream, eh, el)) != hipSuccess)
     return fail(e, "paro_layer_loss: weight transform");
-  hipLaunchKernelGGL(quant_error_kernel, dim3(grid_for(N * d / 2)), dim3(256), 0, stream, qw, sc, zr,
-                     err, err, N, d, gshift);
-  if ((e = hipGetLastError()) != hipSuccess) return fail(e, "paro_layer_loss: quantization error");
   // dX' (column-major d x M, ld d) = E (column-major d x N) * dY^T (column-major N x M),
   // as three bf16 products with fp32 accumulation: E_hi dY_hi + E_hi dY_lo +
   // E_lo dY_hi carries about 16 bits of each operand (relative error ~2^-16),
   // at a fraction of an fp32 GEMM's time, with fp32's range
   uint16_t* yh = (uint16_t*)(base + L.yh);
   uint16_t* yl = (uint16_t*)(base + L.yl);
-  uint16_t* eh = (uint16_t*)(base + L.eh);
-  uint16_t* el = (uint16_t*)(base + L.el);
   hipLaunchKernelGGL(split_bf16_kernel, dim3(grid_for(M * N)), dim3(256), 0, stream, dy, yh, yl, M * N);
-  hipLaunchKernelGGL(split_bf16_kernel, dim3(grid_for(N * d)), dim3(256), 0, stream, err, eh, el, N * d);
   if ((e = hipGetLastError()) != hipSuccess) return fail(e, "paro_layer_loss: split");
   const uint16_t* ea[3] = {eh, eh, el};
   const uint16_t* yb[3] = {yh, yl, yh};

@@ -110,10 +110,13 @@ namespace paro {
 // Kernel launchers (defined in the .hip files). Return hipError_t of the launch.
 hipError_t launch_rotate(const paro_rotation* r, const uint16_t* x, uint16_t* y, int64_t M,
                          hipStream_t stream);
-// uout (may be NULL): also writes the transformed rows T W in fp32 [N][d]
+// ehi, elo (both NULL or both set, 4-byte aligned): also writes the
+// quantization error E = W_hat - T W [N][d] (W_hat = (q - z) s) as bf16 high
+// and low parts, hi = bf16(E), lo = bf16(E - hi)
 hipError_t launch_quantize(const paro_rotation* r, const uint16_t* w, int64_t N, int64_t d,
                            int group, uint8_t* qweight, uint16_t* scales, uint8_t* zeros,
-                           int* d_flag, hipStream_t stream, float* uout = nullptr);
+                           int* d_flag, hipStream_t stream, uint16_t* ehi = nullptr,
+                           uint16_t* elo = nullptr);
 // Large-batch linear (M > 16) on already transformed activations.
 hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
                           const uint8_t* zeros, const uint16_t* bias, uint16_t* y, int64_t M,

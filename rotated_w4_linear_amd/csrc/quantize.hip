@@ -24,6 +24,13 @@
 namespace paro {
 namespace {
 
+// Round to the nearest bfloat16, ties to even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
 // Wave-wide min, max and or, exact in any order: within each row of 16 lanes
 // by DPP moves (lane i with i ^ 1, i ^ 2, its mirror in the half row and in
 // the row), then the four rows' values read from lanes 0, 16, 32 and 48.
@@ -71,7 +78,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     const uint32_t* __restrict__ wt_pairs, const float* __restrict__ wt_c,
     const float* __restrict__ wt_s, const float* __restrict__ alpha, uint8_t* __restrict__ qweight,
     uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros, int* __restrict__ flag,
-    float* __restrict__ uout) {
+    uint16_t* __restrict__ ehi, uint16_t* __restrict__ elo) {
   __shared__ float buf[4][256];
   constexpr int SL = 128;  // floats between the two items' slices (NI = 2)
   const int lane = threadIdx.x & 63;
@@ -160,8 +167,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    // per item: the transformed row itself (fp32, for the layer loss's
-    // gradients), min / max / non-finite over the wave, scale, zero, codes
+    // per item: min / max / non-finite over the wave, scale, zero, codes
     float mn[NI], mx[NI];
     int bad[NI];
 #pragma unroll
@@ -173,7 +179,6 @@ __global__ __launch_bounds__(256) void quantize_kernel(
         const int64_t nq = q ? n1 : n, gq = q ? g1 : g;
         for (int k = lane; k < G; k += 64) {
           const float v = u[SL * q + k];
-          if (uout) uout[nq * d + gq * G + k] = v;
           bad[q] |= !__builtin_isfinite(v);
           mn[q] = fminf(mn[q], v);
           mx[q] = fmaxf(mx[q], v);
@@ -208,6 +213,18 @@ __global__ __launch_bounds__(256) void quantize_kernel(
           const float q1f = fminf(fmaxf(rintf(u[SL * q + 2 * b + 1] / sq) + zf, 0.0f), 15.0f);
           const uint32_t q0 = (uint32_t)q0f, q1 = (uint32_t)q1f;
           qweight[nq * (d / 2) + gq * half + b] = (uint8_t)(q0 | (q1 << 4));
+          if (ehi) {
+            // the quantization error E = (q - z) s - T W ((q - z) s is exact in
+            // fp32), as bf16 high and low parts
+            const float e0 = (q0f - zf) * sq - u[SL * q + 2 * b];
+            const float e1 = (q1f - zf) * sq - u[SL * q + 2 * b + 1];
+            const uint32_t h0 = bf16_rne(e0), h1 = bf16_rne(e1);
+            const uint32_t l0 = bf16_rne(e0 - __builtin_bit_cast(float, h0 << 16));
+            const uint32_t l1 = bf16_rne(e1 - __builtin_bit_cast(float, h1 << 16));
+            const int64_t o = nq * d + gq * G + 2 * b;
+            *(uint32_t*)(ehi + o) = h0 | (h1 << 16);
+            *(uint32_t*)(elo + o) = l0 | (l1 << 16);
+          }
         }
         if (lane == 0) {
           scales[nq * groups + gq] = __builtin_bit_cast(uint16_t, s16);
@@ -226,7 +243,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(
 
 hipError_t launch_quantize(const paro_rotation* r, const uint16_t* w, int64_t N, int64_t d,
                            int group, uint8_t* qweight, uint16_t* scales, uint8_t* zeros,
-                           int* d_flag, hipStream_t stream, float* uout) {
+                           int* d_flag, hipStream_t stream, uint16_t* ehi, uint16_t* elo) {
   const int64_t total = N * (d / group);
   if (total == 0) return hipSuccess;
   const int ni = group <= 128 ? 2 : 1;
@@ -236,7 +253,7 @@ hipError_t launch_quantize(const paro_rotation* r, const uint16_t* w, int64_t N,
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, stream, w, N, d, group,
                      r ? r->K : 0, r ? r->d_wt_pairs : nullptr, r ? r->d_wt_c : nullptr,
                      r ? r->d_wt_s : nullptr, r ? r->d_alpha : nullptr, qweight, scales, zeros,
-                     d_flag, uout);
+                     d_flag, ehi, elo);
   return hipGetLastError();
 }
 
