@@ -20,7 +20,7 @@
 // The two dense products (X W^T, and dY E as three bf16 products of split
 // operands) are plain GEMMs and go to rocBLAS;
 // the rest runs in this library's kernels: the transform, the W4 linear, the
-// fp32 transform of W (the quantizer's own pass), the exact dequantization,
+// fp32 transform of W with the quantization error (the quantizer's own pass),
 // the loss with its deterministic reduction, and the activation side's
 // gradients.
 #include <rocblas/rocblas.h>
@@ -36,18 +36,34 @@ namespace {
 
 constexpr int kLossBlocks = 1024;  // partial sums of the loss (fixed: the order never changes)
 
+// x = hi + lo + (a remainder of about 2^-16 |x|): hi = bf16(x), lo = bf16(x - hi),
+// both rounded to nearest even
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
 // Block b sums (y_q - y)^2 over elements b, b + B, b + 2B, ... (grid-stride
-// by thread, then a fixed tree over the block) into part[b]; with dy != NULL
-// it also writes dy = 2 (y_q - y) (dy may be y).
+// by thread, then a fixed tree over the block) into part[b]; with dyh != NULL
+// it also writes dY = 2 (y_q - y) as bf16 high and low parts,
+// dyh = bf16(dY), dyl = bf16(dY - dyh).
 __global__ __launch_bounds__(256) void loss_partial_kernel(const uint16_t* __restrict__ yq,
-                                                           const float* y, float* dy, int64_t n,
+                                                           const float* __restrict__ y,
+                                                           uint16_t* __restrict__ dyh,
+                                                           uint16_t* __restrict__ dyl, int64_t n,
                                                            float* __restrict__ part) {
   __shared__ float red[256];
   float acc = 0.f;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     const float diff = (float)__builtin_bit_cast(_Float16, yq[i]) - y[i];
     acc += diff * diff;
-    if (dy) dy[i] = 2.0f * diff;
+    if (dyh) {
+      const float g = 2.0f * diff;
+      const uint16_t h = bf16_rne(g);
+      dyh[i] = h;
+      dyl[i] = bf16_rne(g - __builtin_bit_cast(float, (uint32_t)h << 16));
+    }
   }
   red[threadIdx.x] = acc;
   __syncthreads();
@@ -72,24 +88,6 @@ __global__ __launch_bounds__(256) void loss_final_kernel(const float* __restrict
     __syncthreads();
   }
   if (threadIdx.x == 0) loss[0] = (float)red[0];
-}
-
-// x = hi + lo + (a remainder of about 2^-16 |x|): hi = bf16(x), lo = bf16(x - hi),
-// both rounded to nearest even
-__device__ __forceinline__ uint16_t bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-__global__ __launch_bounds__(256) void split_bf16_kernel(const float* __restrict__ a,
-                                                         uint16_t* __restrict__ hi,
-                                                         uint16_t* __restrict__ lo, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const float v = a[i];
-    const uint16_t h = bf16_rne(v);
-    hi[i] = h;
-    lo[i] = bf16_rne(v - __builtin_bit_cast(float, (uint32_t)h << 16));
-  }
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ a, int64_t n) {
@@ -194,13 +192,14 @@ int run_layer_loss(const paro_rotation* r, const uint16_t* x, const uint16_t* w,
     set_error("paro_layer_loss: rocBLAS X W^T");
     return PARO_ERR_HIP;
   }
-  hipLaunchKernelGGL(loss_partial_kernel, dim3(kLossBlocks), dim3(256), 0, stream, yq, y,
-                     grad ? y : nullptr, M * N, part);
+  uint16_t* yh = grad ? (uint16_t*)(base + L.yh) : nullptr;
+  uint16_t* yl = grad ? (uint16_t*)(base + L.yl) : nullptr;
+  hipLaunchKernelGGL(loss_partial_kernel, dim3(kLossBlocks), dim3(256), 0, stream, yq, y, yh, yl,
+                     M * N, part);
   hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(256), 0, stream, part, kLossBlocks, loss);
   if ((e = hipGetLastError()) != hipSuccess) return fail(e, "paro_layer_loss: loss");
   if (!grad) return PARO_OK;
 
-  float* dy = y;
   float* dxr = (float*)(base + L.dxr);
   uint16_t* eh = (uint16_t*)(base + L.eh);
   uint16_t* el = (uint16_t*)(base + L.el);
@@ -212,11 +211,8 @@ int run_layer_loss(const paro_rotation* r, const uint16_t* x, const uint16_t* w,
   // dX' (column-major d x M, ld d) = E (column-major d x N) * dY^T (column-major N x M),
   // as three bf16 products with fp32 accumulation: E_hi dY_hi + E_hi dY_lo +
   // E_lo dY_hi carries about 16 bits of each operand (relative error ~2^-16),
-  // at a fraction of an fp32 GEMM's time, with fp32's range
-  uint16_t* yh = (uint16_t*)(base + L.yh);
-  uint16_t* yl = (uint16_t*)(base + L.yl);
-  hipLaunchKernelGGL(split_bf16_kernel, dim3(grid_for(M * N)), dim3(256), 0, stream, dy, yh, yl, M * N);
-  if ((e = hipGetLastError()) != hipSuccess) return fail(e, "paro_layer_loss: split");
+  // at a fraction of an fp32 GEMM's time, with fp32's range (dY's parts come
+  // from the loss kernel, E's from the quantizer)
   const uint16_t* ea[3] = {eh, eh, el};
   const uint16_t* yb[3] = {yh, yl, yh};
   for (int t = 0; t < 3; ++t) {
