@@ -44,7 +44,10 @@ namespace {
 // K = 8: the table entries, addresses and angle sums of a stage serve twice
 // the rows), four for 256-channel segments (eight measured no faster there).
 __host__ __device__ constexpr int batch_rows(int ppl) { return ppl == 1 ? 8 : 4; }
-constexpr int64_t kTargetWaves = 4096;
+// Wavefronts per launch (measured at 8192 x 4096, K = 8, over 2048..6144):
+// 4096 for 128-channel segments, 3072 for 256-channel segments (170 against
+// 192 us at 4096).
+constexpr int64_t target_waves(int seg_ch) { return seg_ch == 128 ? 4096 : 3072; }
 
 typedef float f4v __attribute__((ext_vector_type(4)));
 
@@ -303,9 +306,9 @@ ChunkPlan chunk_plan(const paro_rotation* r, int64_t M) {
     p.nchunks = 0;
     return p;
   }
-  // about kTargetWaves wavefronts, chunks a multiple of BT rows
+  // about target_waves(S) wavefronts, chunks a multiple of BT rows
   const int64_t batches = (M + BT - 1) / BT;
-  int64_t want = (kTargetWaves + p.segs - 1) / p.segs;
+  int64_t want = (target_waves(S) + p.segs - 1) / p.segs;
   want = std::max<int64_t>(1, std::min(want, batches));
   const int64_t per = (batches + want - 1) / want;
   p.chunk = (int)(per * BT);
