@@ -62,7 +62,8 @@ __all__ = [
     "check_rotation_params", "cos_sin_f32", "rotate_activations",
     "transform_weights_f32", "transform_weights_f64", "quantize_groups",
     "pack_codes", "unpack_codes", "dequantize", "quantize_weights", "linear",
-    "rotated_w4_linear", "rotation_backward", "layer_loss", "QuantizeError",
+    "rotated_w4_linear", "rotation_backward", "layer_loss", "layer_loss_gradients",
+    "QuantizeError",
 ]
 
 
@@ -347,39 +348,42 @@ def rotated_w4_linear(x, qweight, scales, zeros, group, pairs=None, theta=None, 
 # Layer-wise output loss (transform learning)
 # ----------------------------------------------------------------------------
 
-def layer_loss(x, w, qweight, scales, zeros, group, pairs, theta, alpha, grad=False, round16=True):
+def layer_loss(x, w, qweight, scales, zeros, group, pairs, theta, alpha, grad=False):
     """Layer-wise output loss of the quantized, transformed layer, and its
-    gradients with respect to the angles and scales (fp64).
+    gradients with respect to the angles and scales (fp64, no rounding).
 
     [Notes] "损失函数 / 训练策略": L = ||Q(D)(X') - D(X)||, here the squared
     Frobenius norm L = sum (Y_q - Y)^2 with D(X) = X W^T the layer in its
     original fp16 weights and Q(D)(X') = X' W_hat^T the 4-bit layer on the
-    transformed activations (W_hat the dequantized Q(T W)). With round16 the
-    loss rounds to fp16 where the product path does (X', each dequantized
-    weight as the W4 linear multiplies it, and Y_q); the gradients treat those
-    roundings, like the quantizer, as the identity.
+    transformed activations (X' = X T^-1 unrounded, W_hat the exactly
+    dequantized Q(T W)). Every product and sum is fp64.
 
     Gradients (grad=True) pass through the quantizer unchanged (the
-    straight-through reading of training through Q): dL/dY_q = 2 (Y_q - Y),
-    dL/dX' = dY W_hat, dL/dW_hat = dY^T X' taken as dL/d(T W), then each
-    transform's own gradients (``rotation_backward``, activation side for X',
-    weight side for T W), summed. Returns L, or (L, dtheta [K][d/2], dalpha [d]).
+    straight-through reading of training through Q): see
+    ``layer_loss_gradients``. Returns L, or (L, dtheta [K][d/2], dalpha [d]).
     """
-    xr_exact = rotate_activations(x, pairs, theta, alpha)
-    xr = xr_exact.astype(np.float16).astype(np.float64) if round16 else xr_exact
+    xr = rotate_activations(x, pairs, theta, alpha)
     what = dequantize(qweight, scales, zeros, group)
-    # the layer multiplies the fp16 rounding of each dequantized weight
-    yq = xr @ (what.astype(np.float16).astype(np.float64) if round16 else what).T
-    if round16:
-        yq = yq.astype(np.float16).astype(np.float64)
+    yq = xr @ what.T
     y = np.asarray(x).astype(np.float64) @ np.asarray(w).astype(np.float64).T
     diff = yq - y
     loss = float(np.sum(diff * diff))
     if not grad:
         return loss
-    dy = 2.0 * diff
-    dxr = dy @ what
-    dw = dy.T @ xr_exact  # the fp16 rounding of X' passes gradients unchanged too
-    _, dth_a, dal_a = rotation_backward(x, dxr, pairs, theta, alpha, "activation")
-    _, dth_w, dal_w = rotation_backward(w, dw, pairs, theta, alpha, "weight")
-    return loss, dth_a + dth_w, dal_a + dal_w
+    dth, dal = layer_loss_gradients(x, w, xr, what, 2.0 * diff, pairs, theta, alpha)
+    return loss, dth, dal
+
+
+def layer_loss_gradients(x, w, xr, what, dy, pairs, theta, alpha):
+    """Straight-through angle and scale gradients of the layer loss for a given
+    dL/dY_q = ``dy`` [M][N] (fp64; linear in ``dy``).
+
+    dL/dX' = dY W_hat and dL/dW_hat = dY^T X', the latter taken as dL/d(T W);
+    then each transform's own gradients (``rotation_backward``: activation side
+    for X', weight side for T W), summed. ``xr`` is the unrounded X' and
+    ``what`` the dequantized weights [N][d]. Returns (dtheta [K][d/2], dalpha [d]).
+    """
+    dy = np.asarray(dy, dtype=np.float64)
+    _, dth_a, dal_a = rotation_backward(x, dy @ what, pairs, theta, alpha, "activation")
+    _, dth_w, dal_w = rotation_backward(w, dy.T @ xr, pairs, theta, alpha, "weight")
+    return dth_a + dth_w, dal_a + dal_w

@@ -530,7 +530,7 @@ def test_l_loss_is_the_output_error_of_the_quantized_layer():
     q, s, z = oracle.quantize_weights(w, G)
     what = oracle.dequantize(q, s, z, G)
     want = np.sum((x.astype(np.float64) @ what.T - x.astype(np.float64) @ w.astype(np.float64).T) ** 2)
-    got = oracle.layer_loss(x, w, q, s, z, G, pairs, theta, alpha, round16=False)
+    got = oracle.layer_loss(x, w, q, s, z, G, pairs, theta, alpha)
     assert np.isclose(got, want, rtol=1e-12)
 
 
@@ -548,7 +548,7 @@ def test_l_gradients_match_finite_differences_with_frozen_quantization_error():
     q, s, z = oracle.quantize_weights(w, G, pairs, theta, alpha)
     e0 = oracle.dequantize(q, s, z, G) - oracle.transform_weights_f64(w, pairs, theta, alpha)
     y = x.astype(np.float64) @ w.astype(np.float64).T
-    _, dth, dal = oracle.layer_loss(x, w, q, s, z, G, pairs, theta, alpha, grad=True, round16=False)
+    _, dth, dal = oracle.layer_loss(x, w, q, s, z, G, pairs, theta, alpha, grad=True)
 
     def surrogate(th, al):
         xr = oracle.rotate_activations(x, pairs, th, al)
@@ -579,12 +579,63 @@ def test_l_gradient_is_the_activation_side_through_the_quantization_error():
     q, s, z = oracle.quantize_weights(layer.w, 128, layer.pairs, layer.theta, layer.alpha)
     _, dth, dal = oracle.layer_loss(x, layer.w, q, s, z, 128, layer.pairs, layer.theta, layer.alpha,
                                     grad=True)
-    xr16 = oracle.rotate_activations(x, layer.pairs, layer.theta, layer.alpha).astype(np.float16)
+    xr = oracle.rotate_activations(x, layer.pairs, layer.theta, layer.alpha)
     what = oracle.dequantize(q, s, z, 128)
-    w16 = what.astype(np.float16).astype(np.float64)  # as the W4 layer multiplies them
-    yq = (xr16.astype(np.float64) @ w16.T).astype(np.float16).astype(np.float64)
-    dy = 2.0 * (yq - x.astype(np.float64) @ layer.w.astype(np.float64).T)
+    dy = 2.0 * (xr @ what.T - x.astype(np.float64) @ layer.w.astype(np.float64).T)
     e = what - oracle.transform_weights_f64(layer.w, layer.pairs, layer.theta, layer.alpha)
     _, dth2, dal2 = oracle.rotation_backward(x, dy @ e, layer.pairs, layer.theta, layer.alpha)
     assert np.allclose(dth, dth2, rtol=1e-9, atol=1e-9 * np.abs(dth).max())
     assert np.allclose(dal, dal2, rtol=1e-9, atol=1e-9 * np.abs(dal).max())
+
+
+def _fp16_device_layer_loss(x, w, q, s, z, G, layer):
+    """The layer loss as the library documents its arithmetic, simulated in
+    numpy: fp16 X' and dequantized weights, fp32 sums, fp16 Y_q, fp32 Y,
+    dY = 2 (Y_q - Y), and dX' from fp16 dY and E = W_hat - T W with fp32 sums
+    (T W in the canonical fp32 order). Used only to check that the derived
+    tolerance covers that arithmetic."""
+    f32, f16 = np.float32, np.float16
+    xr16 = oracle.rotate_activations(x, layer.pairs, layer.theta, layer.alpha).astype(f16)
+    what = oracle.dequantize(q, s, z, G)
+    yq = (xr16.astype(f32) @ what.astype(f16).astype(f32).T).astype(f16).astype(f32)
+    y = x.astype(f32) @ layer.w.astype(f32).T
+    diff = yq - y
+    loss = float(np.sum(diff.astype(np.float64) ** 2))
+    tw32 = oracle.transform_weights_f32(layer.w, layer.pairs, layer.theta, layer.alpha)
+    e16 = (what.astype(f32) - tw32).astype(f16)
+    dy16 = (f32(2.0) * diff).astype(f16)
+    dxr = dy16.astype(f32) @ e16.astype(f32)
+    _, dth, dal = oracle.rotation_backward(x, dxr, layer.pairs, layer.theta, layer.alpha)
+    return loss, dth, dal
+
+
+@pytest.mark.parametrize("M,d,N,G,K,seed", [(24, 256, 64, 128, 8, 1), (9, 512, 48, 64, 4, 2),
+                                            (40, 256, 32, 256, 8, 3)])
+def test_l_tolerance_covers_fp16_arithmetic_and_rejects_mistakes(M, d, N, G, K, seed):
+    """The derived layer-loss tolerance holds a numpy simulation of the
+    device's documented roundings, and fails planted mistakes: a dropped
+    rounding-free term of the loss, a flipped gradient sign, a gradient taken
+    through W_hat instead of the quantization error, and a transposed pair."""
+    x, layer, _ = synthetic.linear_case(seed=seed, M=M, d=d, N=N, group=G, K=K, bias=False)
+    q, s, z = oracle.quantize_weights(layer.w, G, layer.pairs, layer.theta, layer.alpha)
+    ref = oracle.layer_loss(x, layer.w, q, s, z, G, layer.pairs, layer.theta, layer.alpha, grad=True)
+    tl, tth, tal = metrics.layer_loss_tolerance(x, layer.w, q, s, z, G, layer.pairs, layer.theta,
+                                                layer.alpha)
+    loss, dth, dal = _fp16_device_layer_loss(x, layer.w, q, s, z, G, layer)
+    assert abs(loss - ref[0]) <= tl
+    metrics.assert_within(dth, ref[1], tth, "dtheta")
+    metrics.assert_within(dal, ref[2], tal, "dalpha")
+    # the tolerance is far below the size of a structural mistake
+    assert tl < 0.01 * ref[0]
+    with pytest.raises(AssertionError):
+        metrics.assert_within(-dal, ref[2], tal, "dalpha (sign)")
+    what = oracle.dequantize(q, s, z, G)
+    xr = oracle.rotate_activations(x, layer.pairs, layer.theta, layer.alpha)
+    dy = 2.0 * (xr @ what.T - x.astype(np.float64) @ layer.w.astype(np.float64).T)
+    _, wth, wal = oracle.rotation_backward(x, dy @ what, layer.pairs, layer.theta, layer.alpha)
+    with pytest.raises(AssertionError):
+        metrics.assert_within(wal, ref[2], tal, "dalpha (through W_hat)")
+    swapped = layer.pairs[:, :, ::-1].copy()
+    sth, _ = oracle.layer_loss_gradients(x, layer.w, xr, what, dy, swapped, layer.theta, layer.alpha)
+    with pytest.raises(AssertionError):
+        metrics.assert_within(sth, ref[1], tth, "dtheta (swapped pair)")
