@@ -39,8 +39,10 @@
  * paro_last_error() returns a thread-local message for the last failure.
  *
  * Threads and streams: hot calls (paro_rotate, paro_w4_linear) allocate
- * nothing, do not synchronise and keep no mutable global state; a handle may
- * be used from several threads and streams at once.
+ * nothing, do not synchronise and write no global state (they may be captured
+ * into a HIP graph); a handle may be used from several threads and streams at
+ * once. Per-device set-up that needs allocation and synchronisation happens in
+ * paro_device_init, which paro_rotation_create also runs.
  */
 #ifndef PARO_H
 #define PARO_H
@@ -71,6 +73,20 @@ const char* paro_status_string(int status);
 /* Thread-local detail message of the last failing call on this thread ("" if none). */
 const char* paro_last_error(void);
 
+/*
+ * Per-device set-up (synchronous; allocates, launches and synchronises on the
+ * null stream, so not inside a stream capture). Checks once per device how
+ * workgroups are dispatched to the XCDs (the small-batch linear splits k over
+ * workgroups that must meet in one XCD's L2) and records the result;
+ * idempotent and thread-safe. paro_rotation_create calls it for its device.
+ * A device on which it never ran still gives correct results: the
+ * small-batch linear then exchanges its partial sums through memory-side
+ * (system-scope) accesses, about 15% slower.
+ * Errors: PARO_ERR_HIP (nothing is recorded; a later call tries again),
+ * PARO_ERR_UNSUPPORTED (device ordinal >= 64).
+ */
+int paro_device_init(void);
+
 /* Opaque rotation plan: the K stages of pairs/angles plus alpha for one layer,
  * validated and turned into device tables. Immutable after creation. */
 typedef struct paro_rotation paro_rotation;
@@ -98,6 +114,7 @@ typedef struct paro_rotation paro_rotation;
  *   alpha  host float [d], finite and > 0.
  *   out    receives the handle.
  *
+ * Runs paro_device_init for the current device.
  * Errors: PARO_ERR_NULL, PARO_ERR_SHAPE, PARO_ERR_PAIRING, PARO_ERR_VALUE,
  * PARO_ERR_UNSUPPORTED (group not in {64,128,256}, K > 32, d % 128 != 0,
  * d > 2^24),

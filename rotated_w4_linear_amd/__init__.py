@@ -5,7 +5,7 @@ torch tensors are passed as device pointers plus the current HIP stream, and
 every step of the hot path runs in the library's HIP kernels. There is no
 fallback: if the library is missing or no GPU is visible the calls raise.
 
-Names follow the C ABI: ``paro_rotation_create`` / ``Rotation``,
+Names follow the C ABI: ``paro_device_init``, ``paro_rotation_create`` / ``Rotation``,
 ``paro_rotate``, ``paro_quantize_weights``, ``paro_w4_linear``,
 ``paro_w4_linear_workspace_size``, ``paro_rotation_backward``,
 ``paro_rotation_backward_workspace_size``, ``paro_layer_loss``,
@@ -51,6 +51,8 @@ def load_library() -> ctypes.CDLL:
     lib.paro_status_string.argtypes = [ctypes.c_int]
     lib.paro_last_error.restype = ctypes.c_char_p
     lib.paro_last_error.argtypes = []
+    lib.paro_device_init.restype = ctypes.c_int
+    lib.paro_device_init.argtypes = []
     lib.paro_rotation_create.restype = ctypes.c_int
     lib.paro_rotation_create.argtypes = [c_i64, c_i32, c_i32, vp, vp, vp, ctypes.POINTER(vp)]
     lib.paro_rotation_destroy.restype = None
@@ -115,6 +117,11 @@ def _dptr(t, name, dtype=None):
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def paro_device_init():
+    """Per-device set-up of the current device (``paro_device_init``)."""
+    _check(load_library().paro_device_init())
 
 
 class Rotation:

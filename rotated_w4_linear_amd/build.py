@@ -1,6 +1,8 @@
 """Build the gfx950 shared library ``libparo.so`` in-tree with hipcc.
 
 Usage: ``python -m rotated_w4_linear_amd.build`` (or ``build()`` from Python).
+Each source is compiled to an object of its own (in parallel, under
+``_build/``), then the objects are linked; every call recompiles everything.
 """
 from __future__ import annotations
 
@@ -8,20 +10,25 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libparo.so")
 
 SOURCES = ["api.cpp", "plan.cpp", "rotate.hip", "quantize.hip", "w4_linear.hip", "decode.hip",
            "backward.hip", "layer_loss.hip"]
 
-HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+COMPILE_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off",                         # every rounding is explicit (fma builtins where wanted)
     "-fhip-fp32-correctly-rounded-divide-sqrt",  # IEEE division in the quantizer
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+]
+LINK_FLAGS = [
+    "--offload-arch=gfx950", "-shared", "-fPIC",
     "-Wl,-z,defs",                                # no undefined symbols (e.g. a kernel stub) in the library
     "-L/opt/rocm/lib", "-lrocblas",               # the layer loss's dense products
     "-Wl,-rpath,/opt/rocm/lib",
@@ -35,20 +42,39 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP/C++ source into libparo.so (always recompiles)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(HERE, "..", "include"), *srcs, "-o", tmp]
+def _quiet(stderr: str) -> str:
+    # the host pass does not know the packed-fp32 target feature: harmless
+    return "\n".join(ln for ln in (stderr or "").splitlines() if "packed-fp32-ops" not in ln)
+
+
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    cmd = [hipcc(), *COMPILE_FLAGS, "-I", os.path.join(HERE, "..", "include"), *lang, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(ln for ln in (res.stderr or "").splitlines()
-                    if "packed-fp32-ops" not in ln)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+        raise RuntimeError(f"hipcc failed on {src} ({res.returncode}):\n{_quiet(res.stderr)}")
+    if verbose and _quiet(res.stderr).strip():
+        print(_quiet(res.stderr), file=sys.stderr)
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP/C++ source and link libparo.so (always recompiles)."""
+    os.makedirs(OBJ, exist_ok=True)
+    jobs = max(1, min(len(SOURCES), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(jobs) as pool:
+        objs = list(pool.map(lambda s: _compile(s, verbose), SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *LINK_FLAGS, *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed ({res.returncode}):\n{_quiet(res.stderr)}")
     os.replace(tmp, LIB)
     return LIB
 

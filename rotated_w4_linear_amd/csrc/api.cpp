@@ -94,6 +94,17 @@ int paro_rotation_plan_host(int64_t d, int32_t group, int32_t K, const int32_t* 
   return PARO_OK;
 }
 
+int paro_device_init(void) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "paro_device_init: hipGetDevice");
+  if (dev >= kMaxDevices) {
+    set_error("paro_device_init: device ordinal too large");
+    return PARO_ERR_UNSUPPORTED;
+  }
+  return xcd_dispatch_probe(dev);
+}
+
 int paro_rotation_create(int64_t d, int32_t group, int32_t K, const int32_t* pairs,
                          const float* theta, const float* alpha, paro_rotation** out) {
   if (!out) {
@@ -114,6 +125,10 @@ int paro_rotation_create(int64_t d, int32_t group, int32_t K, const int32_t* pai
   if (e != hipSuccess) {
     free_rotation(r);
     return hip_fail(e, "hipGetDevice");
+  }
+  if ((st = paro_device_init()) != PARO_OK) {
+    free_rotation(r);
+    return st;
   }
   if ((st = upload(&r->d_table, plan.table)) != PARO_OK ||
       (st = upload(&r->d_wt_pairs, plan.wt_pairs)) != PARO_OK ||

@@ -30,10 +30,12 @@
 // agent-scope fence (write-back of the whole L2) costs more than the layer.
 // Workgroup b is dispatched to XCD b % 8, and all k-slices of an n-block get
 // equal b % 8, so they meet in one L2: plain stores, an L2 atomic and loads
-// that skip the per-CU L1 suffice. The library checks that dispatch rule once
-// per device (a probe kernel reads each workgroup's XCC id); where it does not
-// hold, the partial sums and the counter go through memory-side (system
-// scope) stores, loads and atomics instead.
+// that skip the per-CU L1 suffice. paro_device_init (which
+// paro_rotation_create runs too) checks that dispatch rule once per device
+// with a probe kernel that reads each workgroup's XCC id; where it does not
+// hold, or on a device that was never checked, the partial sums and the
+// counter go through memory-side (system scope) stores, loads and atomics
+// instead. The kernel launch itself only reads the recorded result.
 // The rotation is recomputed by each of the N / 128 n-blocks that read a
 // segment: with M <= 16 this is ALU work hidden under the weight loads.
 //
@@ -42,7 +44,9 @@
 // multiply by the fp16 scale rounds once. Nibbles e and e + 4 of a 32-bit word
 // share one packed pair, so the eight codes of a word come out in the k order
 // (0, 4, 1, 5, 2, 6, 3, 7); X' is stored in LDS in the same order.
+#include <atomic>
 #include <mutex>
+#include <string>
 #include <vector>
 
 #include "paro_internal.h"
@@ -355,40 +359,54 @@ __global__ void xcc_probe_kernel(uint32_t* out) {
   if (threadIdx.x == 0) out[blockIdx.x] = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xFu;
 }
 
-// Whether workgroup b runs on the XCD of every other workgroup with the same
-// b % 8 and the eight classes use eight XCDs (the round-robin dispatch the
-// kernel relies on), decided once per device.
-bool xcd_dispatch_is_round_robin() {
+// Per device: 0 = not probed, 1 = workgroup b runs on the XCD of every other
+// workgroup with the same b % 8 and the eight classes use eight XCDs (the
+// round-robin dispatch the kernel relies on), 2 = it does not.
+std::atomic<int> g_xcd_state[kMaxDevices];
+
+}  // namespace
+
+int xcd_dispatch_probe(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return PARO_ERR_UNSUPPORTED;
   static std::mutex mu;
-  static int known[64];
-  static bool value[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
   std::lock_guard<std::mutex> lock(mu);
-  if (known[dev]) return value[dev];
+  if (g_xcd_state[dev].load(std::memory_order_acquire) != 0) return PARO_OK;
   constexpr int kBlocks = 4096;
-  bool ok = false;
   uint32_t* d_out = nullptr;
-  if (hipMalloc(&d_out, kBlocks * sizeof(uint32_t)) == hipSuccess) {
-    std::vector<uint32_t> h(kBlocks, 0xFFFFFFFFu);
-    hipLaunchKernelGGL(xcc_probe_kernel, dim3(kBlocks), dim3(64), 0, 0, d_out);
-    if (hipGetLastError() == hipSuccess &&
-        hipMemcpy(h.data(), d_out, kBlocks * sizeof(uint32_t), hipMemcpyDeviceToHost) == hipSuccess) {
-      ok = true;
-      uint32_t seen = 0;
-      for (int b = 0; b < kBlocks; ++b) {
-        if (h[b] != h[b & 7]) ok = false;
-        if (h[b] < 32) seen |= 1u << h[b];
-        else ok = false;
-      }
-      if (__builtin_popcount(seen) != 8) ok = false;
-    }
-    (void)hipFree(d_out);
+  hipError_t e = hipMalloc(&d_out, kBlocks * sizeof(uint32_t));
+  if (e != hipSuccess) {
+    set_error(std::string("device init: hipMalloc: ") + hipGetErrorString(e));
+    return PARO_ERR_HIP;
   }
-  (void)hipGetLastError();
-  known[dev] = 1;
-  value[dev] = ok;
-  return ok;
+  std::vector<uint32_t> h(kBlocks, 0xFFFFFFFFu);
+  hipLaunchKernelGGL(xcc_probe_kernel, dim3(kBlocks), dim3(64), 0, 0, d_out);
+  e = hipGetLastError();
+  if (e == hipSuccess) e = hipMemcpy(h.data(), d_out, kBlocks * sizeof(uint32_t), hipMemcpyDeviceToHost);
+  (void)hipFree(d_out);
+  if (e != hipSuccess) {  // nothing is cached: a later call probes again
+    set_error(std::string("device init: XCD probe: ") + hipGetErrorString(e));
+    return PARO_ERR_HIP;
+  }
+  bool ok = true;
+  uint32_t seen = 0;
+  for (int b = 0; b < kBlocks; ++b) {
+    if (h[b] != h[b & 7]) ok = false;
+    if (h[b] < 32) seen |= 1u << h[b];
+    else ok = false;
+  }
+  if (__builtin_popcount(seen) != 8) ok = false;
+  g_xcd_state[dev].store(ok ? 1 : 2, std::memory_order_release);
+  return PARO_OK;
+}
+
+namespace {
+
+// The hot path only reads what the probe recorded; a device never probed
+// takes the memory-side path, which is correct under any dispatch.
+bool xcd_dispatch_is_round_robin() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+  return g_xcd_state[dev].load(std::memory_order_acquire) == 1;
 }
 
 template <bool ROT, int KMAX, bool KEXACT, bool FAST, int T, int TJ, bool SZV>

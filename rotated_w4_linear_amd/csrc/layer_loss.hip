@@ -131,10 +131,13 @@ LossLayout loss_layout(const paro_rotation* r, int64_t M, int64_t N, int64_t d, 
     off += a256(bytes);
     return o;
   };
+  // the W4 linear's workspace first: its arrival counters then sit at offset 0
+  // for every M and N, so a workspace reused with other sizes still finds
+  // them zero
+  L.w4 = take(paro_w4_linear_workspace_size(nullptr, M, N, d));
   L.xr = take((size_t)M * d * 2);
   L.yq = take((size_t)M * N * 2);
   L.y = take((size_t)M * N * 4);
-  L.w4 = take(paro_w4_linear_workspace_size(nullptr, M, N, d));
   L.part = take((size_t)kLossBlocks * 4);
   if (grad) {
     L.dxr = take((size_t)M * d * 4);

@@ -129,6 +129,11 @@ hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint1
 constexpr size_t kDecodeCounterBytes = 16384;
 constexpr int64_t kDecodeMaxM = 16;
 bool decode_fuses_rotation(const paro_rotation* r);
+// Devices the library keeps per-device state for (device ordinals below this).
+constexpr int kMaxDevices = 64;
+// Runs the XCD dispatch probe on device dev (current) once and records the
+// result; allocates, launches and synchronizes. Returns a paro_status.
+int xcd_dispatch_probe(int dev);
 hipError_t launch_w4_decode(const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
                             const uint8_t* zeros, const uint16_t* bias, uint16_t* y, int64_t M,
                             int64_t N, int64_t d, int group, const paro_rotation* r, void* ws,

@@ -171,6 +171,18 @@ def test_rotate_sweep_full_size(paro, point):
     check_rotation(paro, x, layer, rows=rows)
 
 
+@pytest.mark.parametrize("which", ["mlp", "down"])
+def test_rotate_prefill_configs_sampled(paro, which):
+    """X' of the prefill configurations' own inputs (MLP: 8192 x 4096, N(0, 1)
+    with 1 % outlier channels; down-proj: 2048 x 14336, Student-t(3)) at the
+    full-size launch, 2e-3 on 128 sampled rows including the last."""
+    x, layer = synthetic.prefill_mlp() if which == "mlp" else synthetic.prefill_down()
+    log(f"rotate prefill {which} {x.shape[0]}x{x.shape[1]} (sampled rows)")
+    rows = np.sort(synthetic.rng_for(3100, 0 if which == "mlp" else 1).choice(x.shape[0], 128, replace=False))
+    rows[-1] = x.shape[0] - 1
+    check_rotation(paro, x, layer, rows=rows)
+
+
 # ----------------------------------------------------------------------------
 # quantization
 # ----------------------------------------------------------------------------
@@ -504,6 +516,31 @@ def test_linear_prefill_down_sampled(paro):
     check_linear(paro, x, layer, rows=rows)
 
 
+@pytest.mark.parametrize("index", list(range(7)))
+def test_decoder_chain_linear(paro, index):
+    """One linear of the Llama-3-8B decoder-layer chain (q, k, v, o, gate, up,
+    down; each with its own rotation, group 128, K = 8) at M = 1, 16 and 2048
+    tokens, rotated W4 against the oracle: every row at M <= 16, 24 sampled
+    rows (including the last) at M = 2048."""
+    name, layer = synthetic.decoder_layer()[index]
+    N, d = layer.w.shape
+    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, 128)
+    qw, s, z = paro.paro_quantize_weights(r, dev(layer.w), 128)
+    qh, sh, zh = host(qw), host(s), host(z)
+    for M in (1, 16, 2048):
+        log(f"chain {name} {d}->{N} M={M}")
+        x = synthetic.decoder_x(index, M)
+        y = host(paro.paro_w4_linear(r, dev(x), qw, s, z))
+        rows = np.arange(M)
+        if M > 16:
+            rows = np.sort(synthetic.rng_for(3600, index).choice(M, 24, replace=False))
+            rows[-1] = M - 1
+        ref = oracle.rotated_w4_linear(x[rows], qh, sh, zh, 128, layer.pairs, layer.theta, layer.alpha)
+        fro, mx = metrics.assert_linear_close(y[rows], ref)
+        log(f"  rel-Frobenius {fro:.2e}, max {mx:.2e}")
+    r.close()
+
+
 # ----------------------------------------------------------------------------
 # gradients of the transform
 # ----------------------------------------------------------------------------
@@ -615,22 +652,11 @@ def test_backward_prefill_layer(paro, side):
 # layer-wise output loss and its straight-through gradients
 # ----------------------------------------------------------------------------
 
-# The device's X' and Y_q are its own fp16 roundings of values that agree with
-# the oracle's to fp32 accuracy. Where an exact value lies within that of an
-# fp16 rounding boundary, the two round differently; the loss barely moves
-# (held to 1e-3 relative), but the straight-through gradients depend on those
-# decisions: re-running the oracle with X' perturbed before its rounding by
-# the fp32 error bound of the transform (24 2^-24 of the group's rms) moves
-# the angle gradients by 0.05-0.4% (floored at their rms); measured device
-# errors are 2e-5 to 1e-3. These cases are held to 1e-2, which still fails a
-# wrong sign, stage, pair or term (errors of order one). In the exact cases
-# (angles 0, so the stages are identities that still carry angle gradients,
-# and power-of-two scales, so X' = X / alpha is exact in fp16) only Y_q's own
-# rounding can fall differently (fp32 sums in another order than the
-# oracle's fp64); they are held to 5e-3.
-LOSS_TOL = 1e-3
-ROUNDING_SENSITIVE_GRAD_TOL = 1e-2
-EXACT_GRAD_TOL = 5e-3
+# The oracle's layer loss is the plain fp64 definition. The device rounds X',
+# each dequantized weight and Y_q to fp16 (and the operands of dY E), so its
+# loss and gradients are held to per-value tolerances derived from those
+# rounding points (metrics.layer_loss_tolerance: six standard deviations of
+# the rounding noise plus the fp32 gradient arithmetic's 1e-4).
 
 
 def check_layer_loss(paro, M, d, N, G, K, seed, gradients=True, keep=1.0, exact=False):
@@ -648,15 +674,16 @@ def check_layer_loss(paro, M, d, N, G, K, seed, gradients=True, keep=1.0, exact=
                             grad=gradients)
     rl = ref[0] if gradients else ref
     got = float(host(loss)[0])
-    log(f"  loss {got:.7g} vs {rl:.7g}")
-    assert abs(got - rl) <= LOSS_TOL * abs(rl), f"loss {got} vs {rl}"
+    tl, tth, tal = metrics.layer_loss_tolerance(x, layer.w, qh, sh, zh, G, layer.pairs, layer.theta,
+                                                layer.alpha, seed=seed)
+    log(f"  loss {got:.7g} vs {rl:.7g} (tolerance {tl:.3g})")
+    assert abs(got - rl) <= tl, f"loss {got} vs {rl}, tolerance {tl}"
     if gradients:
-        tol = EXACT_GRAD_TOL if exact else ROUNDING_SENSITIVE_GRAD_TOL
         if K:
-            e = metrics.assert_grad_close(host(dth), ref[1], "dtheta", tol=tol)
-            log(f"  dtheta err {e:.3e}")
-        e = metrics.assert_grad_close(host(dal), ref[2], "dalpha", tol=tol)
-        log(f"  dalpha err {e:.3e}")
+            e = metrics.assert_within(host(dth), ref[1], tth, "dtheta")
+            log(f"  dtheta error / tolerance {e:.3f}")
+        e = metrics.assert_within(host(dal), ref[2], tal, "dalpha")
+        log(f"  dalpha error / tolerance {e:.3f}")
     r.close()
     return got, rl
 
@@ -671,8 +698,8 @@ def test_layer_loss_and_gradients(paro, M, d, N, G, K):
 
 @pytest.mark.parametrize("M,d,N,G", [(37, 256, 64, 128), (9, 512, 96, 128), (140, 512, 128, 64)])
 def test_layer_loss_exact_case(paro, M, d, N, G):
-    """Angles 0 and power-of-two scales: X' is exact, so only Y_q's rounding can
-    fall differently; loss to 1e-3, gradients to 5e-3."""
+    """Angles 0 (identity stages that still carry angle gradients) and
+    power-of-two scales (X' = X / alpha exact in fp16)."""
     log(f"layer loss, exact case M={M} d={d} N={N} G={G}")
     check_layer_loss(paro, M, d, N, G, 8, seed=M + d, exact=True)
 
@@ -690,3 +717,28 @@ def test_layer_loss_empty(paro):
     e = torch.empty((0, 256), dtype=torch.float16, device="cuda")
     loss, dth, dal = paro.paro_layer_loss(r, e, dev(layer.w), qw, s, z)
     assert float(host(loss)[0]) == 0.0 and not host(dth).any() and not host(dal).any()
+
+
+def test_layer_loss_workspace_reused_across_sizes(paro):
+    """One zero-filled workspace serves a call at M = 16 and then one at M = 8
+    (d = 1024: the small-batch linear splits k, so its arrival counters are
+    used): both results hold and the counters are left at zero."""
+    d, N, G = 1024, 256, 128
+    x, layer, _ = synthetic.linear_case(seed=71, M=16, d=d, N=N, group=G, K=8, bias=False)
+    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, G)
+    qw, s, z = paro.paro_quantize_weights(r, dev(layer.w), G)
+    qh, sh, zh = host(qw), host(s), host(z)
+    need = max(paro.load_library().paro_layer_loss_workspace_size(r.handle, M, N, d, 1) for M in (16, 8))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for M in (16, 8):
+        log(f"layer loss, shared workspace, M={M}")
+        loss, dth, dal = paro.paro_layer_loss(r, dev(x[:M]), dev(layer.w), qw, s, z, workspace=ws)
+        ref = oracle.layer_loss(x[:M], layer.w, qh, sh, zh, G, layer.pairs, layer.theta, layer.alpha,
+                                grad=True)
+        tl, tth, tal = metrics.layer_loss_tolerance(x[:M], layer.w, qh, sh, zh, G, layer.pairs,
+                                                    layer.theta, layer.alpha, seed=M)
+        assert abs(float(host(loss)[0]) - ref[0]) <= tl
+        metrics.assert_within(host(dth), ref[1], tth, "dtheta")
+        metrics.assert_within(host(dal), ref[2], tal, "dalpha")
+        assert not host(ws[:16384]).any(), "arrival counters not left at zero"
+    r.close()
