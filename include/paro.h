@@ -224,6 +224,33 @@ int paro_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qwe
                    uint16_t* y, int64_t M, int64_t N, int64_t d, int32_t group,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * paro_w4_linear for callers that cannot allocate device memory (code under
+ * HIP-graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels, arguments and result as paro_w4_linear, with the
+ * workspace taken from a static device array inside the library instead of a
+ * caller's buffer. The call allocates and frees nothing.
+ *
+ *   Scratch: (64 MiB + 16 KiB) per device, held from the library's load until
+ *            the process ends; its address is looked up and its arrival
+ *            counters cleared by paro_device_init (paro_rotation_create runs
+ *            it), and every completed call leaves the counters zero again.
+ *   Limit:   paro_w4_linear_workspace_size(r, M, N, d) must not exceed that
+ *            size (for example M x d <= 32 Mi elements for a rotated layer
+ *            with M > 16), else PARO_ERR_WORKSPACE and nothing is enqueued.
+ *   Sharing: every call on one device uses that device's single array, so
+ *            calls that may run at the same time on one device (several
+ *            streams or threads) race and give wrong results: serialise them,
+ *            or use paro_w4_linear with a workspace per stream.
+ * Errors: those of paro_w4_linear, PARO_ERR_WORKSPACE (too large, see
+ * above), PARO_ERR_UNSUPPORTED (paro_device_init has not run on the current
+ * device).
+ */
+int paro_w4_linear_noalloc(const paro_rotation* r, const uint16_t* x, const uint8_t* qweight,
+                           const uint16_t* scales, const uint8_t* zeros, const uint16_t* bias,
+                           uint16_t* y, int64_t M, int64_t N, int64_t d, int32_t group,
+                           hipStream_t stream);
+
 /* Which transform paro_rotation_backward differentiates. */
 typedef enum {
   PARO_SIDE_ACTIVATION = 0, /* X' = X T^-1, as paro_rotate computes it */

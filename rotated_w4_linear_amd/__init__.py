@@ -7,7 +7,7 @@ fallback: if the library is missing or no GPU is visible the calls raise.
 
 Names follow the C ABI: ``paro_device_init``, ``paro_rotation_create`` / ``Rotation``,
 ``paro_rotate``, ``paro_quantize_weights``, ``paro_w4_linear``,
-``paro_w4_linear_workspace_size``, ``paro_rotation_backward``,
+``paro_w4_linear_workspace_size``, ``paro_w4_linear_noalloc``, ``paro_rotation_backward``,
 ``paro_rotation_backward_workspace_size``, ``paro_layer_loss``,
 ``paro_layer_loss_workspace_size``.
 """
@@ -69,6 +69,9 @@ def load_library() -> ctypes.CDLL:
     lib.paro_w4_linear.restype = ctypes.c_int
     lib.paro_w4_linear.argtypes = [vp, vp, vp, vp, vp, vp, vp, c_i64, c_i64, c_i64, c_i32, vp,
                                    c_size, vp]
+    lib.paro_w4_linear_noalloc.restype = ctypes.c_int
+    lib.paro_w4_linear_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, c_i64, c_i64, c_i64, c_i32,
+                                           vp]
     lib.paro_rotation_backward_workspace_size.restype = c_size
     lib.paro_rotation_backward_workspace_size.argtypes = [vp, c_i64]
     lib.paro_rotation_backward.restype = ctypes.c_int
@@ -213,6 +216,21 @@ def paro_w4_linear(r: Optional[Rotation], x, qweight, scales, zeros, bias=None, 
         _dptr(scales, "scales", torch.float16), _dptr(zeros, "zeros", torch.uint8),
         _dptr(bias, "bias", torch.float16) if bias is not None else None,
         _dptr(y, "y", torch.float16), M, N, d, group, ws_ptr, ws_bytes, _stream(stream)))
+    return y
+
+
+def paro_w4_linear_noalloc(r: Optional[Rotation], x, qweight, scales, zeros, y, bias=None,
+                           group: int = 128, stream=None):
+    """``paro_w4_linear`` on the library's static scratch: ``y`` (fp16 [M][N])
+    is written in place and nothing is allocated."""
+    import torch
+    M, d = x.shape
+    N = qweight.shape[0]
+    _check(load_library().paro_w4_linear_noalloc(
+        _handle(r), _dptr(x, "x", torch.float16), _dptr(qweight, "qweight", torch.uint8),
+        _dptr(scales, "scales", torch.float16), _dptr(zeros, "zeros", torch.uint8),
+        _dptr(bias, "bias", torch.float16) if bias is not None else None,
+        _dptr(y, "y", torch.float16), M, N, d, group, _stream(stream)))
     return y
 
 

@@ -102,7 +102,9 @@ int paro_device_init(void) {
     set_error("paro_device_init: device ordinal too large");
     return PARO_ERR_UNSUPPORTED;
   }
-  return xcd_dispatch_probe(dev);
+  int st = xcd_dispatch_probe(dev);
+  if (st == PARO_OK) st = noalloc_scratch_setup(dev);
+  return st;
 }
 
 int paro_rotation_create(int64_t d, int32_t group, int32_t K, const int32_t* pairs,
@@ -239,56 +241,65 @@ size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t 
   return kDecodeCounterBytes + round256((size_t)M * (size_t)d * 2);
 }
 
-int paro_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qweight,
-                   const uint16_t* scales, const uint8_t* zeros, const uint16_t* bias,
-                   uint16_t* y, int64_t M, int64_t N, int64_t d, int32_t group,
-                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace paro {
+namespace {
+
+// Argument checks shared by paro_w4_linear and paro_w4_linear_noalloc
+// (everything but the workspace). Returns PARO_OK, or an error with the
+// message set; *noop is set when M == 0 (nothing to do).
+int check_w4_linear(const char* fn, const paro_rotation* r, const uint16_t* x,
+                    const uint8_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                    const uint16_t* bias, const uint16_t* y, int64_t M, int64_t N, int64_t d,
+                    int32_t group, bool* noop) {
+  *noop = false;
+  const std::string f(fn);
   if (M < 0 || N <= 0 || d <= 0) {
-    set_error("paro_w4_linear: bad sizes");
+    set_error(f + ": bad sizes");
     return PARO_ERR_SHAPE;
   }
   if (group != 64 && group != 128 && group != 256) {
-    set_error("paro_w4_linear: group must be 64, 128 or 256");
+    set_error(f + ": group must be 64, 128 or 256");
     return PARO_ERR_UNSUPPORTED;
   }
   if (N % 16 || d % 128 || d % group) {
-    set_error("paro_w4_linear: N must be a multiple of 16, d of 128 and of group");
+    set_error(f + ": N must be a multiple of 16, d of 128 and of group");
     return PARO_ERR_SHAPE;
   }
   // (the kernels address one tile of rows with 32-bit byte offsets)
   if (N > (int64_t(1) << 30) || d > (int64_t(1) << 22) || M > (int64_t(1) << 31) / 2) {
-    set_error("paro_w4_linear: sizes too large (N <= 2^30, d <= 2^22, M < 2^30)");
+    set_error(f + ": sizes too large (N <= 2^30, d <= 2^22, M < 2^30)");
     return PARO_ERR_UNSUPPORTED;
   }
   if (r && (r->d != d || r->group != group)) {
-    set_error("paro_w4_linear: d or group differs from the rotation plan");
+    set_error(f + ": d or group differs from the rotation plan");
     return PARO_ERR_SHAPE;
   }
-  if (M == 0) return PARO_OK;
+  if (M == 0) {
+    *noop = true;
+    return PARO_OK;
+  }
   if (!x || !qweight || !scales || !zeros || !y) {
-    set_error("paro_w4_linear: NULL tensor");
+    set_error(f + ": NULL tensor");
     return PARO_ERR_NULL;
   }
   if (!aligned16(x) || !aligned16(qweight) || !aligned16(y) || (bias && ((uintptr_t)bias & 7))) {
-    set_error("paro_w4_linear: x, qweight, y must be 16-byte aligned (bias 8-byte)");
+    set_error(f + ": x, qweight, y must be 16-byte aligned (bias 8-byte)");
     return PARO_ERR_ALIGN;
   }
   if (M <= kDecodeMaxM && (uint64_t)((d / 128 + 3) / 4) * (uint64_t)M * (uint64_t)N * 4 >= (1ull << 31)) {
-    set_error("paro_w4_linear: ceil(d / 512) * M * N * 4 must be below 2^31 for M <= 16");
+    set_error(f + ": ceil(d / 512) * M * N * 4 must be below 2^31 for M <= 16");
     return PARO_ERR_UNSUPPORTED;
   }
-  const size_t need = paro_w4_linear_workspace_size(r, M, N, d);
-  if (need) {
-    if (!workspace || workspace_bytes < need) {
-      set_error("paro_w4_linear: workspace missing or smaller than paro_w4_linear_workspace_size");
-      return PARO_ERR_WORKSPACE;
-    }
-    if ((uintptr_t)workspace & 255) {
-      set_error("paro_w4_linear: workspace must be 256-byte aligned");
-      return PARO_ERR_ALIGN;
-    }
-  }
-  char* ws = (char*)workspace;
+  return PARO_OK;
+}
+
+// The launches of the W4 linear on a checked workspace of `need` bytes.
+int run_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qweight,
+                  const uint16_t* scales, const uint8_t* zeros, const uint16_t* bias, uint16_t* y,
+                  int64_t M, int64_t N, int64_t d, int32_t group, char* ws, size_t need,
+                  hipStream_t stream) {
   hipError_t e = hipSuccess;
   if (M <= kDecodeMaxM) {
     const paro_rotation* fused = r;
@@ -315,6 +326,61 @@ int paro_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qwe
   if (e != hipSuccess) return hip_fail(e, "paro_w4_linear launch");
   return PARO_OK;
 }
+
+}  // namespace
+}  // namespace paro
+
+extern "C" {
+
+int paro_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qweight,
+                   const uint16_t* scales, const uint8_t* zeros, const uint16_t* bias,
+                   uint16_t* y, int64_t M, int64_t N, int64_t d, int32_t group,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  bool noop = false;
+  int st = check_w4_linear("paro_w4_linear", r, x, qweight, scales, zeros, bias, y, M, N, d, group,
+                           &noop);
+  if (st != PARO_OK || noop) return st;
+  const size_t need = paro_w4_linear_workspace_size(r, M, N, d);
+  if (need) {
+    if (!workspace || workspace_bytes < need) {
+      set_error("paro_w4_linear: workspace missing or smaller than paro_w4_linear_workspace_size");
+      return PARO_ERR_WORKSPACE;
+    }
+    if ((uintptr_t)workspace & 255) {
+      set_error("paro_w4_linear: workspace must be 256-byte aligned");
+      return PARO_ERR_ALIGN;
+    }
+  }
+  return run_w4_linear(r, x, qweight, scales, zeros, bias, y, M, N, d, group, (char*)workspace,
+                       need, stream);
+}
+
+int paro_w4_linear_noalloc(const paro_rotation* r, const uint16_t* x, const uint8_t* qweight,
+                           const uint16_t* scales, const uint8_t* zeros, const uint16_t* bias,
+                           uint16_t* y, int64_t M, int64_t N, int64_t d, int32_t group,
+                           hipStream_t stream) {
+  bool noop = false;
+  int st = check_w4_linear("paro_w4_linear_noalloc", r, x, qweight, scales, zeros, bias, y, M, N, d,
+                           group, &noop);
+  if (st != PARO_OK || noop) return st;
+  const size_t need = paro_w4_linear_workspace_size(r, M, N, d);
+  if (need > kNoallocScratchBytes) {
+    set_error("paro_w4_linear_noalloc: these sizes need " + std::to_string(need) +
+              " bytes of workspace, more than the static scratch's " +
+              std::to_string(kNoallocScratchBytes));
+    return PARO_ERR_WORKSPACE;
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "paro_w4_linear_noalloc: hipGetDevice");
+  char* ws = (char*)noalloc_scratch(dev);
+  if (!ws) {
+    set_error("paro_w4_linear_noalloc: paro_device_init has not run on this device");
+    return PARO_ERR_UNSUPPORTED;
+  }
+  return run_w4_linear(r, x, qweight, scales, zeros, bias, y, M, N, d, group, ws, need, stream);
+}
+
 
 size_t paro_rotation_backward_workspace_size(const paro_rotation* r, int64_t M) {
   if (!r || M <= 0) return 0;

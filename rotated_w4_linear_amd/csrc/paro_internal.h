@@ -134,6 +134,14 @@ constexpr int kMaxDevices = 64;
 // Runs the XCD dispatch probe on device dev (current) once and records the
 // result; allocates, launches and synchronizes. Returns a paro_status.
 int xcd_dispatch_probe(int dev);
+
+// Static device scratch of paro_w4_linear_noalloc (noalloc.hip): its size,
+// the once-per-device look-up of its address (with dev current; clears the
+// arrival counters and synchronizes) and the recorded address (NULL before
+// set-up).
+constexpr size_t kNoallocScratchBytes = (size_t(64) << 20) + kDecodeCounterBytes;
+int noalloc_scratch_setup(int dev);
+void* noalloc_scratch(int dev);
 hipError_t launch_w4_decode(const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
                             const uint8_t* zeros, const uint16_t* bias, uint16_t* y, int64_t M,
                             int64_t N, int64_t d, int group, const paro_rotation* r, void* ws,

@@ -25,6 +25,7 @@ torch = pytest.importorskip("torch")
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 CHILD = r"""
+import gc
 import sys
 import numpy as np
 import torch
@@ -41,6 +42,7 @@ print("child: plain W4, first small-batch call inside a capture", flush=True)
 qw, s, z = paro.paro_quantize_weights(None, wd, 128)  # offline; does not set the device up
 ws = paro.new_workspace(None, M, N, d)
 y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+gc.collect()
 torch.cuda.synchronize()
 g = torch.cuda.CUDAGraph()
 with torch.cuda.graph(g):
@@ -63,6 +65,7 @@ r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, 128)
 qr, sr, zr = paro.paro_quantize_weights(r, wd, 128)
 ws2 = paro.new_workspace(r, M, N, d)
 y2 = torch.empty((M, N), dtype=torch.float16, device="cuda")
+gc.collect()
 torch.cuda.synchronize()
 g2 = torch.cuda.CUDAGraph()
 with torch.cuda.graph(g2):
