@@ -636,7 +636,6 @@ def bench_calib(args, paro, torch):
         out[grads] = (ms, float(res[0].item()))
         log(f"[calib] gradients={grads}: {ms:.3f} ms per step, loss {out[grads][1]:.6g}")
     ms, loss = out[True]
-    flops = 2.0 * M * N * d * 2 + 2.0 * M * N * d  # X W^T, dY E (fp32), the W4 layer
     return {
         "metric": "transform-learning step: layer loss + angle/scale gradients (ms)", "value": round(ms, 4),
         "unit": "ms", "n_gpus": 1, "steps": max(args.steps, 10), "warmup": args.warmup,
@@ -646,7 +645,8 @@ def bench_calib(args, paro, torch):
         "loss_only_ms": round(out[False][0], 4), "loss": loss,
         "calibration_tokens_per_s": round(M / (ms * 1e-3), 1),
         "roofline": None,
-        "note": "three dense products per step (X W^T fp16, dY E fp32, the W4 layer); "
+        "note": "three matrix-core products per step, all in this library (the W4 layer; X W^T "
+                "with the loss and dY in its epilogue; dY E from fp16 operands, fp32 out); "
                 "per-kernel durations in the committed rocprofv3 summary",
     }
 

@@ -329,21 +329,22 @@ size_t paro_layer_loss_workspace_size(const paro_rotation* r, int64_t M, int64_t
  * times larger than the result. E comes from the quantizer's own pass over
  * T W, with W_hat from the codes that pass produces; these equal qweight,
  * scales and zeros bit for bit when those are Q(T W) of this plan, as
- * required above.
+ * required above. dY and E enter that product rounded to fp16, with fp32
+ * sums.
  *
  *   x        device fp16 [M][d], w device fp16 [N][d] (16-byte aligned);
  *   qweight, scales, zeros: as for paro_w4_linear, with the plan's group;
- *   loss     device fp32 [1] (the sum is taken in a fixed order, fp64 at the end);
+ *   loss     device fp32 [1] (per-tile sums in a fixed order, fp64 at the end);
  *   dtheta   device fp32 [K][d/2] or NULL; dalpha device fp32 [d] or NULL;
  *   N % 16 == 0, 0 <= M, N < 2^30; M == 0 writes zeros.
  *   workspace: at least paro_layer_loss_workspace_size(r, M, N, d, dtheta ||
  *            dalpha) bytes, 256-byte aligned, zero-filled once after
- *            allocation (it holds paro_w4_linear's arrival counters for
- *            M <= 16, which every call leaves zero).
- * The dense products go to rocBLAS, through one handle per device created on
- * first use and kept for the process; calls on one device from several host
- * threads at the same time are not supported (rocBLAS handles are not
- * thread-safe). Everything else runs in this library's kernels.
+ *            allocation (its first 16 KiB hold paro_w4_linear's arrival
+ *            counters for M <= 16, which every call leaves zero, whatever M
+ *            and N the workspace is reused with). Calls that may run at the
+ *            same time need different workspaces.
+ * Every step runs in this library's kernels (the dense products on the
+ * matrix cores); the call allocates nothing and does not synchronise.
  * Errors: PARO_ERR_NULL, PARO_ERR_SHAPE, PARO_ERR_ALIGN, PARO_ERR_WORKSPACE,
  * PARO_ERR_HIP, and those of paro_w4_linear.
  */

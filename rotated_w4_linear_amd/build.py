@@ -18,7 +18,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libparo.so")
 
 SOURCES = ["api.cpp", "plan.cpp", "rotate.hip", "quantize.hip", "w4_linear.hip", "decode.hip",
-           "backward.hip", "layer_loss.hip", "noalloc.hip"]
+           "backward.hip", "layer_loss.hip", "noalloc.hip", "dense_gemm.hip"]
 
 COMPILE_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -30,8 +30,6 @@ COMPILE_FLAGS = [
 LINK_FLAGS = [
     "--offload-arch=gfx950", "-shared", "-fPIC",
     "-Wl,-z,defs",                                # no undefined symbols (e.g. a kernel stub) in the library
-    "-L/opt/rocm/lib", "-lrocblas",               # the layer loss's dense products
-    "-Wl,-rpath,/opt/rocm/lib",
 ]
 
 

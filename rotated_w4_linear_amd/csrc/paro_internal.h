@@ -110,13 +110,30 @@ namespace paro {
 // Kernel launchers (defined in the .hip files). Return hipError_t of the launch.
 hipError_t launch_rotate(const paro_rotation* r, const uint16_t* x, uint16_t* y, int64_t M,
                          hipStream_t stream);
-// ehi, elo (both NULL or both set, 4-byte aligned): also writes the
-// quantization error E = W_hat - T W [N][d] (W_hat = (q - z) s) as bf16 high
-// and low parts, hi = bf16(E), lo = bf16(E - hi)
+// err (NULL or 4-byte aligned): also writes the quantization error
+// E = W_hat - T W [N][d] (W_hat = (q - z) s, T W in the canonical fp32 order)
+// rounded to fp16
 hipError_t launch_quantize(const paro_rotation* r, const uint16_t* w, int64_t N, int64_t d,
                            int group, uint8_t* qweight, uint16_t* scales, uint8_t* zeros,
-                           int* d_flag, hipStream_t stream, uint16_t* ehi = nullptr,
-                           uint16_t* elo = nullptr);
+                           int* d_flag, hipStream_t stream, uint16_t* err = nullptr);
+// Dense fp16 "NT" products (dense_gemm.hip), C[m][n] = sum_k A[m][k] B[n][k]
+// with fp32 accumulation; K % 64 == 0, row strides in elements, 16-byte
+// aligned rows.
+//  * launch_nt_gemm_f32: C fp32 [M][ldc].
+//  * launch_nt_gemm_loss: A = x [M][d], B = w [N][d]; part[nt_tiles(M, N)]
+//    receives the per-tile sums of (yq - x w^T)^2 (yq fp16 [M][N]) and, with dy
+//    != NULL, dy [M][ldd] = fp16(2 (yq - x w^T)), zero in columns N .. ldd - 1.
+//  * launch_transpose_pad: out [C][ldo] = in^T for in fp16 [R][C] (C even,
+//    ldo even, ldo >= R), zero in columns R .. ldo - 1.
+int nt_tiles(int64_t M, int64_t N);
+hipError_t launch_nt_gemm_f32(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb,
+                              int64_t M, int64_t N, int64_t K, float* c, int64_t ldc,
+                              hipStream_t stream);
+hipError_t launch_nt_gemm_loss(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N, int64_t d,
+                               const uint16_t* yq, uint16_t* dy, int64_t ldd, float* part,
+                               hipStream_t stream);
+hipError_t launch_transpose_pad(const uint16_t* in, int64_t R, int64_t C, uint16_t* out, int64_t ldo,
+                                hipStream_t stream);
 // Large-batch linear (M > 16) on already transformed activations.
 hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
                           const uint8_t* zeros, const uint16_t* bias, uint16_t* y, int64_t M,

@@ -24,13 +24,6 @@
 namespace paro {
 namespace {
 
-// Round to the nearest bfloat16, ties to even (finite inputs).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
 // Wave-wide min, max and or, exact in any order: within each row of 16 lanes
 // by DPP moves (lane i with i ^ 1, i ^ 2, its mirror in the half row and in
 // the row), then the four rows' values read from lanes 0, 16, 32 and 48.
@@ -78,7 +71,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     const uint32_t* __restrict__ wt_pairs, const float* __restrict__ wt_c,
     const float* __restrict__ wt_s, const float* __restrict__ alpha, uint8_t* __restrict__ qweight,
     uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros, int* __restrict__ flag,
-    uint16_t* __restrict__ ehi, uint16_t* __restrict__ elo) {
+    uint16_t* __restrict__ err) {
   __shared__ float buf[4][256];
   constexpr int SL = 128;  // floats between the two items' slices (NI = 2)
   const int lane = threadIdx.x & 63;
@@ -213,17 +206,14 @@ __global__ __launch_bounds__(256) void quantize_kernel(
           const float q1f = fminf(fmaxf(rintf(u[SL * q + 2 * b + 1] / sq) + zf, 0.0f), 15.0f);
           const uint32_t q0 = (uint32_t)q0f, q1 = (uint32_t)q1f;
           qweight[nq * (d / 2) + gq * half + b] = (uint8_t)(q0 | (q1 << 4));
-          if (ehi) {
+          if (err) {
             // the quantization error E = (q - z) s - T W ((q - z) s is exact in
-            // fp32), as bf16 high and low parts
+            // fp32), rounded once to fp16
             const float e0 = (q0f - zf) * sq - u[SL * q + 2 * b];
             const float e1 = (q1f - zf) * sq - u[SL * q + 2 * b + 1];
-            const uint32_t h0 = bf16_rne(e0), h1 = bf16_rne(e1);
-            const uint32_t l0 = bf16_rne(e0 - __builtin_bit_cast(float, h0 << 16));
-            const uint32_t l1 = bf16_rne(e1 - __builtin_bit_cast(float, h1 << 16));
-            const int64_t o = nq * d + gq * G + 2 * b;
-            *(uint32_t*)(ehi + o) = h0 | (h1 << 16);
-            *(uint32_t*)(elo + o) = l0 | (l1 << 16);
+            const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)e0);
+            const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)e1);
+            *(uint32_t*)(err + nq * d + gq * G + 2 * b) = h0 | (h1 << 16);
           }
         }
         if (lane == 0) {
@@ -243,7 +233,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(
 
 hipError_t launch_quantize(const paro_rotation* r, const uint16_t* w, int64_t N, int64_t d,
                            int group, uint8_t* qweight, uint16_t* scales, uint8_t* zeros,
-                           int* d_flag, hipStream_t stream, uint16_t* ehi, uint16_t* elo) {
+                           int* d_flag, hipStream_t stream, uint16_t* err) {
   const int64_t total = N * (d / group);
   if (total == 0) return hipSuccess;
   const int ni = group <= 128 ? 2 : 1;
@@ -253,7 +243,7 @@ hipError_t launch_quantize(const paro_rotation* r, const uint16_t* w, int64_t N,
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, stream, w, N, d, group,
                      r ? r->K : 0, r ? r->d_wt_pairs : nullptr, r ? r->d_wt_c : nullptr,
                      r ? r->d_wt_s : nullptr, r ? r->d_alpha : nullptr, qweight, scales, zeros,
-                     d_flag, ehi, elo);
+                     d_flag, err);
   return hipGetLastError();
 }
 
