@@ -155,7 +155,12 @@ int paro_rotate(const paro_rotation* r, const uint16_t* x, uint16_t* y, int64_t 
  *            transpose of the math W whose rows are input channels).
  *   group    quantization group along d: 64, 128 or 256; with r != NULL it
  *            must equal the plan's group.
- *   qweight  device uint8 [N][d/2]: byte b of a row = code(2b) | code(2b+1) << 4.
+ *   qweight  device uint8 [N][d/2]: each 4 bytes (a little-endian 32-bit
+ *            word) hold the codes c0 .. c7 of 8 consecutive channels, the even
+ *            channels in the low 16 bits and the odd ones in the high 16 bits,
+ *            4 bits each in channel order: bytes c0 | c2 << 4, c4 | c6 << 4,
+ *            c1 | c3 << 4, c5 | c7 << 4 (so that two codes at a time unpack
+ *            into an fp16 pair with one AND-OR).
  *   scales   device fp16 [N][d/group].
  *   zeros    device uint8 [N][d/group], values 0..15.
  *
@@ -352,6 +357,60 @@ int paro_layer_loss(const paro_rotation* r, const uint16_t* x, const uint16_t* w
                     const uint8_t* qweight, const uint16_t* scales, const uint8_t* zeros, int64_t M,
                     int64_t N, int64_t d, int32_t group, float* loss, float* dtheta, float* dalpha,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Channel-pair selection (host only, synchronous, no GPU): fills pairs
+ * [K][d/2][2] with global channel ids in the layout paro_rotation_create
+ * takes; every stage is a perfect pairing inside every group of `group`
+ * channels (pair p of a stage belongs to group p / (group / 2)).
+ *
+ * paro_pairs_random: random pairs with de-duplication, the selection the
+ * paper notes name ("局限与展望": random plus de-duplication). Reading: for
+ * each group in order and each stage in order, draw a uniformly random
+ * permutation of the group's channels (Fisher-Yates from the last position
+ * down, j = r mod (i + 1) with r the next SplitMix64 output of one stream
+ * seeded with `seed`, state += 0x9E3779B97F4A7C15 per output); then for
+ * positions i = 0, 2, 4, ... pair the channel at i with the first channel
+ * after it not yet paired with it in an earlier stage of the group, which is
+ * exchanged with the channel at position i + 1; if none is left, draw the
+ * stage again (at most 4096 draws).
+ * The pair is stored as (channel at i, its partner). No unordered pair
+ * occurs twice in one group. K <= group - 1; near that bound the earlier
+ * stages can leave no pairing without repeats (for example 7 stages of a
+ * group of 8 need a one-factorization the greedy stages may not extend), and
+ * the call returns PARO_ERR_VALUE.
+ * Errors: PARO_ERR_NULL, PARO_ERR_SHAPE (group odd or not dividing d, d >
+ * 2^24, K out of range), PARO_ERR_VALUE (4096 draws without a pairing).
+ */
+int paro_pairs_random(int64_t d, int32_t group, int32_t K, uint64_t seed, int32_t* pairs);
+
+/*
+ * paro_pairs_by_gap: pairs of channels whose values differ strongly (CSDN
+ * article, section 2.2: pairs with a large numeric difference are preferred).
+ * score: host float [d], one value per input channel (for example the
+ * largest |W| over the output rows). Reading: in each group, rank the
+ * channels by score, largest first (ties: lower channel first); stage t
+ * pairs the i-th largest with the ((i + t) mod (group / 2))-th smallest, for
+ * i = 0 .. group / 2 - 1, stored as (larger, smaller). Stage 0 pairs the
+ * largest with the smallest; every pair joins the top and the bottom half of
+ * the ranking, which is the largest total score difference a perfect
+ * pairing can have, and no pair repeats across stages. K <= group / 2.
+ * Errors: PARO_ERR_NULL, PARO_ERR_SHAPE, PARO_ERR_VALUE (non-finite score).
+ */
+int paro_pairs_by_gap(int64_t d, int32_t group, int32_t K, const float* score, int32_t* pairs);
+
+/*
+ * paro_sparsify_angles: keep only the strongest rotations of a plan (paper
+ * notes, "核心观察": a sparse rotation keeping the top 10% of the channel
+ * pairs matches the full one). theta, theta_out: host float [K][d/2] (may
+ * be the same array). Reading: the n_keep pairs with the largest |theta| over
+ * the whole plan keep their angle (ties: the earlier stage and pair first),
+ * every other pair gets theta = 0, an exact identity. For angles in
+ * [-pi, pi], |theta| orders the rotations by their distance from the
+ * identity. Errors: PARO_ERR_NULL, PARO_ERR_SHAPE (0 <= n_keep <= K d / 2,
+ * d even), PARO_ERR_VALUE (non-finite angle).
+ */
+int paro_sparsify_angles(int64_t d, int32_t K, const float* theta, int64_t n_keep, float* theta_out);
 
 /*
  * Host-only view of the per-segment rotation schedule that

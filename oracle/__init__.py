@@ -40,8 +40,10 @@ notes of the repository):
     round-to-nearest over 15 steps, range widened to include 0, fp16 scale,
     integer zero in [0, 15], codes clamp(rint(u/s) + z, 0, 15), ties to even.
     A zero scale becomes 1.0; an infinite or NaN scale is an error.
-  * Packing: byte b of a row holds code(2b) in its low nibble and code(2b+1)
-    in its high nibble; scales fp16 [N][d/G]; zeros uint8 [N][d/G].
+  * Packing: eight codes per 32-bit little-endian word (channels 8w .. 8w+7),
+    the even channels in its low 16 bits and the odd ones in its high 16
+    bits, 4 bits each in channel order (``pack_codes``); scales fp16 [N][d/G];
+    zeros uint8 [N][d/G].
   * cos/sin: c = float32(cos(float64(theta))), s = float32(sin(...)) for the
     canonical fp32 weight transform; plain fp64 cos/sin for the fp64 parts.
 
@@ -281,17 +283,37 @@ def quantize_groups(u, group):
 
 
 def pack_codes(codes):
-    """Two 4-bit codes per byte: code(2b) in the low nibble, code(2b+1) high."""
+    """Eight codes per 32-bit little-endian word, split by parity (reading R8):
+    a word covers channels 8w .. 8w + 7; its low 16 bits hold the even
+    channels 8w, 8w+2, 8w+4, 8w+6 and its high 16 bits the odd channels
+    8w+1, 8w+3, 8w+5, 8w+7, four bits each in increasing channel order. So
+    byte 0 = c0 | c2 << 4, byte 1 = c4 | c6 << 4, byte 2 = c1 | c3 << 4,
+    byte 3 = c5 | c7 << 4 (c_i the code of channel 8w + i). The row length
+    must be a multiple of 8."""
     codes = np.asarray(codes, dtype=np.uint8)
-    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    N, d = codes.shape
+    if d % 8:
+        raise ValueError("the row length must be a multiple of 8")
+    c = codes.reshape(N, d // 8, 8)
+    out = np.empty((N, d // 8, 4), dtype=np.uint8)
+    out[:, :, 0] = c[:, :, 0] | (c[:, :, 2] << 4)
+    out[:, :, 1] = c[:, :, 4] | (c[:, :, 6] << 4)
+    out[:, :, 2] = c[:, :, 1] | (c[:, :, 3] << 4)
+    out[:, :, 3] = c[:, :, 5] | (c[:, :, 7] << 4)
+    return out.reshape(N, d // 2)
 
 
 def unpack_codes(qweight):
+    """Inverse of ``pack_codes``."""
     qweight = np.asarray(qweight, dtype=np.uint8)
-    out = np.empty((qweight.shape[0], qweight.shape[1] * 2), dtype=np.uint8)
-    out[:, 0::2] = qweight & 0x0F
-    out[:, 1::2] = qweight >> 4
-    return out
+    N = qweight.shape[0]
+    b = qweight.reshape(N, -1, 4)
+    out = np.empty((N, b.shape[1], 8), dtype=np.uint8)
+    out[:, :, 0], out[:, :, 2] = b[:, :, 0] & 0x0F, b[:, :, 0] >> 4
+    out[:, :, 4], out[:, :, 6] = b[:, :, 1] & 0x0F, b[:, :, 1] >> 4
+    out[:, :, 1], out[:, :, 3] = b[:, :, 2] & 0x0F, b[:, :, 2] >> 4
+    out[:, :, 5], out[:, :, 7] = b[:, :, 3] & 0x0F, b[:, :, 3] >> 4
+    return out.reshape(N, -1)
 
 
 def dequantize(qweight, scales, zeros, group):

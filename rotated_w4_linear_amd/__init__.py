@@ -9,7 +9,8 @@ Names follow the C ABI: ``paro_device_init``, ``paro_rotation_create`` / ``Rotat
 ``paro_rotate``, ``paro_quantize_weights``, ``paro_w4_linear``,
 ``paro_w4_linear_workspace_size``, ``paro_w4_linear_noalloc``, ``paro_rotation_backward``,
 ``paro_rotation_backward_workspace_size``, ``paro_layer_loss``,
-``paro_layer_loss_workspace_size``.
+``paro_layer_loss_workspace_size``, ``paro_pairs_random``, ``paro_pairs_by_gap``,
+``paro_sparsify_angles``.
 """
 from __future__ import annotations
 
@@ -81,6 +82,12 @@ def load_library() -> ctypes.CDLL:
     lib.paro_layer_loss.restype = ctypes.c_int
     lib.paro_layer_loss.argtypes = [vp, vp, vp, vp, vp, vp, c_i64, c_i64, c_i64, c_i32, vp, vp, vp,
                                     vp, c_size, vp]
+    lib.paro_pairs_random.restype = ctypes.c_int
+    lib.paro_pairs_random.argtypes = [c_i64, c_i32, c_i32, ctypes.c_uint64, vp]
+    lib.paro_pairs_by_gap.restype = ctypes.c_int
+    lib.paro_pairs_by_gap.argtypes = [c_i64, c_i32, c_i32, vp, vp]
+    lib.paro_sparsify_angles.restype = ctypes.c_int
+    lib.paro_sparsify_angles.argtypes = [c_i64, c_i32, vp, c_i64, vp]
     lib.paro_rotation_plan_host.restype = ctypes.c_int
     lib.paro_rotation_plan_host.argtypes = [c_i64, c_i32, c_i32, vp, vp, vp, vp, c_size,
                                             ctypes.POINTER(c_size), ctypes.POINTER(c_i32)]
@@ -307,3 +314,29 @@ def paro_rotation_plan_host(pairs, theta, alpha, group: int) -> Tuple[np.ndarray
                                        ctypes.byref(need), lay))
     return img, {"seg_ch": lay[0], "ppl": lay[1], "words": lay[2], "fast": bool(lay[3]),
                  "stages": lay[4]}
+
+
+def paro_pairs_random(d: int, group: int, K: int, seed: int) -> np.ndarray:
+    """Random pairs with de-duplication across stages: int32 [K][d/2][2]."""
+    out = np.zeros((K, d // 2, 2), dtype=np.int32)
+    _check(load_library().paro_pairs_random(d, group, K, ctypes.c_uint64(seed & (2 ** 64 - 1)),
+                                            _ptr(out)))
+    return out
+
+
+def paro_pairs_by_gap(score, group: int, K: int) -> np.ndarray:
+    """Pairs of strongly differing channels by per-channel ``score``: int32 [K][d/2][2]."""
+    score = np.ascontiguousarray(np.asarray(score, dtype=np.float32))
+    d = int(score.shape[0])
+    out = np.zeros((K, d // 2, 2), dtype=np.int32)
+    _check(load_library().paro_pairs_by_gap(d, group, K, _ptr(score), _ptr(out)))
+    return out
+
+
+def paro_sparsify_angles(theta, n_keep: int) -> np.ndarray:
+    """The ``n_keep`` largest-|theta| pairs keep their angle, the rest get 0."""
+    theta = np.ascontiguousarray(np.asarray(theta, dtype=np.float32))
+    K, half = theta.shape
+    out = np.zeros_like(theta)
+    _check(load_library().paro_sparsify_angles(2 * half, K, _ptr(theta), int(n_keep), _ptr(out)))
+    return out

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libparo.so")
 
-SOURCES = ["api.cpp", "plan.cpp", "rotate.hip", "quantize.hip", "w4_linear.hip", "decode.hip",
+SOURCES = ["api.cpp", "plan.cpp", "pairs.cpp", "rotate.hip", "quantize.hip", "w4_linear.hip", "decode.hip",
            "backward.hip", "layer_loss.hip", "noalloc.hip", "dense_gemm.hip"]
 
 COMPILE_FLAGS = [

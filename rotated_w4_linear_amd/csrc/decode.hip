@@ -39,11 +39,10 @@
 // The rotation is recomputed by each of the N / 128 n-blocks that read a
 // segment: with M <= 16 this is ALU work hidden under the weight loads.
 //
-// Dequantization: v = (1024 + q) is built in fp16 by OR-ing a nibble into the
-// mantissa of 1024.0, (v - (1024 + z)) = q - z is exact, and one packed
-// multiply by the fp16 scale rounds once. Nibbles e and e + 4 of a 32-bit word
-// share one packed pair, so the eight codes of a word come out in the k order
-// (0, 4, 1, 5, 2, 6, 3, 7); X' is stored in LDS in the same order.
+// Dequantization (w4_common.h): two codes at a time are masked into the
+// mantissas of a pair of fp16 1024.0 values, (v - (1024 + z)) = q - z is
+// exact, and one packed multiply by the fp16 scale rounds once; the codes of
+// a word come out in channel order, and X' is stored in LDS in channel order.
 #include <atomic>
 #include <mutex>
 #include <string>
@@ -66,30 +65,11 @@ constexpr int kRsrcWord3 = 0x00020000;     // gfx9 buffer resource word 3
 constexpr int kAuxL2 = 1;                  // sc0: skip the per-CU cache
 constexpr int kAuxSys = 17;                // sc0 | sc1: memory-side coherence
 
-// Eight codes of a word -> fp16 (q - z) s in k order (0, 4, 1, 5, 2, 6, 3, 7).
-__device__ __forceinline__ h8 dequant8_interleaved(uint32_t w, h2 zz, h2 ss) {
-  constexpr uint32_t kMask = 0x000F000Fu, kOne = 0x64006400u;  // fp16 1024.0 pairs
-  uint32_t p[4];
-  p[0] = (w & kMask) | kOne;
-  p[1] = ((w >> 4) & kMask) | kOne;
-  p[2] = ((w >> 8) & kMask) | kOne;
-  p[3] = ((w >> 12) & kMask) | kOne;
-  h8 out;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    h2 v = __builtin_bit_cast(h2, p[i]);
-    v = (v - zz) * ss;
-    out[2 * i] = v.x;
-    out[2 * i + 1] = v.y;
-  }
-  return out;
-}
-
 // Byte offset in the X' tile of channel k (local to the 512-wide slice) of
-// token m: chunk k / 8 at position (k / 8) ^ m, half (k % 4) * 2 + (k % 8) / 4.
+// token m: chunk k / 8 at position (k / 8) ^ m, half k % 8 inside it.
 __device__ __forceinline__ int xl_offset(int m, int k) {
-  const int c = k >> 3, e = k & 7;
-  return (m * 64 + (c ^ m)) * 16 + 2 * (((e & 3) << 1) | (e >> 2));
+  const int c = k >> 3;
+  return (m * 64 + (c ^ m)) * 16 + 2 * (k & 7);
 }
 
 // T: token rows staged and rotated (4 for M <= 4, else 16); MFMA columns past
@@ -213,26 +193,27 @@ __global__ __launch_bounds__(256) void w4_decode_kernel(
       for (int i = 0; i < T; ++i) pk[i] = raw[i];
       k0 = 128 * w + 2 * lane;
     }
+    // (k0 is even: the lane's two channels are adjacent halves of one chunk)
 #pragma unroll
-    for (int i = 0; i < T; ++i) {
-      *(uint16_t*)(xlb + xl_offset(i, k0)) = (uint16_t)pk[i];
-      *(uint16_t*)(xlb + xl_offset(i, k0 + 1)) = (uint16_t)(pk[i] >> 16);
-    }
+    for (int i = 0; i < T; ++i) *(uint32_t*)(xlb + xl_offset(i, k0)) = pk[i];
   }
   __syncthreads();
 
   // ---- 4. dequantize and multiply, group by group as the weights land -------
+  const uint32_t one = fp16_1024_pair();
   f4 acc[TJ];
 #pragma unroll
   for (int j = 0; j < TJ; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int q = 0; q < DK_SEGS; ++q) {
     if (q < nq) {
-      h2 ss[TJ], zz[TJ];
+      h2 ss[TJ], zz[TJ], ss16[TJ], zz16[TJ];
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         ss[j] = splat2(__builtin_bit_cast(_Float16, (uint16_t)sraw[j][q]));
+        ss16[j] = ss[j] * splat2((_Float16)0.0625f);
         zz[j] = splat2((_Float16)(1024.0f + (float)zraw[j][q]));
+        zz16[j] = splat2((_Float16)(1024.0f + 16.0f * (float)zraw[j][q]));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -240,7 +221,7 @@ __global__ __launch_bounds__(256) void w4_decode_kernel(
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
           acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              dequant8_interleaved(wv[j][q][i], zz[j], ss[j]), b, acc[j], 0, 0, 0);
+              dequant8(wv[j][q][i], zz[j], ss[j], zz16[j], ss16[j], one), b, acc[j], 0, 0, 0);
       }
     }
   }

@@ -202,18 +202,22 @@ __global__ __launch_bounds__(256) void quantize_kernel(
         const float negmn = -mn[q];
         const float zf = fminf(fmaxf(rintf(negmn / sq), 0.0f), 15.0f);
         for (int b = lane; b < half; b += 64) {
-          const float q0f = fminf(fmaxf(rintf(u[SL * q + 2 * b] / sq) + zf, 0.0f), 15.0f);
-          const float q1f = fminf(fmaxf(rintf(u[SL * q + 2 * b + 1] / sq) + zf, 0.0f), 15.0f);
+          // byte b of the group: byte b % 4 of the word of channels 8 (b / 4) ..
+          // + 7, which holds channels c0 and c0 + 2 (low, high nibble) with
+          // c0 = 0, 4, 1, 5 for bytes 0 .. 3 (even channels in the word's low
+          // half, odd ones in its high half)
+          const int c0 = 8 * (b >> 2) + ((b & 1) << 2) + ((b >> 1) & 1);
+          const float u0 = u[SL * q + c0], u1 = u[SL * q + c0 + 2];
+          const float q0f = fminf(fmaxf(rintf(u0 / sq) + zf, 0.0f), 15.0f);
+          const float q1f = fminf(fmaxf(rintf(u1 / sq) + zf, 0.0f), 15.0f);
           const uint32_t q0 = (uint32_t)q0f, q1 = (uint32_t)q1f;
           qweight[nq * (d / 2) + gq * half + b] = (uint8_t)(q0 | (q1 << 4));
           if (err) {
             // the quantization error E = (q - z) s - T W ((q - z) s is exact in
             // fp32), rounded once to fp16
-            const float e0 = (q0f - zf) * sq - u[SL * q + 2 * b];
-            const float e1 = (q1f - zf) * sq - u[SL * q + 2 * b + 1];
-            const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)e0);
-            const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)e1);
-            *(uint32_t*)(err + nq * d + gq * G + 2 * b) = h0 | (h1 << 16);
+            uint16_t* e = err + nq * d + gq * G + c0;
+            e[0] = __builtin_bit_cast(uint16_t, (_Float16)((q0f - zf) * sq - u0));
+            e[2] = __builtin_bit_cast(uint16_t, (_Float16)((q1f - zf) * sq - u1));
           }
         }
         if (lane == 0) {

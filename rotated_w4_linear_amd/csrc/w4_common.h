@@ -14,25 +14,43 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-// Eight 4-bit codes (k0 in bits 0..3, ..., k7 in bits 28..31) -> eight fp16
-// values (q - z) * s in k order.
-__device__ __forceinline__ h8 dequant8(uint32_t w, h2 zz, h2 ss) {
-  const uint32_t lo = w & 0x0F0F0F0Fu;         // q0 q2 q4 q6 (one per byte)
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // q1 q3 q5 q7
-  uint32_t p[4];
-  p[0] = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x64006400u;
-  p[1] = __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x64006400u;
-  p[2] = __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x64006400u;
-  p[3] = __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x64006400u;
+// Packed codes: one 32-bit word per 8 consecutive channels c0 .. c7, the even
+// channels in bits 0..15 and the odd ones in bits 16..31, 4 bits each in
+// channel order (word = c0 | c2 << 4 | c4 << 8 | c6 << 12 | c1 << 16 | ...).
+// Masking one nibble of each 16-bit half and OR-ing in the fp16 pattern of
+// 1024.0 gives the pair (c_{2i}, c_{2i+1}) in channel order: with the mask
+// 0x000F000F as 1024 + q, with 0x00F000F0 as 1024 + 16 q. Then (v - (1024 +
+// z)) = q - z (or 16 (q - z)) is exact in packed fp16, and one packed multiply
+// by s (or s / 16, exact: a power of two) rounds (q - z) s once. Eight values
+// cost one shift, four and-or and eight packed fp16 operations.
+//
+// zz = (1024 + z, 1024 + z), ss = (s, s), zz16 = (1024 + 16 z, ...),
+// ss16 = (s / 16, ...); `one` = 0x64006400 held in a vector register, so that
+// each (w & mask) | one is a single v_and_or_b32 (the mask is then the only
+// scalar operand, as gfx9 encodings allow).
+__device__ __forceinline__ h8 dequant8(uint32_t w, h2 zz, h2 ss, h2 zz16, h2 ss16, uint32_t one) {
+  const uint32_t w8 = w >> 8;
+  const h2 v0 = (__builtin_bit_cast(h2, (w & 0x000F000Fu) | one) - zz) * ss;      // c0, c1
+  const h2 v1 = (__builtin_bit_cast(h2, (w & 0x00F000F0u) | one) - zz16) * ss16;  // c2, c3
+  const h2 v2 = (__builtin_bit_cast(h2, (w8 & 0x000F000Fu) | one) - zz) * ss;     // c4, c5
+  const h2 v3 = (__builtin_bit_cast(h2, (w8 & 0x00F000F0u) | one) - zz16) * ss16; // c6, c7
   h8 out;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    h2 v = __builtin_bit_cast(h2, p[i]);
-    v = (v - zz) * ss;
-    out[2 * i] = v.x;
-    out[2 * i + 1] = v.y;
-  }
+  out[0] = v0.x;
+  out[1] = v0.y;
+  out[2] = v1.x;
+  out[3] = v1.y;
+  out[4] = v2.x;
+  out[5] = v2.y;
+  out[6] = v3.x;
+  out[7] = v3.y;
   return out;
+}
+
+// The fp16 pattern pair of 1024.0 in a vector register (see dequant8).
+__device__ __forceinline__ uint32_t fp16_1024_pair() {
+  uint32_t v;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(v));
+  return v;
 }
 
 __device__ __forceinline__ h2 splat2(_Float16 v) { return h2{v, v}; }

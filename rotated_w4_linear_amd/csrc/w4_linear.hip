@@ -4,10 +4,10 @@
 // (CSDN article section 2.1: Y = (X T^-1)(T W) + b; paper notes "主实验":
 // 4-bit weights, group G = 128; 64 and 256 are taken as well, each 64-channel
 // k-tile reading the one group it lies in). Here the layer is a dense contraction and runs
-// on the matrix cores. Dequantization: two nibbles are spread into the
-// mantissas of two fp16 1024.0 values with v_perm, (1024 + q) - (1024 + z) =
-// q - z is exact in packed fp16, and one packed multiply by the fp16 scale
-// rounds once.
+// on the matrix cores. Dequantization (w4_common.h): two codes at a time are
+// masked into the mantissas of a pair of fp16 1024.0 values with one
+// v_and_or_b32, (1024 + q) - (1024 + z) = q - z is exact in packed fp16, and
+// one packed multiply by the fp16 scale rounds once.
 #include "paro_internal.h"
 #include "w4_common.h"
 
@@ -152,6 +152,7 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
                                                kglob * (GB_K / 2), 0, 0);
   };
 
+  const uint32_t one = fp16_1024_pair();
   f16v acc[2][4];  // m tiles mm < MT used
 #pragma unroll
   for (int j = 0; j < 2; ++j)
@@ -168,20 +169,23 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
     dma(min(kt + 1, KT - 1), xn, wn, sn, zn);
     __builtin_amdgcn_sched_barrier(0);
     u4 wf[2];
-    h2 ss[2], zz[2];
+    h2 ss[2], zz[2], ss16[2], zz16[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int r = 64 * w + 32 * j + l32;
       wf[j] = wl[2 * r + (g ^ ((r >> 3) & 1))];
-      const bool ok = nw0 + r < N;
-      ss[j] = splat2(ok ? __builtin_bit_cast(_Float16, (uint16_t)(ss_l[r] & 0xffffu)) : (_Float16)0.0f);
-      zz[j] = splat2((_Float16)(1024.0f + (float)(zs_l[r] & 0xffu)));
+      // (rows past N read the last row's scale, clamped by the DMA; never stored)
+      ss[j] = splat2(__builtin_bit_cast(_Float16, (uint16_t)(ss_l[r] & 0xffffu)));
+      ss16[j] = ss[j] * splat2((_Float16)0.0625f);
+      const float zf = (float)(zs_l[r] & 0xffu);
+      zz[j] = splat2((_Float16)(1024.0f + zf));
+      zz16[j] = splat2((_Float16)(1024.0f + 16.0f * zf));
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       h8 a[2], b[MT];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) a[j] = dequant8(wf[j][i], zz[j], ss[j]);
+      for (int j = 0; j < 2; ++j) a[j] = dequant8(wf[j][i], zz[j], ss[j], zz16[j], ss16[j], one);
 #pragma unroll
       for (int mm = 0; mm < MT; ++mm) {
         const int r = 32 * mm + l32;

@@ -542,6 +542,42 @@ def test_decoder_chain_linear(paro, index):
 
 
 # ----------------------------------------------------------------------------
+# plans from the library's pair selection (random + de-duplication, largest
+# gaps, top-10% sparsification) through the same kernels
+# ----------------------------------------------------------------------------
+
+def selected_layer(paro, kind, d=4096, N=1024, G=128, K=8):
+    rng = synthetic.rng_for(3700, {"random": 0, "gap": 1, "top10": 2}[kind])
+    w = synthetic.draw_w(rng, N, d, 0.02, n_outlier_cols=synthetic.n_outliers(d), factor=10.0)
+    theta = synthetic.draw_theta(rng, d, K)
+    alpha = synthetic.draw_alpha(rng, d)
+    if kind == "gap":
+        pairs = paro.paro_pairs_by_gap(np.abs(w.astype(np.float32)).max(axis=0), G, K)
+    else:
+        pairs = paro.paro_pairs_random(d, G, K, 0x5041524F + d)
+    if kind == "top10":
+        theta = paro.paro_sparsify_angles(theta, int(round(0.1 * theta.size)))
+    return synthetic.Layer(w, pairs, theta, alpha, G)
+
+
+@pytest.mark.parametrize("kind", ["random", "gap", "top10"])
+def test_selected_pairings_through_the_kernels(paro, kind):
+    """Plans built by paro_pairs_random / paro_pairs_by_gap (score: the largest
+    |W| of each input channel) / paro_sparsify_angles (10% of the pairs kept):
+    X' at 2e-3, codes bit-exact on sampled rows, the linear at M = 16 and 300."""
+    layer = selected_layer(paro, kind)
+    log(f"selected pairing {kind}")
+    x = synthetic.draw_x(synthetic.rng_for(3701, 0), 2048, layer.d, synthetic.n_outliers(layer.d), 20.0)
+    rows = np.sort(synthetic.rng_for(3702, 0).choice(2048, 64, replace=False))
+    rows[-1] = 2047
+    check_rotation(paro, x, layer, rows=rows)
+    check_quantize(paro, layer, rows=np.arange(0, layer.w.shape[0], 37))
+    for M in (16, 300):
+        fro, mx = check_linear(paro, x[:M], layer)
+        log(f"  linear M={M}: rel-Frobenius {fro:.2e}, max {mx:.2e}")
+
+
+# ----------------------------------------------------------------------------
 # gradients of the transform
 # ----------------------------------------------------------------------------
 

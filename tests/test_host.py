@@ -340,3 +340,66 @@ def test_schedule_full_decode_layer(paro):
     check_slots_conflict_free(img, lay, 8, 4096)
     ref = oracle.rotate_activations(x, layer.pairs, layer.theta, layer.alpha)
     metrics.assert_rotated_close(emulate_rotate(img, lay, x, 8, 4096), ref, 128)
+
+
+# ----------------------------------------------------------------------------
+# channel-pair selection (host functions of the library) against the oracle
+# ----------------------------------------------------------------------------
+
+from oracle import pairs as opairs  # noqa: E402
+
+
+@pytest.mark.parametrize("d,G,K,seed", [(256, 128, 8, 1), (4096, 128, 8, 0x5041524F), (128, 64, 16, 2),
+                                        (512, 256, 8, 3), (8, 4, 3, 11), (640, 64, 0, 5),
+                                        (2 ** 10, 8, 4, 2 ** 64 - 1)])
+def test_pairs_random_equal_oracle(paro, d, G, K, seed):
+    got = paro.paro_pairs_random(d, G, K, seed)
+    want = opairs.pairs_random(d, G, K, seed)
+    assert np.array_equal(got, want)
+
+
+def test_pairs_random_infeasible_is_an_error(paro):
+    """Seven greedy stages of a group of 8 can run out of unrepeated pairs;
+    the library reports it where the oracle does."""
+    try:
+        opairs.pairs_random(64, 8, 7, 4)
+        feasible = True
+    except RuntimeError:
+        feasible = False
+    if feasible:
+        assert np.array_equal(paro.paro_pairs_random(64, 8, 7, 4), opairs.pairs_random(64, 8, 7, 4))
+    else:
+        with pytest.raises(paro.ParoError) as ei:
+            paro.paro_pairs_random(64, 8, 7, 4)
+        assert ei.value.status == -4
+    with pytest.raises(paro.ParoError):
+        paro.paro_pairs_random(100, 8, 3, 1)  # group does not divide d
+    with pytest.raises(paro.ParoError):
+        paro.paro_pairs_random(64, 8, 8, 1)  # K > group - 1
+
+
+@pytest.mark.parametrize("d,G,K", [(256, 128, 8), (4096, 128, 8), (512, 64, 32), (256, 256, 8), (8, 8, 4)])
+def test_pairs_by_gap_equal_oracle(paro, d, G, K):
+    rng = synthetic.rng_for(99, d + G + K)
+    w = synthetic.draw_w(rng, 64, d, 0.02, n_outlier_cols=max(1, d // 64), factor=10.0)
+    score = np.abs(w.astype(np.float32)).max(axis=0)  # the largest |W| of each input channel
+    score[::7] = score[3]  # ties
+    got = paro.paro_pairs_by_gap(score, G, K)
+    assert np.array_equal(got, opairs.pairs_by_gap(score, G, K))
+    with pytest.raises(paro.ParoError):
+        paro.paro_pairs_by_gap(score, G, G // 2 + 1)
+    bad = score.copy()
+    bad[1] = np.nan
+    with pytest.raises(paro.ParoError):
+        paro.paro_pairs_by_gap(bad, G, K)
+
+
+@pytest.mark.parametrize("K,d,frac", [(8, 4096, 0.1), (8, 256, 0.25), (1, 128, 0.0), (4, 512, 1.0)])
+def test_sparsify_angles_equal_oracle(paro, K, d, frac):
+    rng = synthetic.rng_for(99, 7 * K + d)
+    theta = synthetic.draw_theta(rng, d, K)
+    theta.reshape(-1)[::5] = theta.reshape(-1)[2]  # ties
+    n = int(round(frac * theta.size))
+    got = paro.paro_sparsify_angles(theta, n)
+    assert np.array_equal(got.view(np.uint32), opairs.sparsify_angles(theta, n).view(np.uint32))
+    assert int((got != 0).sum()) <= n

@@ -228,29 +228,32 @@ def test_param_validation():
 # ----------------------------------------------------------------------------
 
 def read_quant_golden():
-    cases = []
-    for ln in open(os.path.join(GOLDEN, "quantize_worked.txt")):
-        if not ln.strip() or ln.startswith("#"):
+    path = os.path.join(os.path.dirname(__file__), "golden", "quantize_worked.txt")
+    cases, packed = [], None
+    for ln in open(path):
+        ln = ln.strip()
+        if not ln or ln.startswith("#"):
             continue
-        u, sz, q, packed = [p.split() for p in ln.split("|")]
-        cases.append((np.array(u, np.float32), int(sz[0], 16), int(sz[1]),
-                      np.array(q, np.uint8), bytes(int(b, 16) for b in packed)))
-    return cases
+        if ln.startswith("packed"):
+            packed = bytes(int(b, 16) for b in ln.split()[1:])
+            continue
+        u, sz, q = [p.split() for p in ln.split("|")]
+        cases.append((np.array(u, np.float32), int(sz[0], 16), int(sz[1]), np.array(q, np.uint8)))
+    return cases, packed
 
 
 def test_quantize_worked_examples():
-    cases = read_quant_golden()
+    cases, packed = read_quant_golden()
     assert len(cases) == 6
-    for u, s_bits, z, q, packed in cases:
+    for u, s_bits, z, q in cases:
         codes, s16, zeros = oracle.quantize_groups(u[None, :], 4)
         assert int(s16.view(np.uint16)[0, 0]) == s_bits
         assert int(zeros[0, 0]) == z
         np.testing.assert_array_equal(codes[0], q)
-        assert oracle.pack_codes(codes)[0].tobytes() == packed
-    # all six as one row of six groups
+    # all six as one row of six groups, packed by hand
     row = np.concatenate([c[0] for c in cases])[None, :]
     codes, s16, zeros = oracle.quantize_groups(row, 4)
-    assert oracle.pack_codes(codes)[0].tobytes() == b"".join(c[4] for c in cases)
+    assert oracle.pack_codes(codes)[0].tobytes() == packed
 
 
 def test_r1_r2_r3_on_random_groups():
@@ -299,8 +302,9 @@ def test_r5_packing_and_one_hot_linear():
     codes = rng.integers(0, 16, size=(7, 32)).astype(np.uint8)
     packed = oracle.pack_codes(codes)
     np.testing.assert_array_equal(oracle.unpack_codes(packed), codes)
-    # nibble order: channel 0 -> low nibble
-    assert oracle.pack_codes(np.array([[1, 2]], np.uint8))[0, 0] == 0x21
+    # word layout: even channels in the low half, odd channels in the high half
+    word = oracle.pack_codes(np.array([[1, 2, 3, 4, 5, 6, 7, 8]], np.uint8))[0].view("<u4")[0]
+    assert word == 0x86427531
     # one-hot activations read out single dequantized weights plus the bias
     scales = (rng.random((7, 2)) * 0.1 + 0.01).astype(np.float16)
     zeros = rng.integers(0, 16, size=(7, 2)).astype(np.uint8)
@@ -639,3 +643,125 @@ def test_l_tolerance_covers_fp16_arithmetic_and_rejects_mistakes(M, d, N, G, K, 
     sth, _ = oracle.layer_loss_gradients(x, layer.w, xr, what, dy, swapped, layer.theta, layer.alpha)
     with pytest.raises(AssertionError):
         metrics.assert_within(sth, ref[1], tth, "dtheta (swapped pair)")
+
+
+# ----------------------------------------------------------------------------
+# S1-S6: choosing the channel pairs (oracle.pairs)
+# ----------------------------------------------------------------------------
+
+from oracle import pairs as opairs  # noqa: E402
+
+
+def _golden(name):
+    path = os.path.join(os.path.dirname(__file__), "golden", name)
+    return [ln.split() for ln in open(path) if ln.strip() and not ln.startswith("#")]
+
+
+def test_s1_splitmix64_reference_outputs():
+    """The generator reproduces the published SplitMix64 outputs."""
+    for row in _golden("splitmix64.txt"):
+        rng = opairs.SplitMix64(int(row[0]))
+        assert [rng.next() for _ in row[1:]] == [int(v) for v in row[1:]]
+
+
+def test_s2_shuffle_is_uniform():
+    """Fisher-Yates from SplitMix64 draws every permutation of 3 items equally
+    often (chi-square over 60000 draws); the common mistake of drawing j from
+    all n positions at every step gives frequencies 4/27 .. 5/27 and fails."""
+    rng = opairs.SplitMix64(7)
+    counts = {}
+    n = 60000
+    for _ in range(n):
+        key = tuple(opairs.shuffle(rng, 3))
+        counts[key] = counts.get(key, 0) + 1
+    assert len(counts) == 6
+    exp = n / 6
+    chi2 = sum((c - exp) ** 2 / exp for c in counts.values())
+    assert chi2 < 25.7  # 5 degrees of freedom, p = 1e-4
+
+
+def _assert_valid_plan(p, d, G):
+    theta = np.zeros(p.shape[:2], np.float32)
+    oracle.check_rotation_params(p, theta, np.ones(d, np.float32), G)
+
+
+def test_s3_random_pairs_never_repeat_and_complete_a_factorization():
+    """Every stage is a perfect pairing inside the groups and no unordered pair
+    occurs twice in a group; with G = 4 and K = 3 the three stages use each of
+    the six pairs of the group exactly once (the one-factorization of K4)."""
+    for d, G, K, seed in [(256, 128, 8, 1), (128, 64, 16, 2), (512, 256, 8, 3), (64, 8, 4, 4)]:
+        p = opairs.pairs_random(d, G, K, seed)
+        _assert_valid_plan(p, d, G)
+        for g in range(d // G):
+            sl = p[:, g * (G // 2):(g + 1) * (G // 2)].reshape(-1, 2)
+            keys = {frozenset(map(int, r)) for r in sl}
+            assert len(keys) == sl.shape[0]
+    for seed in range(20):
+        p = opairs.pairs_random(8, 4, 3, seed)
+        for g in range(2):
+            sl = p[:, 2 * g:2 * g + 2].reshape(-1, 2) - 4 * g
+            assert sorted(tuple(sorted(map(int, r))) for r in sl) == \
+                [(0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3)]
+
+
+def test_s4_gap_pairs_hand_worked():
+    rows = _golden("pairs_by_gap_g8.txt")
+    cases = []
+    for r in rows:
+        if r[0] == "score":
+            cases.append([np.array([float(v) for v in r[1:]], np.float32), []])
+        else:
+            cases[-1][1].append(np.array([int(v) for v in r[1:]]).reshape(4, 2))
+    for score, stages in cases:
+        p = opairs.pairs_by_gap(score, 8, len(stages))
+        for t, want in enumerate(stages):
+            assert np.array_equal(p[t], want), (t, p[t], want)
+
+
+def _matchings(items):
+    if not items:
+        yield []
+        return
+    a = items[0]
+    for k in range(1, len(items)):
+        rest = items[1:k] + items[k + 1:]
+        for m in _matchings(rest):
+            yield [(a, items[k])] + m
+
+
+def test_s5_gap_pairs_reach_the_largest_total_difference():
+    """Brute force over all 105 perfect pairings of 8 channels: every stage's
+    total |score_i - score_j| equals the largest any pairing reaches, and the
+    stages' pairs are distinct."""
+    rng = synthetic.rng_for(98, 0)
+    for trial in range(5):
+        s = rng.standard_normal(8).astype(np.float32)
+        best = max(sum(abs(float(s[a]) - float(s[b])) for a, b in m) for m in _matchings(list(range(8))))
+        p = opairs.pairs_by_gap(s, 8, 4)
+        _assert_valid_plan(p, 8, 8)
+        seen = set()
+        for t in range(4):
+            tot = sum(abs(float(s[a]) - float(s[b])) for a, b in p[t])
+            assert abs(tot - best) <= 1e-6 * max(1.0, best)
+            for a, b in p[t]:
+                assert float(s[a]) >= float(s[b])
+                key = frozenset((int(a), int(b)))
+                assert key not in seen
+                seen.add(key)
+
+
+def test_s6_sparsify_keeps_the_largest_angles():
+    """Brute force: the kept pairs are the n_keep largest |theta| (ties by
+    position), with their angle unchanged; all others are 0."""
+    theta = np.array([[0.5, -2.0, 0.1, 2.0], [-0.5, 3.0, 0.0, -0.1]], np.float32)
+    got = opairs.sparsify_angles(theta, 4)
+    assert np.array_equal(got, np.array([[0.5, -2.0, 0.0, 2.0], [0.0, 3.0, 0.0, 0.0]], np.float32))
+    rng = synthetic.rng_for(98, 1)
+    th = rng.uniform(-np.pi, np.pi, size=(3, 16)).astype(np.float32)
+    th[1, 3] = th[0, 5]  # a tie
+    for n in (0, 1, 7, 24, 48):
+        got = opairs.sparsify_angles(th, n)
+        flat = [(abs(float(v)), i) for i, v in enumerate(th.reshape(-1))]
+        chosen = {i for _, i in sorted(flat, key=lambda e: (-e[0], e[1]))[:n]}
+        for i, v in enumerate(got.reshape(-1)):
+            assert v == (th.reshape(-1)[i] if i in chosen else 0.0)
