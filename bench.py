@@ -264,24 +264,30 @@ def time_layer(paro, torch, r, xs, qr, qp, steps, warmup, M, N, d):
     }
 
 
-def copy_rate_gbps(torch, nbytes, ring=4, reps=12):
-    """Read + write GB/s of a plain device copy of nbytes, cycling a ring of buffers
-    (the same cold-cache condition as the kernels)."""
-    src = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(ring)]
-    dst = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(ring)]
-    for i in range(ring):
-        dst[i].copy_(src[i])
-    torch.cuda.synchronize()
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
-    s.record()
-    for i in range(reps):
-        dst[i % ring].copy_(src[(i + 1) % ring])
-    e.record()
-    torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / reps
+def copy_rate_gbps(torch, paro, nbytes, ring=4, reps=12):
+    """Read + write GB/s of the library's plain device copy (paro_stream_copy)
+    of nbytes, cycling a ring of buffers (the same cold-cache condition as the
+    kernels): the best over a few launch sizes, i.e. the measured ceiling of a
+    read stream plus a write stream of that size. Returns (GB/s, blocks)."""
+    n = (nbytes + 15) // 16 * 16
+    src = [torch.ones(n, dtype=torch.uint8, device="cuda") for _ in range(ring)]
+    dst = [torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(ring)]
+    best = (0.0, 0)
+    for blocks in (2048, 4096, 8192, 16384):
+        for i in range(ring):
+            paro.paro_stream_copy(src[i], dst[i], blocks)
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for i in range(reps):
+            paro.paro_stream_copy(src[(i + 1) % ring], dst[i % ring], blocks)
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        best = max(best, (2.0 * n / (ms * 1e-3) / 1e9, blocks))
     del src, dst
-    return 2.0 * nbytes / (ms * 1e-3) / 1e9
+    return best
 
 
 def cpu_baseline(x, layer, paro_q, N, d, target_s=12.0):
@@ -308,14 +314,16 @@ def cpu_baseline(x, layer, paro_q, N, d, target_s=12.0):
 def bench_layer(args, paro, torch, name, x, layer):
     M, d = x.shape
     N = layer.w.shape[0]
-    ring = args.ring or 4
+    # distinct copies of X and of both weight sets: > 1 GiB in total for the
+    # MLP layer (10 x (64 + 2 x 30) MB), beyond the 256 MB Infinity Cache
+    ring = args.ring or 10
     log(f"[bench] {name}: M={M} d={d} N={N} ring={ring}")
     r, xs, qr, qp = setup_layer(paro, torch, x, layer, ring)
     tm = time_layer(paro, torch, r, xs, qr, qp, args.steps, args.warmup, M, N, d)
     flops = 2.0 * M * N * d
     rot_bytes = 4.0 * M * d
     lin_tflops = flops / (tm["lin_ms"] * 1e-3) / 1e12
-    copy_gbps = copy_rate_gbps(torch, M * d * 2)
+    copy_gbps, _ = copy_rate_gbps(torch, paro, M * d * 2)
     rot_gbps = rot_bytes / (tm["rot_ms"] * 1e-3) / 1e9
     out = {
         "metric": METRIC,
@@ -440,6 +448,10 @@ def bench_sweep(args, paro, torch):
     T = Timer(torch)
     pts = []
     ring = args.ring or 6
+    # measured ceiling: the library's plain copy of the largest point's bytes
+    # (8192 x 5120 fp16 in and out), cycled over the same kind of ring
+    copy_gbps, copy_blocks = copy_rate_gbps(torch, paro, 8192 * 5120 * 2, ring=ring)
+    log(f"[sweep] copy ceiling {copy_gbps:.0f} GB/s ({copy_blocks} workgroups)")
     for p, (d, K, G) in enumerate(synthetic.sweep_points()):
         x, layer = synthetic.sweep(p)
         r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, G)
@@ -458,7 +470,7 @@ def bench_sweep(args, paro, torch):
         ms = s.elapsed_time(e) / n
         gbps = 4.0 * x.shape[0] * d / (ms * 1e-3) / 1e9
         pts.append({"d": d, "K": K, "G": G, "us": round(ms * 1e3, 2), "gbps": round(gbps, 1),
-                    "frac": round(gbps / HBM_PEAK_GBPS, 4)})
+                    "frac": round(gbps / HBM_PEAK_GBPS, 4), "frac_of_copy": round(gbps / copy_gbps, 4)})
         log(f"[sweep] d={d} K={K} G={G}: {ms*1e3:.1f} us, {gbps:.0f} GB/s")
         del xs, ys
     g = [q["gbps"] for q in pts]
@@ -469,6 +481,7 @@ def bench_sweep(args, paro, torch):
         "ms_per_step": round(sum(q["us"] for q in pts) / 1e3, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "rotation_sweep_8192xd_27pts"}, "points": pts,
+        "copy_ceiling_gbps": round(copy_gbps, 1), "copy_ceiling_blocks": copy_blocks,
         "roofline": {"bound": "hbm", "achieved": k8["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": k8["frac"], "traffic": traffic_for("rotate:sweep_d4096_K8_G128")},
     }
@@ -743,19 +756,20 @@ def bench_chain(args, paro, torch):
             "chain": res}
 
 
-def bench_copy(args, torch):
-    """A plain device copy of known size (for calibrating HBM byte counters)."""
+def bench_copy(args, paro, torch):
+    """The library's plain device copy of 256 MiB (paro_stream_copy), for
+    calibrating the HBM byte counters and as the measured copy ceiling."""
     n = 256 << 20
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     a.fill_(1)
     for _ in range(3):
-        b.copy_(a)
+        paro.paro_stream_copy(a, b)
     torch.cuda.synchronize()
     T = Timer(torch)
     s = T.event()
     for _ in range(args.steps):
-        b.copy_(a)
+        paro.paro_stream_copy(a, b)
     e = T.event()
     torch.cuda.synchronize()
     ms = s.elapsed_time(e) / args.steps
@@ -814,7 +828,7 @@ def main():
     elif args.workload == "calib":
         out = bench_calib(args, paro, torch)
     else:
-        out = bench_copy(args, torch)
+        out = bench_copy(args, paro, torch)
     print(json.dumps(out), flush=True)
 
 

@@ -413,6 +413,21 @@ int paro_pairs_by_gap(int64_t d, int32_t group, int32_t K, const float* score, i
 int paro_sparsify_angles(int64_t d, int32_t K, const float* theta, int64_t n_keep, float* theta_out);
 
 /*
+ * Measurement: a plain device copy dst[0 .. bytes) = src[0 .. bytes) at the
+ * rate HBM sustains for one read and one write stream (16-byte buffer loads
+ * and stores, 4 per lane in flight, `blocks` workgroups of 256 lanes striding
+ * over the buffer). It is the measured ceiling that the memory-bound kernels
+ * (paro_rotate, the small-batch paro_w4_linear) are reported against, next to
+ * the datasheet peak; it takes no part in the method.
+ *   src, dst  device memory, 16-byte aligned, not overlapping;
+ *   bytes     a multiple of 16 (0 is a no-op);
+ *   blocks    1 .. 2^20.
+ * Asynchronous on stream. Errors: PARO_ERR_NULL, PARO_ERR_ALIGN,
+ * PARO_ERR_SHAPE, PARO_ERR_HIP.
+ */
+int paro_stream_copy(const void* src, void* dst, size_t bytes, int32_t blocks, hipStream_t stream);
+
+/*
  * Host-only view of the per-segment rotation schedule that
  * paro_rotation_create uploads (for testing the plan logic without a GPU).
  * Fills `out` (host memory of out_bytes) with the exact table image and writes

@@ -88,6 +88,8 @@ def load_library() -> ctypes.CDLL:
     lib.paro_pairs_by_gap.argtypes = [c_i64, c_i32, c_i32, vp, vp]
     lib.paro_sparsify_angles.restype = ctypes.c_int
     lib.paro_sparsify_angles.argtypes = [c_i64, c_i32, vp, c_i64, vp]
+    lib.paro_stream_copy.restype = ctypes.c_int
+    lib.paro_stream_copy.argtypes = [vp, vp, c_size, c_i32, vp]
     lib.paro_rotation_plan_host.restype = ctypes.c_int
     lib.paro_rotation_plan_host.argtypes = [c_i64, c_i32, c_i32, vp, vp, vp, vp, c_size,
                                             ctypes.POINTER(c_size), ctypes.POINTER(c_i32)]
@@ -340,3 +342,14 @@ def paro_sparsify_angles(theta, n_keep: int) -> np.ndarray:
     out = np.zeros_like(theta)
     _check(load_library().paro_sparsify_angles(2 * half, K, _ptr(theta), int(n_keep), _ptr(out)))
     return out
+
+
+def paro_stream_copy(src, dst, blocks: int = 8192, stream=None):
+    """Plain device copy of ``src`` into ``dst`` (same byte size): the
+    measured HBM ceiling the memory-bound kernels are reported against."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same size")
+    _check(load_library().paro_stream_copy(_dptr(src, "src"), _dptr(dst, "dst"), nbytes, int(blocks),
+                                           _stream(stream)))
+    return dst

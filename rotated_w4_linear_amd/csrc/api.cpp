@@ -477,4 +477,23 @@ int paro_layer_loss(const paro_rotation* r, const uint16_t* x, const uint16_t* w
                         workspace, stream);
 }
 
+int paro_stream_copy(const void* src, void* dst, size_t bytes, int32_t blocks, hipStream_t stream) {
+  if (bytes == 0) return PARO_OK;
+  if (!src || !dst) {
+    set_error("paro_stream_copy: NULL pointer");
+    return PARO_ERR_NULL;
+  }
+  if (!aligned16(src) || !aligned16(dst) || (bytes & 15)) {
+    set_error("paro_stream_copy: pointers must be 16-byte aligned and bytes a multiple of 16");
+    return PARO_ERR_ALIGN;
+  }
+  if (blocks < 1 || blocks > (1 << 20)) {
+    set_error("paro_stream_copy: blocks must be in [1, 2^20]");
+    return PARO_ERR_SHAPE;
+  }
+  hipError_t e = launch_stream_copy(src, dst, bytes, blocks, stream);
+  if (e != hipSuccess) return hip_fail(e, "paro_stream_copy launch");
+  return PARO_OK;
+}
+
 }  // extern "C"

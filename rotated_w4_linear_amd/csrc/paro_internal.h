@@ -126,6 +126,8 @@ hipError_t launch_quantize(const paro_rotation* r, const uint16_t* w, int64_t N,
 //  * launch_transpose_pad: out [C][ldo] = in^T for in fp16 [R][C] (C even,
 //    ldo even, ldo >= R), zero in columns R .. ldo - 1.
 int nt_tiles(int64_t M, int64_t N);
+// Plain device copy (copy.hip): bytes % 16 == 0, 16-byte aligned pointers.
+hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, int blocks, hipStream_t stream);
 hipError_t launch_nt_gemm_f32(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb,
                               int64_t M, int64_t N, int64_t K, float* c, int64_t ldc,
                               hipStream_t stream);
