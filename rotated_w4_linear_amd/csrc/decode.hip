@@ -440,9 +440,14 @@ hipError_t launch_w4_decode(const uint16_t* x, const uint8_t* qweight, const uin
   if (M == 0) return hipSuccess;
   const int m = (int)M, n = (int)N, k = (int)d;
   const int gsh = group == 64 ? 0 : group == 128 ? 1 : 2;
-  // 64-channel workgroups when 128-channel ones would not give two per CU
+  // 64-channel workgroups when 128-channel ones would not give two per CU;
+  // but with the transform fused and more than 4 tokens, every workgroup's
+  // transform of its k-slice (an LDS-bound chain of exchanges) sits on the
+  // critical path, and 128-channel workgroups halve how often each segment is
+  // transformed (4096 -> 4096 at M = 16: 10.9 -> 10.0 us measured)
   const int64_t wg128 = ((N + 127) / 128) * ((d / 128 + DK_SEGS - 1) / DK_SEGS);
-  const bool tj1 = wg128 < 384, small = M <= 4;
+  const bool small = M <= 4;
+  const bool tj1 = wg128 < 384 && (small || r == nullptr);
   // full slices and aligned bases: vector scale / zero loads
   if (group == 128 && (d / 128) % DK_SEGS == 0 && ((uintptr_t)scales & 7) == 0 &&
       ((uintptr_t)zeros & 3) == 0) {

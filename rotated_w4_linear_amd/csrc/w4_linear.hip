@@ -239,29 +239,50 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
     if (kg == 1) return;
   }
 
-  // epilogue: acc[j][mm][e] = C[n = n0 + 32 j + 8 (e/4) + 4 g + e%4][m = m0 + 32 mm + l32]
+  // epilogue: acc[j][mm][e] = C[n = n0 + 32 j + 8 (e/4) + 4 g + e%4][m = m0 + 32 mm + l32].
+  // Each wavefront stages its 64 (n) x 64 (m) output blocks through an 8 KB LDS
+  // region of its own (the operand stages are free after the last barrier) as
+  // fp16 rows of 64 outputs, 16-byte chunk c of row r at position c ^ (r & 7),
+  // and then stores whole 128-byte rows: lane l writes chunk l % 8 of row l / 8
+  // of each group of 8 rows.
+  {
+    uint8_t* stage = w == 0 ? (uint8_t*)&X0[0][0] : w == 1 ? (uint8_t*)&X1[0][0]
+                   : w == 2 ? (uint8_t*)&W0[0][0] : (uint8_t*)&W1[0][0];
+    constexpr int PASSES = MT / 2;  // 64 tokens per pass
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+    for (int ps = 0; ps < PASSES; ++ps) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int n = n0 + 32 * j + 8 * q + 4 * g;
-      if (n >= N) continue;
-      float bv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (bias) {
-        const uint2 braw = *(const uint2*)(bias + n);
-        bv[0] = half_lo(braw.x);
-        bv[1] = half_hi(braw.x);
-        bv[2] = half_lo(braw.y);
-        bv[3] = half_hi(braw.y);
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nl = 32 * j + 8 * q + 4 * g;  // local output channel of e = 4 q
+          float b4[4] = {0.f, 0.f, 0.f, 0.f};
+          if (bias && n0 + nl < N) {
+            const uint2 braw = *(const uint2*)(bias + n0 + nl);
+            b4[0] = half_lo(braw.x);
+            b4[1] = half_hi(braw.x);
+            b4[2] = half_lo(braw.y);
+            b4[3] = half_hi(braw.y);
+          }
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int mm = 2 * ps + t;
+            const int rl = 32 * t + l32;  // row of the staged block
+            uint2 pk;
+            pk.x = half_bits(acc[j][mm][4 * q + 0] + b4[0]) | (half_bits(acc[j][mm][4 * q + 1] + b4[1]) << 16);
+            pk.y = half_bits(acc[j][mm][4 * q + 2] + b4[2]) | (half_bits(acc[j][mm][4 * q + 3] + b4[3]) << 16);
+            const int c = nl >> 3;  // 16-byte chunk, 8-byte half (nl >> 2) & 1
+            *(uint2*)(stage + rl * 128 + ((c ^ (rl & 7)) << 4) + (((nl >> 2) & 1) << 3)) = pk;
+          }
+        }
       }
+      // (the region is this wavefront's own: its LDS accesses complete in order)
 #pragma unroll
-      for (int mm = 0; mm < MT; ++mm) {
-        const int m = m0 + 32 * mm + l32;
-        if (m >= M) continue;
-        uint2 pk;
-        pk.x = half_bits(acc[j][mm][4 * q + 0] + bv[0]) | (half_bits(acc[j][mm][4 * q + 1] + bv[1]) << 16);
-        pk.y = half_bits(acc[j][mm][4 * q + 2] + bv[2]) | (half_bits(acc[j][mm][4 * q + 3] + bv[3]) << 16);
-        *(uint2*)(y + (size_t)m * N + n) = pk;
+      for (int rr = 0; rr < 8; ++rr) {
+        const int rl = 8 * rr + (lane >> 3), c = lane & 7;
+        const u4 v = *(const u4*)(stage + rl * 128 + ((c ^ (rl & 7)) << 4));
+        const int m = m0 + 64 * ps + rl, n = n0 + 8 * c;
+        if (m < M && n < N) *(u4*)(y + (size_t)m * N + n) = v;
       }
     }
   }
