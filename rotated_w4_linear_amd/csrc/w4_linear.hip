@@ -65,6 +65,12 @@ constexpr int kWaitVmLgkm0 = 0x70;
 // on MI355X, 64-token tiles win at 128 tiles (1024 x 4096 -> 4096: 699
 // against 581 TFLOP/s) and lose at 256 (2048 x 4096 -> 4096: 760 against 918).
 constexpr int64_t kHalfTileBelow = 256;
+// 256 x 256 tiles (at 256 tokens) from which the wide kernel is used: measured
+// on MI355X, 4096 x 4096 -> 4096 (256 tiles): 128 against 135 us; 2048 x
+// 14336 -> 4096 (128 tiles) runs 372 against 288 us
+constexpr int64_t kWideMinTiles = 256;
+// n tiles of 32 channels per wavefront in the wide kernel
+constexpr int kWideWN = 2;
 
 // MT: 32-token m tiles per wavefront (4: 128-token workgroup tiles; 2: 64,
 // for layers with few output tiles).
@@ -288,6 +294,261 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
   }
 }
 
+// --------------------------------------------------------------------------
+// prefill, layers with many output tiles: 256 (m) x 256 (n) workgroup tiles
+// and one wavefront per SIMD, owning a 128 (m) x 128 (n) tile (4 x 4
+// accumulator tiles, 256 fp32 per lane). Against the 128 x 64 wavefront tiles
+// above, each X' fragment read from LDS feeds twice as many MFMAs, and the
+// wavefront's own instruction stream overlaps its dequantization with its
+// MFMAs. Staging, swizzles, the k order and the dequantization are those of
+// w4_gemm_kernel; the X' stage holds 256 rows (32 KB).
+// --------------------------------------------------------------------------
+constexpr int GW_M = 256;
+constexpr int GW_XSTAGE = GW_M * GB_K;  // halfs per X' stage (32 KB)
+
+// Instruction order inside a scheduling region of 16 MFMAs: the region's ND
+// LDS reads first, the first NW MFMAs alone (while those reads return), then
+// each MFMA followed by up to NV vector instructions (the next step's
+// dequantization).
+template <int ND, int NW, int NV>
+__device__ __forceinline__ void sched_order() {
+  __builtin_amdgcn_sched_group_barrier(0x100, ND, 0);
+  if constexpr (NW > 0) __builtin_amdgcn_sched_group_barrier(0x008, NW, 0);
+#pragma unroll
+  for (int k = NW; k < 16; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+  }
+}
+
+// WN: 32-channel n tiles per wavefront (4: 128 (n) x 128 (m) wavefront tiles,
+// 2: 64 (n) x 256 (m)); MTW = 16 / WN m tiles of 32 tokens.
+template <int WN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
+void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ qw,
+                         const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zr,
+                         const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N,
+                         int d, int gsh, int mblk, int nblk) {
+  __shared__ __attribute__((aligned(1024))) _Float16 X0[GW_XSTAGE], X1[GW_XSTAGE];
+  __shared__ __attribute__((aligned(1024))) u4 W0[GB_WSTAGE], W1[GB_WSTAGE];
+  __shared__ __attribute__((aligned(16))) uint32_t S0[GB_N], S1[GB_N], Z0[GB_N], Z1[GB_N];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront 0..3
+  constexpr int MTW = 16 / WN, NWAV = 8 / WN;               // m tiles; wavefronts along n
+  const int wn = w % NWAV, wm = w / NWAV;                   // the wavefront's n and m blocks
+  // XCD-aware tile order, as in w4_gemm_kernel
+  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  const int nbx = (nblk - xcd + 7) >> 3;
+  if (nbx <= 0) return;
+  const int mg = idx / (8 * nbx), rem = idx - mg * 8 * nbx;
+  const int nb = xcd + 8 * (rem / 8);
+  const int mb = mg * 8 + (rem & 7);
+  if (mb >= mblk) return;
+  const int m0 = mb * GW_M;
+  const int nw0 = nb * GB_N;
+  const int groups = d >> (6 + gsh);
+  const int KT = d / GB_K;
+  const int l32 = lane & 31, g = lane >> 5;
+
+  // buffer resources at the tile's first row (byte offsets < 2^31: d <= 2^21,
+  // checked on the host); rows past M or N are clamped to the last row
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(x + (size_t)m0 * d), (short)0, min(M - m0, GW_M) * d * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(qw + (size_t)nw0 * (d >> 1)), (short)0, min(N - nw0, GB_N) * (d >> 1), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(sc + (size_t)nw0 * groups), (short)0, min(N - nw0, GB_N) * groups * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(zr + (size_t)nw0 * groups), (short)0, min(N - nw0, GB_N) * groups, kRsrcWord3);
+  // X' DMA c (0..7) of wavefront w fills tile rows 8 (8 w + c) .. + 7
+  uint32_t xoff[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int r = 8 * (8 * w + c) + (lane >> 3);
+    const int row = min(r, M - 1 - m0);
+    xoff[c] = (uint32_t)(row * d + 8 * ((lane & 7) ^ ((r >> 1) & 7))) * 2u;
+  }
+  // code DMA c (0..1) of wavefront w fills tile rows 32 (2 w + c) .. + 31
+  uint32_t woff[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int r = 32 * (2 * w + c) + (lane >> 1);
+    const int row = min(r, N - 1 - nw0);
+    woff[c] = (uint32_t)(row * (d >> 1) + 16 * ((lane & 1) ^ ((r >> 3) & 1)));
+  }
+  // group scale and zero: lane l of wavefront w fetches row 64 w + l
+  const uint32_t szrow = (uint32_t)(min(64 * w + lane, N - 1 - nw0) * groups);
+
+  // the DMA of one k-tile: twelve load-to-LDS instructions per lane
+  auto dma = [&](int kt, _Float16* xs, u4* ws, uint32_t* ss_l, uint32_t* zs_l) {
+    const uint32_t gi = (uint32_t)(kt >> gsh);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)&ss_l[64 * w], 2, (szrow + gi) * 2u, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_void*)&zs_l[64 * w], 1, szrow + gi, 0, 0, 0);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)&xs[(8 * w + c) * 64 * 8], 16, xoff[c],
+                                               kt * GB_K * 2, 0, 0);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)&ws[(2 * w + c) * 64], 16, woff[c],
+                                               kt * (GB_K / 2), 0, 0);
+  };
+
+  const uint32_t one = fp16_1024_pair();
+  // (arrays are sized for the largest WN and MTW and used up to WN, MTW: the
+  // host pass of hipcc cannot instantiate lambdas capturing arrays of
+  // template-dependent size)
+  f16v acc[4][8];  // [n tile j][m tile mm]
+#pragma unroll
+  for (int j = 0; j < WN; ++j)
+#pragma unroll
+    for (int mm = 0; mm < MTW; ++mm)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[j][mm][e] = 0.0f;
+
+  // A k-tile's per-row operands: the 32 codes of each of the wavefront's WN
+  // n tiles and their group's scale and zero, in the forms dequant8 takes.
+  struct Params {
+    u4 wf[4];
+    h2 ss[4], zz[4], ss16[4], zz16[4];
+  };
+  auto load_params = [&](const u4* wl, const uint32_t* ss_l, const uint32_t* zs_l, Params& p) {
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      const int r = 32 * WN * wn + 32 * j + l32;
+      p.wf[j] = wl[2 * r + (g ^ ((r >> 3) & 1))];
+      p.ss[j] = splat2(__builtin_bit_cast(_Float16, (uint16_t)(ss_l[r] & 0xffffu)));
+      p.ss16[j] = p.ss[j] * splat2((_Float16)0.0625f);
+      const float zf = (float)(zs_l[r] & 0xffu);
+      p.zz[j] = splat2((_Float16)(1024.0f + zf));
+      p.zz16[j] = splat2((_Float16)(1024.0f + 16.0f * zf));
+    }
+  };
+  // X' fragments of MFMA step i (0..3) of a k-tile for the MTW m tiles
+  auto read_b = [&](const _Float16* xb, int i, h8* bf) {
+#pragma unroll
+    for (int mm = 0; mm < MTW; ++mm) {
+      const int r = 32 * MTW * wm + 32 * mm + l32;
+      bf[mm] = *(const h8*)(xb + r * GB_K + 8 * ((4 * g + i) ^ ((r >> 1) & 7)));
+    }
+  };
+  auto deq = [&](const Params& p, int i, h8* af) {
+#pragma unroll
+    for (int j = 0; j < WN; ++j) af[j] = dequant8(p.wf[j][i], p.zz[j], p.ss[j], p.zz16[j], p.ss16[j], one);
+  };
+  auto mma = [&](const h8* af, const h8* bf) {
+#pragma unroll
+    for (int j = 0; j < WN; ++j)
+#pragma unroll
+      for (int mm = 0; mm < MTW; ++mm)
+        acc[j][mm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[j], bf[mm], acc[j][mm], 0, 0, 0);
+  };
+  // Pipeline: while the MFMAs of step i of k-tile kt run, the wavefront reads
+  // and dequantizes the operands of step i + 1. After step 2 it waits for the
+  // DMA of k-tile kt + 1 and the barrier, so that step 3 overlaps the first
+  // operands of kt + 1 (read from the other stage). Past that barrier every
+  // wavefront has read all it needs of k-tile kt, so the DMA of kt + 2 into
+  // kt's stage goes out there, a whole k-tile before it is waited for; past
+  // the last tile it reloads the last tile, which is read but not used.
+  Params P, Pn;
+  h8 a[4], b[8], an[4], bn[8];
+  auto tile = [&](int kt, _Float16* xb, u4* wl, uint32_t* sb, uint32_t* zb, const _Float16* xn,
+                  const u4* wnx, const uint32_t* sn, const uint32_t* zn) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      read_b(xb, i + 1, bn);
+      deq(P, i + 1, an);
+      mma(a, b);
+      sched_order<MTW, 0, WN + 1>();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        if (t < WN) a[t] = an[t];
+        if (t < MTW) b[t] = bn[t];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+    __builtin_amdgcn_s_barrier();
+    dma(min(kt + 2, KT - 1), xb, wl, sb, zb);
+    __builtin_amdgcn_sched_barrier(0);
+    load_params(wnx, sn, zn, Pn);
+    read_b(xn, 0, bn);
+    deq(Pn, 0, an);
+    mma(a, b);
+    sched_order<MTW + 3 * WN, 4, 2 * WN>();
+    __builtin_amdgcn_sched_barrier(0);
+    P = Pn;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (t < WN) a[t] = an[t];
+      if (t < MTW) b[t] = bn[t];
+    }
+  };
+
+  dma(0, X0, W0, S0, Z0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+  __builtin_amdgcn_s_barrier();
+  dma(min(1, KT - 1), X1, W1, S1, Z1);
+  load_params(W0, S0, Z0, P);
+  read_b(X0, 0, b);
+  deq(P, 0, a);
+  for (int kt = 0; kt < KT; kt += 2) {  // KT even (checked on the host)
+    tile(kt, X0, W0, S0, Z0, X1, W1, S1, Z1);
+    tile(kt + 1, X1, W1, S1, Z1, X0, W0, S0, Z0);
+  }
+  // the last tile's step 3 read a stage that the epilogue below overwrites
+  __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+  __builtin_amdgcn_s_barrier();
+
+  // epilogue: acc[j][mm][e] = C[n = n0 + 32 j + 8 (e/4) + 4 g + e%4][m = mw0 + 32 mm + l32],
+  // staged per wavefront through an 8 KB LDS region of its own (a quarter of
+  // the X' stage 0, free after the last barrier) in 64 x 64 blocks, as in
+  // w4_gemm_kernel
+  const int n0 = nw0 + 32 * WN * wn, mw0 = m0 + 32 * MTW * wm;
+  uint8_t* stage = (uint8_t*)X0 + 8192 * w;
+#pragma unroll
+  for (int jh = 0; jh < WN / 2; ++jh) {
+#pragma unroll
+    for (int ps = 0; ps < MTW / 2; ++ps) {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * jh + jj;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nl = 32 * jj + 8 * q + 4 * g;  // channel of e = 4 q inside the 64-channel block
+          const int n = n0 + 64 * jh + nl;
+          float b4[4] = {0.f, 0.f, 0.f, 0.f};
+          if (bias && n < N) {
+            const uint2 braw = *(const uint2*)(bias + n);
+            b4[0] = half_lo(braw.x);
+            b4[1] = half_hi(braw.x);
+            b4[2] = half_lo(braw.y);
+            b4[3] = half_hi(braw.y);
+          }
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int mm = 2 * ps + t;
+            const int rl = 32 * t + l32;
+            uint2 pk;
+            pk.x = half_bits(acc[j][mm][4 * q + 0] + b4[0]) | (half_bits(acc[j][mm][4 * q + 1] + b4[1]) << 16);
+            pk.y = half_bits(acc[j][mm][4 * q + 2] + b4[2]) | (half_bits(acc[j][mm][4 * q + 3] + b4[3]) << 16);
+            const int c = nl >> 3;
+            *(uint2*)(stage + rl * 128 + ((c ^ (rl & 7)) << 4) + (((nl >> 2) & 1) << 3)) = pk;
+          }
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const int rl = 8 * rr + (lane >> 3), c = lane & 7;
+        const u4 v = *(const u4*)(stage + rl * 128 + ((c ^ (rl & 7)) << 4));
+        const int m = mw0 + 64 * ps + rl, n = n0 + 64 * jh + 8 * c;
+        if (m < M && n < N) *(u4*)(y + (size_t)m * N + n) = v;
+      }
+    }
+  }
+}
+
 template <int KS, int MT>
 void launch_gemm(unsigned blocks, hipStream_t stream, const uint16_t* x, const uint8_t* qweight,
                  const uint16_t* scales, const uint8_t* zeros, const uint16_t* bias, uint16_t* y,
@@ -315,6 +576,14 @@ hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint1
   // too few tiles to give every SIMD two wavefronts: split k inside the workgroup
   const bool ks2 = tiles < 512 && (d / GB_K) % 2 == 0 && d / GB_K >= 4;
   const unsigned g = (unsigned)blocks;
+  // layers with many 256 x 256 tiles take the one-wavefront-per-SIMD kernel
+  const int mblkw = (int)((M + GW_M - 1) / GW_M);
+  if (d <= (int64_t(1) << 21) && (d / GB_K) % 2 == 0 && (int64_t)mblkw * nblk >= kWideMinTiles) {
+    const int64_t bw = 8 * nbp * (((int64_t)mblkw + 7) / 8) * 8;
+    hipLaunchKernelGGL(w4_gemm_wide_kernel<kWideWN>, dim3((unsigned)bw), dim3(256), 0, stream, x, qweight, scales,
+                       zeros, bias, y, (int)M, (int)N, (int)d, gsh, mblkw, nblk);
+    return hipGetLastError();
+  }
   if (half && ks2) launch_gemm<2, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
   else if (half) launch_gemm<1, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
   else if (ks2) launch_gemm<2, 4>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);

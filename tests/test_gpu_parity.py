@@ -305,6 +305,18 @@ def test_linear_shapes_with_bias(paro, M, d, N):
     check_linear(paro, x, layer, bias=b)
 
 
+# shapes with at least 512 output tiles of 256 x 256 run the one-wavefront-per-SIMD
+# kernel: ragged in M and N, rows sampled (the last included), every column checked
+@pytest.mark.parametrize("M,d,N", [(4200, 256, 8208), (2600, 512, 13008), (2304, 1024, 14336)])
+def test_linear_wide_tiles(paro, M, d, N):
+    log(f"linear wide tiles M={M} d={d} N={N}")
+    x, layer, b = synthetic.linear_case(seed=M + d + N, M=M, d=d, N=N)
+    rows = np.sort(synthetic.rng_for(3510, M).choice(M, 64, replace=False))
+    rows[-1] = M - 1
+    check_linear(paro, x, layer, bias=b, rows=rows)
+    check_linear(paro, x, layer, rotated=False, rows=rows)
+
+
 def test_linear_gemv_vs_gemm_same_rows(paro):
     """Rows 0..15 through the GEMV (M = 16) and the GEMM (M = 40) agree."""
     x, layer, b = synthetic.linear_case(seed=5, M=40, d=1024, N=256)
