@@ -307,6 +307,9 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
 // --------------------------------------------------------------------------
 constexpr int GW_M = 256;
 constexpr int GW_XSTAGE = GW_M * GB_K;  // halfs per X' stage (32 KB)
+// groups per row up to which the wide kernel keeps all scales and zeros of its
+// tile in LDS (48 KB at 64)
+constexpr int kPanelGroups = 64;
 
 // Instruction order inside a scheduling region of 16 MFMAs: the region's ND
 // LDS reads first, the first NW MFMAs alone (while those reads return), then
@@ -347,7 +350,7 @@ __device__ __forceinline__ void sched_order() {
 
 // WN: 32-channel n tiles per wavefront (4: 128 (n) x 128 (m) wavefront tiles,
 // 2: 64 (n) x 256 (m)); MTW = 16 / WN m tiles of 32 tokens.
-template <int WN>
+template <int WN, bool PANEL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ qw,
                          const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zr,
@@ -356,6 +359,9 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
   __shared__ __attribute__((aligned(1024))) _Float16 X0[GW_XSTAGE], X1[GW_XSTAGE];
   __shared__ __attribute__((aligned(1024))) u4 W0[GB_WSTAGE], W1[GB_WSTAGE];
   __shared__ __attribute__((aligned(16))) uint32_t S0[GB_N], S1[GB_N], Z0[GB_N], Z1[GB_N];
+  // PANEL: the tile's scales and zeros of every group, loaded once
+  __shared__ __attribute__((aligned(1024))) uint16_t SP[PANEL ? GB_N * kPanelGroups : 8];
+  __shared__ __attribute__((aligned(1024))) uint8_t ZP[PANEL ? GB_N * kPanelGroups : 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront 0..3
@@ -404,12 +410,14 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
   // group scale and zero: lane l of wavefront w fetches row 64 w + l
   const uint32_t szrow = (uint32_t)(min(64 * w + lane, N - 1 - nw0) * groups);
 
-  // the DMA of one k-tile: twelve load-to-LDS instructions per lane; dma3(q)
-  // issues instructions 3 q .. 3 q + 2
+  // the DMA of one k-tile: twelve load-to-LDS instructions per lane (ten
+  // with PANEL: no scale and zero); dma3(q) issues instructions 3 q .. 3 q + 2
   auto dma3 = [&](int q, int kt, _Float16* xs, u4* ws, uint32_t* ss_l, uint32_t* zs_l) {
     const uint32_t gi = (uint32_t)(kt >> gsh);
 #pragma unroll
-    for (int c = 3 * q; c < 3 * q + 3; ++c) {
+    for (int c0 = 3 * q; c0 < 3 * q + 3; ++c0) {
+      const int c = c0 + (PANEL ? 2 : 0);
+      if (c >= 12) break;
       if (c == 0)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)&ss_l[64 * w], 2, (szrow + gi) * 2u, 0, 0, 0);
       else if (c == 1)
@@ -451,13 +459,19 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
     u4 wf[4];
     uint32_t s[4], z[4];
   };
-  auto read_raw = [&](const u4* wl, const uint32_t* ss_l, const uint32_t* zs_l, Raw& q) {
+  auto read_raw = [&](int kt, const u4* wl, const uint32_t* ss_l, const uint32_t* zs_l, Raw& q) {
+    const int gi = kt >> gsh;
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
       const int r = 32 * WN * wn + 32 * j + l32;
       q.wf[j] = wl[2 * r + (g ^ ((r >> 3) & 1))];
-      q.s[j] = ss_l[r];
-      q.z[j] = zs_l[r];
+      if constexpr (PANEL) {
+        q.s[j] = SP[r * groups + gi];
+        q.z[j] = ZP[r * groups + gi];
+      } else {
+        q.s[j] = ss_l[r];
+        q.z[j] = zs_l[r];
+      }
     }
   };
   auto convert = [&](const Raw& q, Params& p) {
@@ -471,9 +485,9 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
       p.zz16[j] = splat2((_Float16)(1024.0f + 16.0f * zf));
     }
   };
-  auto load_params = [&](const u4* wl, const uint32_t* ss_l, const uint32_t* zs_l, Params& p) {
+  auto load_params = [&](int kt, const u4* wl, const uint32_t* ss_l, const uint32_t* zs_l, Params& p) {
     Raw q;
-    read_raw(wl, ss_l, zs_l, q);
+    read_raw(kt, wl, ss_l, zs_l, q);
     convert(q, p);
   };
   // X' fragments of MFMA step i (0..3) of a k-tile for the MTW m tiles
@@ -532,7 +546,7 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
     // loads of the DMA of kt + 2 and a share of kt + 1's operand work
     const int kd = min(kt + 2, KT - 1);
     Raw raw;
-    read_raw(wnx, sn, zn, raw);
+    read_raw(kt + 1, wnx, sn, zn, raw);
     read_b(xn, 0, bn);
     mma4(0, a, b);
     dma3(0, kd, xb, wl, sb, zb);
@@ -563,11 +577,26 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
     }
   };
 
+  if constexpr (PANEL) {
+    // the scale panel [256 rows][groups] fp16 and the zero panel [256][groups]
+    // bytes are contiguous in global memory: copied in 4 KB rounds of 1 KB per
+    // wavefront (bytes past the tile's last row read as zero)
+    const __amdgpu_buffer_rsrc_t rsp = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(sc + (size_t)nw0 * groups), (short)0, min(N - nw0, GB_N) * groups * 2, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rzp = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(zr + (size_t)nw0 * groups), (short)0, min(N - nw0, GB_N) * groups, kRsrcWord3);
+    for (int q = 0; q < (groups + 7) / 8; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsp, (lds_void*)&SP[(4 * q + w) * 512], 16, lane * 16,
+                                               (4 * q + w) * 1024, 0, 0);
+    for (int q = 0; q < (groups + 15) / 16; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rzp, (lds_void*)&ZP[(4 * q + w) * 1024], 16, lane * 16,
+                                               (4 * q + w) * 1024, 0, 0);
+  }
   dma(0, X0, W0, S0, Z0);
   __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
   __builtin_amdgcn_s_barrier();
   dma(min(1, KT - 1), X1, W1, S1, Z1);
-  load_params(W0, S0, Z0, P);
+  load_params(0, W0, S0, Z0, P);
   read_b(X0, 0, b);
   deq(P, 0, a);
   for (int kt = 0; kt < KT; kt += 2) {  // KT even (checked on the host)
@@ -657,8 +686,12 @@ hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint1
   const int mblkw = (int)((M + GW_M - 1) / GW_M);
   if (d <= (int64_t(1) << 21) && (d / GB_K) % 2 == 0 && (int64_t)mblkw * nblk >= kWideMinTiles) {
     const int64_t bw = 8 * nbp * (((int64_t)mblkw + 7) / 8) * 8;
-    hipLaunchKernelGGL(w4_gemm_wide_kernel<kWideWN>, dim3((unsigned)bw), dim3(256), 0, stream, x, qweight, scales,
-                       zeros, bias, y, (int)M, (int)N, (int)d, gsh, mblkw, nblk);
+    if (d >> (6 + gsh) <= kPanelGroups)
+      hipLaunchKernelGGL((w4_gemm_wide_kernel<kWideWN, true>), dim3((unsigned)bw), dim3(256), 0, stream, x,
+                         qweight, scales, zeros, bias, y, (int)M, (int)N, (int)d, gsh, mblkw, nblk);
+    else
+      hipLaunchKernelGGL((w4_gemm_wide_kernel<kWideWN, false>), dim3((unsigned)bw), dim3(256), 0, stream, x,
+                         qweight, scales, zeros, bias, y, (int)M, (int)N, (int)d, gsh, mblkw, nblk);
     return hipGetLastError();
   }
   if (half && ks2) launch_gemm<2, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
