@@ -308,7 +308,8 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
 constexpr int GW_M = 256;
 constexpr int GW_XSTAGE = GW_M * GB_K;  // halfs per X' stage (32 KB)
 // groups per row up to which the wide kernel keeps all scales and zeros of its
-// tile in LDS (48 KB at 64)
+// tile in LDS (48 KB at 64; a multiple of 16 groups, scales and zeros 16-byte
+// aligned)
 constexpr int kPanelGroups = 64;
 
 // Instruction order inside a scheduling region of 16 MFMAs: the region's ND
@@ -359,9 +360,11 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
   __shared__ __attribute__((aligned(1024))) _Float16 X0[GW_XSTAGE], X1[GW_XSTAGE];
   __shared__ __attribute__((aligned(1024))) u4 W0[GB_WSTAGE], W1[GB_WSTAGE];
   __shared__ __attribute__((aligned(16))) uint32_t S0[GB_N], S1[GB_N], Z0[GB_N], Z1[GB_N];
-  // PANEL: the tile's scales and zeros of every group, loaded once
-  __shared__ __attribute__((aligned(1024))) uint16_t SP[PANEL ? GB_N * kPanelGroups : 8];
-  __shared__ __attribute__((aligned(1024))) uint8_t ZP[PANEL ? GB_N * kPanelGroups : 16];
+  // PANEL: the tile's scales and zeros of every group, loaded once and stored
+  // group-major ([group][256 rows]), so that the 32 rows one read spans are
+  // consecutive in LDS
+  __shared__ __attribute__((aligned(1024))) uint16_t SPT[PANEL ? GB_N * kPanelGroups : 8];
+  __shared__ __attribute__((aligned(1024))) uint8_t ZPT[PANEL ? GB_N * kPanelGroups : 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront 0..3
@@ -466,8 +469,8 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
       const int r = 32 * WN * wn + 32 * j + l32;
       q.wf[j] = wl[2 * r + (g ^ ((r >> 3) & 1))];
       if constexpr (PANEL) {
-        q.s[j] = SP[r * groups + gi];
-        q.z[j] = ZP[r * groups + gi];
+        q.s[j] = SPT[gi * GB_N + r];
+        q.z[j] = ZPT[gi * GB_N + r];
       } else {
         q.s[j] = ss_l[r];
         q.z[j] = zs_l[r];
@@ -578,19 +581,35 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
   };
 
   if constexpr (PANEL) {
-    // the scale panel [256 rows][groups] fp16 and the zero panel [256][groups]
-    // bytes are contiguous in global memory: copied in 4 KB rounds of 1 KB per
-    // wavefront (bytes past the tile's last row read as zero)
+    // lane l of wavefront w loads the scales (groups x fp16) and zeros (groups
+    // bytes) of tile row 64 w + l, its own rows, in 16-byte pieces (rows past N
+    // read as zero), and stores them group-major
     const __amdgpu_buffer_rsrc_t rsp = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(sc + (size_t)nw0 * groups), (short)0, min(N - nw0, GB_N) * groups * 2, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rzp = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(zr + (size_t)nw0 * groups), (short)0, min(N - nw0, GB_N) * groups, kRsrcWord3);
-    for (int q = 0; q < (groups + 7) / 8; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsp, (lds_void*)&SP[(4 * q + w) * 512], 16, lane * 16,
-                                               (4 * q + w) * 1024, 0, 0);
-    for (int q = 0; q < (groups + 15) / 16; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rzp, (lds_void*)&ZP[(4 * q + w) * 1024], 16, lane * 16,
-                                               (4 * q + w) * 1024, 0, 0);
+    const int rr = 64 * w + lane;
+    u4 sv[kPanelGroups / 8], zv[kPanelGroups / 16];
+#pragma unroll
+    for (int c = 0; c < kPanelGroups / 8; ++c)
+      if (c < groups / 8)
+        sv[c] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rsp, rr * groups * 2 + 16 * c, 0, 0));
+#pragma unroll
+    for (int c = 0; c < kPanelGroups / 16; ++c)
+      if (c < groups / 16)
+        zv[c] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rzp, rr * groups + 16 * c, 0, 0));
+#pragma unroll
+    for (int c = 0; c < kPanelGroups / 8; ++c)
+      if (c < groups / 8) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) SPT[(8 * c + t) * GB_N + rr] = (uint16_t)(sv[c][t >> 1] >> (16 * (t & 1)));
+      }
+#pragma unroll
+    for (int c = 0; c < kPanelGroups / 16; ++c)
+      if (c < groups / 16) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) ZPT[(16 * c + t) * GB_N + rr] = (uint8_t)(zv[c][t >> 2] >> (8 * (t & 3)));
+      }
   }
   dma(0, X0, W0, S0, Z0);
   __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
@@ -686,7 +705,8 @@ hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint1
   const int mblkw = (int)((M + GW_M - 1) / GW_M);
   if (d <= (int64_t(1) << 21) && (d / GB_K) % 2 == 0 && (int64_t)mblkw * nblk >= kWideMinTiles) {
     const int64_t bw = 8 * nbp * (((int64_t)mblkw + 7) / 8) * 8;
-    if (d >> (6 + gsh) <= kPanelGroups)
+    const int64_t groups = d >> (6 + gsh);
+    if (groups <= kPanelGroups && groups % 16 == 0 && ((uintptr_t)scales & 15) == 0 && ((uintptr_t)zeros & 15) == 0)
       hipLaunchKernelGGL((w4_gemm_wide_kernel<kWideWN, true>), dim3((unsigned)bw), dim3(256), 0, stream, x,
                          qweight, scales, zeros, bias, y, (int)M, (int)N, (int)d, gsh, mblkw, nblk);
     else
