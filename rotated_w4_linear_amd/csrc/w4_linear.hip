@@ -558,19 +558,19 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
     convert(raw, Pn);
     mma4(1, a, b);
     dma3(1, kd, xb, wl, sb, zb);
-    sched_chunk<0, 6, 3>();
+    sched_chunk<0, 3 * WN, 3>();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < WN / 2; ++j) an[j] = dequant8(Pn.wf[j][0], Pn.zz[j], Pn.ss[j], Pn.zz16[j], Pn.ss16[j], one);
     mma4(2, a, b);
     dma3(2, kd, xb, wl, sb, zb);
-    sched_chunk<0, 4, 3>();
+    sched_chunk<0, (13 * WN / 2 + 3) / 4, 3>();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = WN / 2; j < WN; ++j) an[j] = dequant8(Pn.wf[j][0], Pn.zz[j], Pn.ss[j], Pn.zz16[j], Pn.ss16[j], one);
     mma4(3, a, b);
     dma3(3, kd, xb, wl, sb, zb);
-    sched_chunk<0, 4, 3>();
+    sched_chunk<0, (13 * WN / 2 + 3) / 4, 3>();
     __builtin_amdgcn_sched_barrier(0);
     P = Pn;
 #pragma unroll
