@@ -305,9 +305,11 @@ def test_linear_shapes_with_bias(paro, M, d, N):
     check_linear(paro, x, layer, bias=b)
 
 
-# shapes with at least 512 output tiles of 256 x 256 run the one-wavefront-per-SIMD
-# kernel: ragged in M and N, rows sampled (the last included), every column checked
-@pytest.mark.parametrize("M,d,N", [(4200, 256, 8208), (2600, 512, 13008), (2304, 1024, 14336)])
+# shapes with at least 256 output tiles of 256 x 256 run the one-wavefront-per-SIMD
+# kernel (d = 2048 and 4096 with the scale and zero panel in LDS): ragged in M
+# and N, rows sampled (the last included), every column checked
+@pytest.mark.parametrize("M,d,N", [(4200, 256, 8208), (2600, 512, 13008), (2304, 1024, 14336),
+                                   (2600, 2048, 13008), (4100, 4096, 4112)])
 def test_linear_wide_tiles(paro, M, d, N):
     log(f"linear wide tiles M={M} d={d} N={N}")
     x, layer, b = synthetic.linear_case(seed=M + d + N, M=M, d=d, N=N)
