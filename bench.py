@@ -290,6 +290,33 @@ def copy_rate_gbps(torch, paro, nbytes, ring=4, reps=12):
     return best
 
 
+def mfma_rate_tflops(torch, paro, iters=20000, reps=3):
+    """fp16 matrix-core rate of the library's MFMA loop (paro_mfma_loop) on
+    uniform(-1, 1) operands, one workgroup of four wavefronts per CU: the
+    ceiling the matrix cores sustain under the chip's power limit (with random
+    data the clock falls well below the one the datasheet peak assumes).
+    Returns TFLOP/s, the best of a few runs."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    src = (torch.rand(1 << 20, device="cuda", generator=g) * 2 - 1).half()
+    out = torch.empty(cus * 256, dtype=torch.float32, device="cuda")
+    paro.paro_mfma_loop(src, out, cus, 500)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        paro.paro_mfma_loop(src, out, cus, iters)
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e)
+        best = max(best, cus * 4 * 16 * iters * 32768.0 / (ms * 1e-3) / 1e12)
+    del src, out
+    return best
+
+
 def cpu_baseline(x, layer, paro_q, N, d, target_s=12.0):
     """Time the oracle (rotation + fp64 linear) on a bounded sample of token rows."""
     import oracle
@@ -324,6 +351,7 @@ def bench_layer(args, paro, torch, name, x, layer):
     rot_bytes = 4.0 * M * d
     lin_tflops = flops / (tm["lin_ms"] * 1e-3) / 1e12
     copy_gbps, _ = copy_rate_gbps(torch, paro, M * d * 2)
+    mfma_ceiling = mfma_rate_tflops(torch, paro)
     rot_gbps = rot_bytes / (tm["rot_ms"] * 1e-3) / 1e9
     out = {
         "metric": METRIC,
@@ -347,8 +375,10 @@ def bench_layer(args, paro, torch, name, x, layer):
         "p10_p50_p90_ms": tm["pct"],
         "copy_same_bytes_gbps": round(copy_gbps, 1),
         "rotation_frac_of_copy": round(rot_gbps / copy_gbps, 4),
+        "mfma_ceiling_tflops": round(mfma_ceiling, 1),
         "roofline": {"bound": "mfma", "achieved": round(lin_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(lin_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                     "frac_of_mfma_ceiling": round(lin_tflops / mfma_ceiling, 4),
                      "traffic": traffic_for(f"w4_gemm:{name}")},
         "roofline_rotation": {"bound": "hbm", "achieved": round(rot_bytes / (tm["rot_ms"] * 1e-3) / 1e9, 1),
                               "peak": HBM_PEAK_GBPS, "unit": "GB/s",

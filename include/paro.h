@@ -428,6 +428,24 @@ int paro_sparsify_angles(int64_t d, int32_t K, const float* theta, int64_t n_kee
 int paro_stream_copy(const void* src, void* dst, size_t bytes, int32_t blocks, hipStream_t stream);
 
 /*
+ * Measurement: fp16 matrix-core throughput with operands in registers. Each
+ * of `blocks` workgroups runs one wavefront per SIMD (256 lanes); every
+ * wavefront runs `iters` rounds of 16 independent v_mfma_f32_32x32x16_f16
+ * (32768 flop each) on operands read once from src, then each lane writes the
+ * sum of its 256 fp32 accumulators to out[lane]. With random operands the
+ * rate is the ceiling the matrix cores sustain under the chip's power limit,
+ * which the prefill linear is reported against next to the datasheet peak; it
+ * takes no part in the method. With every operand 1.0, each output is
+ * 4096 * iters.
+ *   src   device fp16 [n], 16-byte aligned, n a multiple of 8 in [8, 2^30];
+ *   out   device float [blocks * 256];
+ *   blocks 1 .. 2^16, iters >= 0.
+ * Asynchronous on stream. Errors: PARO_ERR_NULL, PARO_ERR_ALIGN,
+ * PARO_ERR_SHAPE, PARO_ERR_HIP.
+ */
+int paro_mfma_loop(const void* src, int64_t n, float* out, int32_t blocks, int32_t iters, hipStream_t stream);
+
+/*
  * Host-only view of the per-segment rotation schedule that
  * paro_rotation_create uploads (for testing the plan logic without a GPU).
  * Fills `out` (host memory of out_bytes) with the exact table image and writes

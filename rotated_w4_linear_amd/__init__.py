@@ -90,6 +90,8 @@ def load_library() -> ctypes.CDLL:
     lib.paro_sparsify_angles.argtypes = [c_i64, c_i32, vp, c_i64, vp]
     lib.paro_stream_copy.restype = ctypes.c_int
     lib.paro_stream_copy.argtypes = [vp, vp, c_size, c_i32, vp]
+    lib.paro_mfma_loop.restype = ctypes.c_int
+    lib.paro_mfma_loop.argtypes = [vp, c_i64, vp, c_i32, c_i32, vp]
     lib.paro_rotation_plan_host.restype = ctypes.c_int
     lib.paro_rotation_plan_host.argtypes = [c_i64, c_i32, c_i32, vp, vp, vp, vp, c_size,
                                             ctypes.POINTER(c_size), ctypes.POINTER(c_i32)]
@@ -353,3 +355,18 @@ def paro_stream_copy(src, dst, blocks: int = 8192, stream=None):
     _check(load_library().paro_stream_copy(_dptr(src, "src"), _dptr(dst, "dst"), nbytes, int(blocks),
                                            _stream(stream)))
     return dst
+
+
+def paro_mfma_loop(src, out, blocks: int, iters: int, stream=None):
+    """fp16 matrix-core loop on operands read from ``src`` (fp16, a multiple of
+    8 elements); ``out`` holds blocks * 256 floats: the measured matrix-core
+    ceiling the prefill linear is reported against."""
+    import torch
+    if src.numel() % 8:
+        raise ValueError("src must hold a multiple of 8 elements")
+    if out.numel() < int(blocks) * 256:
+        raise ValueError("out must hold blocks * 256 floats")
+    _check(load_library().paro_mfma_loop(_dptr(src, "src", torch.float16), src.numel(),
+                                         _dptr(out, "out", torch.float32), int(blocks), int(iters),
+                                         _stream(stream)))
+    return out

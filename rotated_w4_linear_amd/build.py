@@ -18,7 +18,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libparo.so")
 
 SOURCES = ["api.cpp", "plan.cpp", "pairs.cpp", "rotate.hip", "quantize.hip", "w4_linear.hip", "decode.hip",
-           "backward.hip", "layer_loss.hip", "noalloc.hip", "dense_gemm.hip", "copy.hip"]
+           "backward.hip", "layer_loss.hip", "noalloc.hip", "dense_gemm.hip", "measure.hip"]
 
 COMPILE_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -496,4 +496,22 @@ int paro_stream_copy(const void* src, void* dst, size_t bytes, int32_t blocks, h
   return PARO_OK;
 }
 
+int paro_mfma_loop(const void* src, int64_t n, float* out, int32_t blocks, int32_t iters, hipStream_t stream) {
+  if (!src || !out) {
+    set_error("paro_mfma_loop: NULL pointer");
+    return PARO_ERR_NULL;
+  }
+  if (!aligned16(src) || ((uintptr_t)out & 3)) {
+    set_error("paro_mfma_loop: src must be 16-byte aligned, out 4-byte aligned");
+    return PARO_ERR_ALIGN;
+  }
+  if (n < 8 || n % 8 || n > (int64_t(1) << 30) || blocks < 1 || blocks > (1 << 16) || iters < 0) {
+    set_error("paro_mfma_loop: n a multiple of 8 in [8, 2^30], blocks in [1, 2^16], iters >= 0");
+    return PARO_ERR_SHAPE;
+  }
+  hipError_t e = launch_mfma_loop(src, n / 8, out, blocks, iters, stream);
+  if (e != hipSuccess) return hip_fail(e, "paro_mfma_loop launch");
+  return PARO_OK;
+}
+
 }  // extern "C"

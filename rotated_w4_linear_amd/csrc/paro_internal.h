@@ -128,6 +128,7 @@ hipError_t launch_quantize(const paro_rotation* r, const uint16_t* w, int64_t N,
 int nt_tiles(int64_t M, int64_t N);
 // Plain device copy (copy.hip): bytes % 16 == 0, 16-byte aligned pointers.
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, int blocks, hipStream_t stream);
+hipError_t launch_mfma_loop(const void* src, int64_t n8, float* out, int blocks, int iters, hipStream_t stream);
 hipError_t launch_nt_gemm_f32(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb,
                               int64_t M, int64_t N, int64_t K, float* c, int64_t ldc,
                               hipStream_t stream);

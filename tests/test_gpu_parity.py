@@ -792,3 +792,31 @@ def test_layer_loss_workspace_reused_across_sizes(paro):
         metrics.assert_within(host(dal), ref[2], tal, "dalpha")
         assert not host(ws[:16384]).any(), "arrival counters not left at zero"
     r.close()
+
+
+# ----------------------------------------------------------------------------
+# measurement kernels (the ceilings the benchmark reports next to the peaks)
+# ----------------------------------------------------------------------------
+
+def test_stream_copy_copies(paro):
+    log("measurement: device copy")
+    src = torch.randint(0, 256, (3 << 20,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros_like(src)
+    paro.paro_stream_copy(src, dst, blocks=300)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+
+
+def test_mfma_loop_counts_every_product(paro):
+    """With every operand 1.0 each of a lane's 256 accumulators gains 16 per
+    round, so each output is 4096 * iters exactly."""
+    log("measurement: MFMA loop")
+    src = torch.ones(4096, dtype=torch.float16, device="cuda")
+    out = torch.full((7 * 256,), -1.0, dtype=torch.float32, device="cuda")
+    paro.paro_mfma_loop(src, out, 7, 100)
+    torch.cuda.synchronize()
+    assert torch.all(out == 4096.0 * 100)
+    lib = paro.load_library()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    rc = lib.paro_mfma_loop(ctypes.c_void_p(src.data_ptr()), 12, ctypes.c_void_p(out.data_ptr()), 7, 1, stream)
+    assert paro.STATUS[rc] == "PARO_ERR_SHAPE"
