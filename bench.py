@@ -182,17 +182,18 @@ def time_layer(paro, torch, r, xs, qr, qp, steps, warmup, M, N, d):
     ring = len(xs)
     xr = torch.empty((M, d), dtype=torch.float16, device="cuda")
     y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    wsp = paro.new_workspace(None, M, N, d)  # the plain layer's (split-k partial tiles, or none)
     T = Timer(torch)
 
     def rotated_step(i):
         k = i % ring
         paro.paro_rotate(r, xs[k], xr)
         e1 = T.event()
-        paro.paro_w4_linear(None, xr, *qr[k], y=y)
+        paro.paro_w4_linear(None, xr, *qr[k], y=y, workspace=wsp)
         return e1
 
     def plain_step(i):
-        paro.paro_w4_linear(None, xs[i % ring], *qp[i % ring], y=y)
+        paro.paro_w4_linear(None, xs[i % ring], *qp[i % ring], y=y, workspace=wsp)
 
     settle(torch, [rotated_step, plain_step], warmup)
 

@@ -181,9 +181,13 @@ int paro_quantize_weights(const paro_rotation* r, const uint16_t* w, int64_t N, 
                           int32_t group, uint8_t* qweight, uint16_t* scales, uint8_t* zeros,
                           hipStream_t stream);
 
-/* Bytes of device workspace paro_w4_linear needs for this plan (NULL: plain
- * W4) and these sizes. 0 means the call needs no workspace (M > 16 with
- * r == NULL). */
+/* Bytes of device workspace with which paro_w4_linear runs its fastest
+ * kernels for this plan (NULL: plain W4) and these sizes; 0 means the call
+ * uses no workspace. For M > 16 on layers with fewer than 256 output tiles of
+ * 256 x 256 (at least 16) this includes fp32 partial tiles (256 KB per tile
+ * and k-split) for splitting k across workgroups; paro_w4_linear also runs,
+ * with the 128 x 256-tile kernel, on the minimum: 16 KiB + M d 2 bytes
+ * (rounded up to 256) with a plan, none without. */
 size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t N, int64_t d);
 
 /*
@@ -203,9 +207,11 @@ size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t 
  *            quantization groups), else PARO_ERR_SHAPE.
  *   N % 16 == 0, d % 128 == 0, d % G == 0, M >= 0 (M == 0 is a no-op); N <= 2^30,
  *   d <= 2^22, M < 2^30, else PARO_ERR_UNSUPPORTED.
- *   workspace, workspace_bytes: device memory of at least
- *            paro_w4_linear_workspace_size(r, M, N, d) bytes, 256-byte
- *            aligned (may be NULL when that size is 0). Its first 16 KiB hold
+ *   workspace, workspace_bytes: device memory of
+ *            paro_w4_linear_workspace_size(r, M, N, d) bytes, or of at least
+ *            the minimum given there (M > 16: then without the k-split),
+ *            256-byte aligned (may be NULL when the size in use is 0;
+ *            smaller than the minimum: PARO_ERR_WORKSPACE). Its first 16 KiB hold
  *            arrival counters that must be zero before the first call that
  *            uses the workspace (zero-fill it once after allocating it); every
  *            call leaves them zero again. The rest is scratch. Calls that may
@@ -216,11 +222,17 @@ size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t 
  * plans of group 64 or 128 that execute at most 8 stages, applies the
  * transform to the activations inside the same kernel; other plans rotate
  * into the workspace first. M > 16 rotates into the workspace and then runs
- * the matrix-core kernel.
+ * a matrix-core kernel: 256 x 256 tiles from 256 such tiles; with fewer (at
+ * least 16) the same kernel with k split across 2 to 8 workgroups per tile,
+ * which meet through fp32 partial tiles in the workspace (the last to arrive
+ * adds them in split order), when the workspace holds them; else 128 x 256
+ * tiles.
  *
  * Arithmetic: X' exactly as paro_rotate computes it (fp16); fp32 accumulation
  * of exact fp16 products against the fp16 rounding of each dequantized weight
- * (q - z) * s, in an order that depends on M but not on timing; fp16 output.
+ * (q - z) * s, in an order that depends on the sizes (and for M > 16 on
+ * whether the workspace holds the k-split's partial tiles) but not on timing;
+ * fp16 output.
  * Errors: PARO_ERR_NULL, PARO_ERR_SHAPE, PARO_ERR_ALIGN, PARO_ERR_UNSUPPORTED,
  * PARO_ERR_WORKSPACE, PARO_ERR_HIP.
  */
@@ -240,9 +252,11 @@ int paro_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qwe
  *            the process ends; its address is looked up and its arrival
  *            counters cleared by paro_device_init (paro_rotation_create runs
  *            it), and every completed call leaves the counters zero again.
- *   Limit:   paro_w4_linear_workspace_size(r, M, N, d) must not exceed that
- *            size (for example M x d <= 32 Mi elements for a rotated layer
- *            with M > 16), else PARO_ERR_WORKSPACE and nothing is enqueued.
+ *   Limit:   the minimum workspace of paro_w4_linear (see
+ *            paro_w4_linear_workspace_size) must not exceed that size (for
+ *            example M x d <= 32 Mi elements for a rotated layer with
+ *            M > 16), else PARO_ERR_WORKSPACE and nothing is enqueued; the
+ *            k-split's partial tiles are used when they fit as well.
  *   Sharing: every call on one device uses that device's single array, so
  *            calls that may run at the same time on one device (several
  *            streams or threads) race and give wrong results: serialise them,

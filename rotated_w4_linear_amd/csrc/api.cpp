@@ -237,8 +237,9 @@ size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t 
     if (r && !decode_fuses_rotation(r)) bytes += round256((size_t)M * (size_t)d * 2);
     return bytes;
   }
-  if (!r) return 0;
-  return kDecodeCounterBytes + round256((size_t)M * (size_t)d * 2);
+  const size_t split = plan_w4_gemm(M, N, d).partial_bytes;
+  if (!r && !split) return 0;
+  return kDecodeCounterBytes + (r ? round256((size_t)M * (size_t)d * 2) : 0) + split;
 }
 
 }  // extern "C"
@@ -295,10 +296,20 @@ int check_w4_linear(const char* fn, const paro_rotation* r, const uint16_t* x,
   return PARO_OK;
 }
 
-// The launches of the W4 linear on a checked workspace of `need` bytes.
+// The smallest workspace paro_w4_linear runs with: as reported for M <= 16,
+// the transformed activations (and the counters before them) for M > 16; the
+// partial tiles of the split large-batch kernel only speed the call up.
+size_t w4_linear_min_workspace(const paro_rotation* r, int64_t M, int64_t N, int64_t d) {
+  if (M <= kDecodeMaxM || M <= 0) return paro_w4_linear_workspace_size(r, M, N, d);
+  if (!r) return 0;
+  return kDecodeCounterBytes + (((size_t)M * (size_t)d * 2 + 255) & ~(size_t)255);
+}
+
+// The launches of the W4 linear on a checked workspace ws of ws_bytes bytes
+// (at least w4_linear_min_workspace; NULL when that is 0).
 int run_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qweight,
                   const uint16_t* scales, const uint8_t* zeros, const uint16_t* bias, uint16_t* y,
-                  int64_t M, int64_t N, int64_t d, int32_t group, char* ws, size_t need,
+                  int64_t M, int64_t N, int64_t d, int32_t group, char* ws, size_t ws_bytes,
                   hipStream_t stream) {
   hipError_t e = hipSuccess;
   if (M <= kDecodeMaxM) {
@@ -306,7 +317,7 @@ int run_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qwei
     const uint16_t* xin = x;
     if (r && !decode_fuses_rotation(r)) {
       // stand-alone transform into the workspace tail, then the plain kernel
-      uint16_t* xr = (uint16_t*)(ws + need - (((size_t)M * (size_t)d * 2 + 255) & ~(size_t)255));
+      uint16_t* xr = (uint16_t*)(ws + ws_bytes - (((size_t)M * (size_t)d * 2 + 255) & ~(size_t)255));
       e = launch_rotate(r, x, xr, M, stream);
       if (e != hipSuccess) return hip_fail(e, "paro_w4_linear rotate launch");
       xin = xr;
@@ -315,13 +326,18 @@ int run_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qwei
     e = launch_w4_decode(xin, qweight, scales, zeros, bias, y, M, N, d, group, fused, ws, stream);
   } else {
     const uint16_t* xin = x;
+    const size_t xbytes = r ? (((size_t)M * (size_t)d * 2 + 255) & ~(size_t)255) : 0;
     if (r) {
       uint16_t* xr = (uint16_t*)(ws + kDecodeCounterBytes);
       e = launch_rotate(r, x, xr, M, stream);
       if (e != hipSuccess) return hip_fail(e, "paro_w4_linear rotate launch");
       xin = xr;
     }
-    e = launch_w4_gemm(xin, qweight, scales, zeros, bias, y, M, N, d, group, stream);
+    // split-k partial tiles after the counters and X', when the workspace holds them
+    const GemmPlan plan = plan_w4_gemm(M, N, d);
+    const bool split = plan.partial_bytes && ws && ws_bytes >= kDecodeCounterBytes + xbytes + plan.partial_bytes;
+    e = launch_w4_gemm(xin, qweight, scales, zeros, bias, y, M, N, d, group, split ? (uint32_t*)ws : nullptr,
+                       split ? (float*)(ws + kDecodeCounterBytes + xbytes) : nullptr, stream);
   }
   if (e != hipSuccess) return hip_fail(e, "paro_w4_linear launch");
   return PARO_OK;
@@ -340,19 +356,17 @@ int paro_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qwe
   int st = check_w4_linear("paro_w4_linear", r, x, qweight, scales, zeros, bias, y, M, N, d, group,
                            &noop);
   if (st != PARO_OK || noop) return st;
-  const size_t need = paro_w4_linear_workspace_size(r, M, N, d);
-  if (need) {
-    if (!workspace || workspace_bytes < need) {
-      set_error("paro_w4_linear: workspace missing or smaller than paro_w4_linear_workspace_size");
-      return PARO_ERR_WORKSPACE;
-    }
-    if ((uintptr_t)workspace & 255) {
-      set_error("paro_w4_linear: workspace must be 256-byte aligned");
-      return PARO_ERR_ALIGN;
-    }
+  const size_t need = w4_linear_min_workspace(r, M, N, d);
+  if (need && (!workspace || workspace_bytes < need)) {
+    set_error("paro_w4_linear: workspace missing or smaller than the minimum (see paro_w4_linear_workspace_size)");
+    return PARO_ERR_WORKSPACE;
+  }
+  if (workspace && ((uintptr_t)workspace & 255)) {
+    set_error("paro_w4_linear: workspace must be 256-byte aligned");
+    return PARO_ERR_ALIGN;
   }
   return run_w4_linear(r, x, qweight, scales, zeros, bias, y, M, N, d, group, (char*)workspace,
-                       need, stream);
+                       workspace ? workspace_bytes : 0, stream);
 }
 
 int paro_w4_linear_noalloc(const paro_rotation* r, const uint16_t* x, const uint8_t* qweight,
@@ -363,7 +377,7 @@ int paro_w4_linear_noalloc(const paro_rotation* r, const uint16_t* x, const uint
   int st = check_w4_linear("paro_w4_linear_noalloc", r, x, qweight, scales, zeros, bias, y, M, N, d,
                            group, &noop);
   if (st != PARO_OK || noop) return st;
-  const size_t need = paro_w4_linear_workspace_size(r, M, N, d);
+  const size_t need = w4_linear_min_workspace(r, M, N, d);
   if (need > kNoallocScratchBytes) {
     set_error("paro_w4_linear_noalloc: these sizes need " + std::to_string(need) +
               " bytes of workspace, more than the static scratch's " +
@@ -378,7 +392,7 @@ int paro_w4_linear_noalloc(const paro_rotation* r, const uint16_t* x, const uint
     set_error("paro_w4_linear_noalloc: paro_device_init has not run on this device");
     return PARO_ERR_UNSUPPORTED;
   }
-  return run_w4_linear(r, x, qweight, scales, zeros, bias, y, M, N, d, group, ws, need, stream);
+  return run_w4_linear(r, x, qweight, scales, zeros, bias, y, M, N, d, group, ws, kNoallocScratchBytes, stream);
 }
 
 

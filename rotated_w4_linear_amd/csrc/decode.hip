@@ -380,8 +380,6 @@ int xcd_dispatch_probe(int dev) {
   return PARO_OK;
 }
 
-namespace {
-
 // The hot path only reads what the probe recorded; a device never probed
 // takes the memory-side path, which is correct under any dispatch.
 bool xcd_dispatch_is_round_robin() {
@@ -389,6 +387,8 @@ bool xcd_dispatch_is_round_robin() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
   return g_xcd_state[dev].load(std::memory_order_acquire) == 1;
 }
+
+namespace {
 
 template <bool ROT, int KMAX, bool KEXACT, bool FAST, int T, int TJ, bool SZV>
 hipError_t launch_t(const uint16_t* x, const uint8_t* qw, const uint16_t* sc, const uint8_t* zr,

@@ -24,6 +24,8 @@
 // out), and the activation side's transform gradients. fp16 operands for dY E
 // cost nothing measurable: dY already carries the fp16 rounding of Y_q, whose
 // relative size against Y_q - Y is tens of times larger than fp16's own.
+#include <algorithm>
+
 #include "paro_internal.h"
 
 #pragma clang fp contract(off)
@@ -79,10 +81,10 @@ LossLayout loss_layout(const paro_rotation* r, int64_t M, int64_t N, int64_t d, 
     off += a256(bytes);
     return o;
   };
-  // the W4 linear's workspace first: its arrival counters then sit at offset 0
-  // for every M and N, so a workspace reused with other sizes still finds
-  // them zero
-  L.w4 = take(paro_w4_linear_workspace_size(nullptr, M, N, d));
+  // the W4 linear's workspace first, never shorter than its arrival
+  // counters: they then sit at offset 0 for every M and N, so a workspace
+  // reused with other sizes still finds them zero
+  L.w4 = take(std::max(paro_w4_linear_workspace_size(nullptr, M, N, d), kDecodeCounterBytes));
   L.xr = take((size_t)M * d * 2);
   L.yq = take((size_t)M * N * 2);
   L.part = take((size_t)nt_tiles(M, N) * 4);

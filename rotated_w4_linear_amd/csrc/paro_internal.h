@@ -137,10 +137,22 @@ hipError_t launch_nt_gemm_loss(const uint16_t* x, const uint16_t* w, int64_t M, 
                                hipStream_t stream);
 hipError_t launch_transpose_pad(const uint16_t* in, int64_t R, int64_t C, uint16_t* out, int64_t ldo,
                                 hipStream_t stream);
-// Large-batch linear (M > 16) on already transformed activations.
+// Large-batch linear (M > 16) on already transformed activations. The plan
+// says whether the 256 x 256-tile kernel runs and with how many k-splits
+// across workgroups; a split run needs the arrival counters (zero between
+// calls) and partial_bytes of fp32 partial tiles, and without them (NULL) the
+// layer takes the 128 x 256-tile kernel.
+struct GemmPlan {
+  bool wide = false;
+  int ksplit = 1;
+  size_t partial_bytes = 0;
+};
+GemmPlan plan_w4_gemm(int64_t M, int64_t N, int64_t d);
 hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
                           const uint8_t* zeros, const uint16_t* bias, uint16_t* y, int64_t M,
-                          int64_t N, int64_t d, int group, hipStream_t stream);
+                          int64_t N, int64_t d, int group, uint32_t* cnt, float* part, hipStream_t stream);
+// Whether paro_device_init found workgroup b running on XCD b % 8.
+bool xcd_dispatch_is_round_robin();
 
 // Small-batch linear (M <= 16). With r != NULL the activation transform runs
 // inside the kernel (requires decode_fuses_rotation(r)); ws is the workspace:

@@ -59,6 +59,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int GB_N = 256, GB_K = 64;
 constexpr int GB_WSTAGE = GB_N * 2;     // 16-byte chunks per weight stage (8 KB)
 constexpr int kRsrcWord3 = 0x00020000;  // gfx9 buffer resource word 3
+// buffer access cache bits: sc0 (skip the per-CU cache) for loads of data
+// another workgroup stored; sc0 | sc1 (memory-side) where workgroups may sit
+// on different XCDs
+constexpr int kAuxL2R = 1;
+constexpr int kAuxSysW = 17;
 // s_waitcnt immediate (gfx9 encoding): vmcnt(0) lgkmcnt(0), expcnt untouched
 constexpr int kWaitVmLgkm0 = 0x70;
 // Output tiles (at 128 tokens) below which 64-token tiles are used: measured
@@ -69,6 +74,15 @@ constexpr int64_t kHalfTileBelow = 256;
 // on MI355X, 4096 x 4096 -> 4096 (256 tiles): 128 against 135 us; 2048 x
 // 14336 -> 4096 (128 tiles) runs 372 against 288 us
 constexpr int64_t kWideMinTiles = 256;
+// with fewer (but at least kSplitMinTiles) the wide kernel splits k across up to
+// kMaxSplit workgroups per tile, each taking at least kMinSplitKT k-tiles: the
+// partial tiles (256 KB per workgroup, written and read back) pay off only on
+// long k. Measured on MI355X: 2048 x 14336 -> 4096 (two splits of 112 k-tiles)
+// 242 against 292 us for the 128 x 256-tile kernel; 2048 x 4096 -> 4096 (two
+// of 32) 88 against 73 us, 2048 x 4096 -> 1024 (eight of 8) 102 against 48 us
+constexpr int64_t kSplitMinTiles = 16;
+constexpr int kMaxSplit = 8;
+constexpr int64_t kMinSplitKT = 48;
 // n tiles of 32 channels per wavefront in the wide kernel
 constexpr int kWideWN = 2;
 
@@ -356,7 +370,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ qw,
                          const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zr,
                          const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N,
-                         int d, int gsh, int mblk, int nblk) {
+                         int d, int gsh, int mblk, int nblk, int ksplit, float* __restrict__ part,
+                         uint32_t* __restrict__ cnt, int sys) {
   __shared__ __attribute__((aligned(1024))) _Float16 X0[GW_XSTAGE], X1[GW_XSTAGE];
   __shared__ __attribute__((aligned(1024))) u4 W0[GB_WSTAGE], W1[GB_WSTAGE];
   __shared__ __attribute__((aligned(16))) uint32_t S0[GB_N], S1[GB_N], Z0[GB_N], Z1[GB_N];
@@ -370,8 +385,11 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront 0..3
   constexpr int MTW = 16 / WN, NWAV = 8 / WN;               // m tiles; wavefronts along n
   const int wn = w % NWAV, wm = w / NWAV;                   // the wavefront's n and m blocks
-  // XCD-aware tile order, as in w4_gemm_kernel
-  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  // XCD-aware tile order, as in w4_gemm_kernel; with ksplit > 1 the ksplit
+  // workgroups of a tile (consecutive slots of one XCD, so that they meet in
+  // its L2) each take 1 / ksplit of the k-tiles
+  const int xcd = blockIdx.x & 7, idx0 = blockIdx.x >> 3;
+  const int ks = idx0 % ksplit, idx = idx0 / ksplit;
   const int nbx = (nblk - xcd + 7) >> 3;
   if (nbx <= 0) return;
   const int mg = idx / (8 * nbx), rem = idx - mg * 8 * nbx;
@@ -381,7 +399,8 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
   const int m0 = mb * GW_M;
   const int nw0 = nb * GB_N;
   const int groups = d >> (6 + gsh);
-  const int KT = d / GB_K;
+  const int KT = d / GB_K / ksplit;  // k-tiles of this workgroup: kt0 .. kt0 + KT - 1
+  const int kt0 = ks * KT;
   const int l32 = lane & 31, g = lane >> 5;
 
   // buffer resources at the tile's first row (byte offsets < 2^31: d <= 2^21,
@@ -415,7 +434,8 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
 
   // the DMA of one k-tile: twelve load-to-LDS instructions per lane (ten
   // with PANEL: no scale and zero); dma3(q) issues instructions 3 q .. 3 q + 2
-  auto dma3 = [&](int q, int kt, _Float16* xs, u4* ws, uint32_t* ss_l, uint32_t* zs_l) {
+  auto dma3 = [&](int q, int ktl, _Float16* xs, u4* ws, uint32_t* ss_l, uint32_t* zs_l) {
+    const int kt = kt0 + ktl;  // global k-tile
     const uint32_t gi = (uint32_t)(kt >> gsh);
 #pragma unroll
     for (int c0 = 3 * q; c0 < 3 * q + 3; ++c0) {
@@ -462,8 +482,8 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
     u4 wf[4];
     uint32_t s[4], z[4];
   };
-  auto read_raw = [&](int kt, const u4* wl, const uint32_t* ss_l, const uint32_t* zs_l, Raw& q) {
-    const int gi = kt >> gsh;
+  auto read_raw = [&](int ktl, const u4* wl, const uint32_t* ss_l, const uint32_t* zs_l, Raw& q) {
+    const int gi = (kt0 + ktl) >> gsh;
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
       const int r = 32 * WN * wn + 32 * j + l32;
@@ -626,6 +646,72 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
   __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
   __builtin_amdgcn_s_barrier();
 
+  if (ksplit > 1) {
+    // Split k: every workgroup of the tile stores its fp32 partial tile
+    // (wavefront w's 256 accumulators per lane as [w][64 groups of 4][lane],
+    // 256 KB per workgroup) and counts itself in; the last to arrive adds the
+    // partial tiles in split order (so the sum does not depend on the order
+    // of arrival), resets the counter and runs the epilogue. As in the
+    // small-batch kernel, the workgroups of a tile share an XCD, so plain
+    // stores, an L2 atomic and loads that skip the per-CU cache suffice; where
+    // the dispatch rule is not established (sys) they go through memory.
+    __shared__ uint32_t s_last;
+    const int tile = mb * nblk + nb;
+    const size_t tile_floats = (size_t)GW_M * GB_N;
+    auto rsrc = [&](int k2) {
+      return __builtin_amdgcn_make_buffer_rsrc((void*)(part + ((size_t)tile * ksplit + k2) * tile_floats), (short)0,
+                                               (int)(tile_floats * 4), kRsrcWord3);
+    };
+    const __amdgpu_buffer_rsrc_t rmine = rsrc(ks);
+#pragma unroll
+    for (int f = 0; f < 64; ++f) {
+      const int j = f >> 5, mm = (f >> 2) & 7, q = f & 3;
+      const u4 v = __builtin_bit_cast(u4, f4{acc[j][mm][4 * q], acc[j][mm][4 * q + 1], acc[j][mm][4 * q + 2],
+                                             acc[j][mm][4 * q + 3]});
+      const int off = ((w * 64 + f) * 64 + lane) * 16;
+      if (sys) __builtin_amdgcn_raw_buffer_store_b128(v, rmine, off, 0, kAuxSysW);
+      else __builtin_amdgcn_raw_buffer_store_b128(v, rmine, off, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wavefront's stores have reached L2 / memory
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t old;
+      if (sys) old = __hip_atomic_fetch_add(&cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      else old = __hip_atomic_fetch_add(&cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = old == (uint32_t)(ksplit - 1);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    // 16 groups of 4 accumulators at a time, summed in split order from the
+    // stored partial tiles (this workgroup's own included)
+#pragma unroll
+    for (int f0 = 0; f0 < 64; f0 += 16) {
+      f4 r[16];
+      for (int k2 = 0; k2 < ksplit; ++k2) {
+        const __amdgpu_buffer_rsrc_t rk = rsrc(k2);
+        f4 v[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int off = ((w * 64 + f0 + t) * 64 + lane) * 16;
+          v[t] = __builtin_bit_cast(f4, sys ? __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, kAuxSysW)
+                                            : __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, kAuxL2R));
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) r[t] = k2 == 0 ? v[t] : r[t] + v[t];
+      }
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int f = f0 + t, j = f >> 5, mm = (f >> 2) & 7, q = f & 3;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[j][mm][4 * q + e] = r[t][e];
+      }
+    }
+    if (tid == 0) {
+      if (sys) __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      else __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
   // epilogue: acc[j][mm][e] = C[n = n0 + 32 j + 8 (e/4) + 4 g + e%4][m = mw0 + 32 mm + l32],
   // staged per wavefront through an 8 KB LDS region of its own (a quarter of
   // the X' stage 0, free after the last barrier) in 64 x 64 blocks, as in
@@ -684,9 +770,30 @@ void launch_gemm(unsigned blocks, hipStream_t stream, const uint16_t* x, const u
 
 }  // namespace
 
+GemmPlan plan_w4_gemm(int64_t M, int64_t N, int64_t d) {
+  GemmPlan p;
+  const int64_t nblk = (N + GB_N - 1) / GB_N, mblkw = (M + GW_M - 1) / GW_M;
+  const int64_t tiles = nblk * mblkw, kt = d / GB_K;
+  if (M <= 16 || d > (int64_t(1) << 21) || kt % 2 || d < 4 * GB_K) return p;
+  if (tiles >= kWideMinTiles) {
+    p.wide = true;
+    return p;
+  }
+  if (tiles < kSplitMinTiles) return p;
+  // split k across workgroups until the tiles fill one workgroup per CU
+  int ks = 1;
+  while (2 * ks <= kMaxSplit && tiles * 2 * ks <= kWideMinTiles && kt % (4 * ks) == 0 && kt / (2 * ks) >= kMinSplitKT)
+    ks *= 2;
+  if (ks < 2) return p;
+  p.wide = true;
+  p.ksplit = ks;
+  p.partial_bytes = (size_t)tiles * ks * GW_M * GB_N * 4;
+  return p;
+}
+
 hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
                           const uint8_t* zeros, const uint16_t* bias, uint16_t* y, int64_t M,
-                          int64_t N, int64_t d, int group, hipStream_t stream) {
+                          int64_t N, int64_t d, int group, uint32_t* cnt, float* part, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const int gsh = group == 64 ? 0 : group == 128 ? 1 : 2;
   const int nblk = (int)((N + GB_N - 1) / GB_N);
@@ -701,17 +808,23 @@ hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint1
   // too few tiles to give every SIMD two wavefronts: split k inside the workgroup
   const bool ks2 = tiles < 512 && (d / GB_K) % 2 == 0 && d / GB_K >= 4;
   const unsigned g = (unsigned)blocks;
-  // layers with many 256 x 256 tiles take the one-wavefront-per-SIMD kernel
-  const int mblkw = (int)((M + GW_M - 1) / GW_M);
-  if (d <= (int64_t(1) << 21) && (d / GB_K) % 2 == 0 && (int64_t)mblkw * nblk >= kWideMinTiles) {
-    const int64_t bw = 8 * nbp * (((int64_t)mblkw + 7) / 8) * 8;
+  // layers with many 256 x 256 tiles take the one-wavefront-per-SIMD kernel,
+  // layers with fewer the same kernel with k split across workgroups when the
+  // workspace holds the partial tiles
+  const GemmPlan plan = plan_w4_gemm(M, N, d);
+  if (plan.wide && (plan.ksplit == 1 || (cnt && part))) {
+    const int mblkw = (int)((M + GW_M - 1) / GW_M);
+    const int64_t bw = 8 * nbp * (((int64_t)mblkw + 7) / 8) * 8 * plan.ksplit;
     const int64_t groups = d >> (6 + gsh);
+    const int sys = plan.ksplit > 1 && !xcd_dispatch_is_round_robin();
     if (groups <= kPanelGroups && groups % 16 == 0 && ((uintptr_t)scales & 15) == 0 && ((uintptr_t)zeros & 15) == 0)
       hipLaunchKernelGGL((w4_gemm_wide_kernel<kWideWN, true>), dim3((unsigned)bw), dim3(256), 0, stream, x,
-                         qweight, scales, zeros, bias, y, (int)M, (int)N, (int)d, gsh, mblkw, nblk);
+                         qweight, scales, zeros, bias, y, (int)M, (int)N, (int)d, gsh, mblkw, nblk, plan.ksplit,
+                         part, cnt, sys);
     else
       hipLaunchKernelGGL((w4_gemm_wide_kernel<kWideWN, false>), dim3((unsigned)bw), dim3(256), 0, stream, x,
-                         qweight, scales, zeros, bias, y, (int)M, (int)N, (int)d, gsh, mblkw, nblk);
+                         qweight, scales, zeros, bias, y, (int)M, (int)N, (int)d, gsh, mblkw, nblk, plan.ksplit,
+                         part, cnt, sys);
     return hipGetLastError();
   }
   if (half && ks2) launch_gemm<2, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);

@@ -319,6 +319,47 @@ def test_linear_wide_tiles(paro, M, d, N):
     check_linear(paro, x, layer, rotated=False, rows=rows)
 
 
+# layers with 16 to 255 output tiles of 256 x 256 and long k split k across 2 to
+# 8 workgroups per tile (full workspace); with the minimum workspace the same
+# call runs the 128 x 256-tile kernel. Both against the oracle: the down-proj
+# configuration (two splits) and ragged shapes (two and four splits, with and
+# without the scale/zero panel).
+@pytest.mark.parametrize("M,d,N", [(2048, 14336, 4096), (1000, 8192, 2064), (600, 14336, 4096)])
+def test_linear_split_k(paro, M, d, N):
+    log(f"linear split-k M={M} d={d} N={N}")
+    x, layer, b = synthetic.linear_case(seed=M + d + N + 7, M=M, d=d, N=N)
+    G = layer.group
+    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, G)
+    qw, s, z = paro.paro_quantize_weights(r, dev(layer.w), G)
+    rows = np.sort(synthetic.rng_for(3520, M).choice(M, 48, replace=False))
+    rows[-1] = M - 1
+    ref = oracle.rotated_w4_linear(x[rows], host(qw), host(s), host(z), G, layer.pairs, layer.theta,
+                                   layer.alpha, b)
+    full = paro.paro_w4_linear_workspace_size(r, M, N, d)
+    minimum = 16384 + (M * d * 2 + 255) // 256 * 256
+    assert full > minimum
+    for nbytes in (full, minimum, full):
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        y = host(paro.paro_w4_linear(r, dev(x), qw, s, z, dev(b), group=G, workspace=ws))
+        assert np.all(np.isfinite(y[rows].astype(np.float32)))
+        metrics.assert_linear_close(y[rows], ref)
+        assert int(ws[:16384].count_nonzero()) == 0  # every call leaves the counters zero
+    # plain layer: the split run (default workspace) and, with no workspace at
+    # all, the 128 x 256-tile kernel
+    refp = oracle.rotated_w4_linear(x[rows], host(qw), host(s), host(z), G, bias=b)
+    yp = host(paro.paro_w4_linear(None, dev(x), qw, s, z, dev(b), group=G))
+    metrics.assert_linear_close(yp[rows], refp)
+    lib = paro.load_library()
+    xd, bd = dev(x), dev(b)
+    y0 = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    vp = ctypes.c_void_p
+    rc = lib.paro_w4_linear(None, vp(xd.data_ptr()), vp(qw.data_ptr()), vp(s.data_ptr()), vp(z.data_ptr()),
+                            vp(bd.data_ptr()), vp(y0.data_ptr()), M, N, d, G, None, 0,
+                            vp(torch.cuda.current_stream().cuda_stream))
+    assert paro.STATUS[rc] == "PARO_OK"
+    metrics.assert_linear_close(host(y0)[rows], refp)
+
+
 def test_linear_gemv_vs_gemm_same_rows(paro):
     """Rows 0..15 through the GEMV (M = 16) and the GEMM (M = 40) agree."""
     x, layer, b = synthetic.linear_case(seed=5, M=40, d=1024, N=256)

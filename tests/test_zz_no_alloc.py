@@ -38,10 +38,22 @@ def log(msg):
     print(msg, flush=True)
 
 
+SCRATCH_BYTES = (64 << 20) + 16384  # the static scratch (include/paro.h)
+
+
 def run_pair(paro, r, x, qw, s, z, bias, G):
-    M = x.shape[0]
+    M, d = x.shape
     N = qw.shape[0]
-    ref = paro.paro_w4_linear(r, x, qw, s, z, bias, group=G)
+    # the workspace entry point with the workspace the scratch stands for: the
+    # full size when it fits (the k-split's partial tiles included), else the
+    # minimum (for M > 16: X' only, or nothing for a plain layer)
+    full = paro.paro_w4_linear_workspace_size(r, M, N, d)
+    if full <= SCRATCH_BYTES:
+        nbytes = full
+    else:
+        nbytes = 16384 + (M * d * 2 + 255) // 256 * 256 if r is not None else 0
+    ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")[:nbytes]
+    ref = paro.paro_w4_linear(r, x, qw, s, z, bias, group=G, workspace=ws)
     y = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
     paro.paro_w4_linear_noalloc(r, x, qw, s, z, y, bias, group=G)
     torch.cuda.synchronize()
