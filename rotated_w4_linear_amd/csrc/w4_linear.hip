@@ -365,7 +365,9 @@ __device__ __forceinline__ void sched_order() {
 
 // WN: 32-channel n tiles per wavefront (4: 128 (n) x 128 (m) wavefront tiles,
 // 2: 64 (n) x 256 (m)); MTW = 16 / WN m tiles of 32 tokens.
-template <int WN, bool PANEL>
+// SPLIT: k split across ksplit > 1 workgroups per tile (a separate
+// instantiation, so that the reduction's registers do not weigh on the other).
+template <int WN, bool PANEL, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ qw,
                          const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zr,
@@ -375,9 +377,9 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
   __shared__ __attribute__((aligned(1024))) _Float16 X0[GW_XSTAGE], X1[GW_XSTAGE];
   __shared__ __attribute__((aligned(1024))) u4 W0[GB_WSTAGE], W1[GB_WSTAGE];
   __shared__ __attribute__((aligned(16))) uint32_t S0[GB_N], S1[GB_N], Z0[GB_N], Z1[GB_N];
-  // PANEL: the tile's scales and zeros of every group, loaded once and stored
-  // group-major ([group][256 rows]), so that the 32 rows one read spans are
-  // consecutive in LDS
+  // PANEL: the tile's scales and zeros of the groups this workgroup's k-tiles
+  // span, loaded once and stored group-major ([group][256 rows]), so that the
+  // 32 rows one read spans are consecutive in LDS
   __shared__ __attribute__((aligned(1024))) uint16_t SPT[PANEL ? GB_N * kPanelGroups : 8];
   __shared__ __attribute__((aligned(1024))) uint8_t ZPT[PANEL ? GB_N * kPanelGroups : 16];
   const int tid = threadIdx.x;
@@ -389,6 +391,7 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
   // workgroups of a tile (consecutive slots of one XCD, so that they meet in
   // its L2) each take 1 / ksplit of the k-tiles
   const int xcd = blockIdx.x & 7, idx0 = blockIdx.x >> 3;
+  if (!SPLIT) ksplit = 1;
   const int ks = idx0 % ksplit, idx = idx0 / ksplit;
   const int nbx = (nblk - xcd + 7) >> 3;
   if (nbx <= 0) return;
@@ -401,6 +404,7 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
   const int groups = d >> (6 + gsh);
   const int KT = d / GB_K / ksplit;  // k-tiles of this workgroup: kt0 .. kt0 + KT - 1
   const int kt0 = ks * KT;
+  const int pg0 = kt0 >> gsh;  // first group of the panel
   const int l32 = lane & 31, g = lane >> 5;
 
   // buffer resources at the tile's first row (byte offsets < 2^31: d <= 2^21,
@@ -489,8 +493,8 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
       const int r = 32 * WN * wn + 32 * j + l32;
       q.wf[j] = wl[2 * r + (g ^ ((r >> 3) & 1))];
       if constexpr (PANEL) {
-        q.s[j] = SPT[gi * GB_N + r];
-        q.z[j] = ZPT[gi * GB_N + r];
+        q.s[j] = SPT[(gi - pg0) * GB_N + r];
+        q.z[j] = ZPT[(gi - pg0) * GB_N + r];
       } else {
         q.s[j] = ss_l[r];
         q.z[j] = zs_l[r];
@@ -601,32 +605,35 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
   };
 
   if constexpr (PANEL) {
-    // lane l of wavefront w loads the scales (groups x fp16) and zeros (groups
-    // bytes) of tile row 64 w + l, its own rows, in 16-byte pieces (rows past N
-    // read as zero), and stores them group-major
+    // lane l of wavefront w loads the scales (fp16) and zeros (bytes) of the
+    // panel's pg groups of tile row 64 w + l, its own row, in 16-byte pieces
+    // (the last piece may run into the next groups or row, which are stored
+    // but never read; past the tile's rows it reads zero), and stores them
+    // group-major
     const __amdgpu_buffer_rsrc_t rsp = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(sc + (size_t)nw0 * groups), (short)0, min(N - nw0, GB_N) * groups * 2, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rzp = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(zr + (size_t)nw0 * groups), (short)0, min(N - nw0, GB_N) * groups, kRsrcWord3);
     const int rr = 64 * w + lane;
+    const int pg = KT >> gsh;  // KT a multiple of the group's k-tiles (checked on the host)
     u4 sv[kPanelGroups / 8], zv[kPanelGroups / 16];
 #pragma unroll
     for (int c = 0; c < kPanelGroups / 8; ++c)
-      if (c < groups / 8)
-        sv[c] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rsp, rr * groups * 2 + 16 * c, 0, 0));
+      if (c < (pg + 7) / 8)
+        sv[c] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rsp, (rr * groups + pg0) * 2 + 16 * c, 0, 0));
 #pragma unroll
     for (int c = 0; c < kPanelGroups / 16; ++c)
-      if (c < groups / 16)
-        zv[c] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rzp, rr * groups + 16 * c, 0, 0));
+      if (c < (pg + 15) / 16)
+        zv[c] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rzp, rr * groups + pg0 + 16 * c, 0, 0));
 #pragma unroll
     for (int c = 0; c < kPanelGroups / 8; ++c)
-      if (c < groups / 8) {
+      if (c < (pg + 7) / 8) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) SPT[(8 * c + t) * GB_N + rr] = (uint16_t)(sv[c][t >> 1] >> (16 * (t & 1)));
       }
 #pragma unroll
     for (int c = 0; c < kPanelGroups / 16; ++c)
-      if (c < groups / 16) {
+      if (c < (pg + 15) / 16) {
 #pragma unroll
         for (int t = 0; t < 16; ++t) ZPT[(16 * c + t) * GB_N + rr] = (uint8_t)(zv[c][t >> 2] >> (8 * (t & 3)));
       }
@@ -646,7 +653,7 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
   __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
   __builtin_amdgcn_s_barrier();
 
-  if (ksplit > 1) {
+  if constexpr (SPLIT) {
     // Split k: every workgroup of the tile stores its fp32 partial tile
     // (wavefront w's 256 accumulators per lane as [w][64 groups of 4][lane],
     // 256 KB per workgroup) and counts itself in; the last to arrive adds the
@@ -817,14 +824,22 @@ hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint1
     const int64_t bw = 8 * nbp * (((int64_t)mblkw + 7) / 8) * 8 * plan.ksplit;
     const int64_t groups = d >> (6 + gsh);
     const int sys = plan.ksplit > 1 && !xcd_dispatch_is_round_robin();
-    if (groups <= kPanelGroups && groups % 16 == 0 && ((uintptr_t)scales & 15) == 0 && ((uintptr_t)zeros & 15) == 0)
-      hipLaunchKernelGGL((w4_gemm_wide_kernel<kWideWN, true>), dim3((unsigned)bw), dim3(256), 0, stream, x,
-                         qweight, scales, zeros, bias, y, (int)M, (int)N, (int)d, gsh, mblkw, nblk, plan.ksplit,
-                         part, cnt, sys);
-    else
-      hipLaunchKernelGGL((w4_gemm_wide_kernel<kWideWN, false>), dim3((unsigned)bw), dim3(256), 0, stream, x,
-                         qweight, scales, zeros, bias, y, (int)M, (int)N, (int)d, gsh, mblkw, nblk, plan.ksplit,
-                         part, cnt, sys);
+    // the scale and zero panel: whole groups per workgroup, at most 64 of
+    // them, a multiple of 8; scales 16-byte and zeros 8-byte aligned
+    const int64_t ktw = d / GB_K / plan.ksplit, pg = ktw >> gsh;
+    const bool panel = ktw % (int64_t(1) << gsh) == 0 && pg <= kPanelGroups && pg % 8 == 0 &&
+                       ((uintptr_t)scales & 15) == 0 && ((uintptr_t)zeros & 7) == 0;
+    auto go = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3((unsigned)bw), dim3(256), 0, stream, x, qweight, scales, zeros, bias, y,
+                         (int)M, (int)N, (int)d, gsh, mblkw, nblk, plan.ksplit, part, cnt, sys);
+    };
+    if (plan.ksplit > 1) {
+      if (panel) go(w4_gemm_wide_kernel<kWideWN, true, true>);
+      else go(w4_gemm_wide_kernel<kWideWN, false, true>);
+    } else {
+      if (panel) go(w4_gemm_wide_kernel<kWideWN, true, false>);
+      else go(w4_gemm_wide_kernel<kWideWN, false, false>);
+    }
     return hipGetLastError();
   }
   if (half && ks2) launch_gemm<2, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);

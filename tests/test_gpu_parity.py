@@ -306,7 +306,7 @@ def test_linear_shapes_with_bias(paro, M, d, N):
 
 
 # shapes with at least 256 output tiles of 256 x 256 run the one-wavefront-per-SIMD
-# kernel (d = 2048 and 4096 with the scale and zero panel in LDS): ragged in M
+# kernel (d = 1024, 2048 and 4096 with the scale and zero panel in LDS): ragged in M
 # and N, rows sampled (the last included), every column checked
 @pytest.mark.parametrize("M,d,N", [(4200, 256, 8208), (2600, 512, 13008), (2304, 1024, 14336),
                                    (2600, 2048, 13008), (4100, 4096, 4112)])
@@ -322,13 +322,16 @@ def test_linear_wide_tiles(paro, M, d, N):
 # layers with 16 to 255 output tiles of 256 x 256 and long k split k across 2 to
 # 8 workgroups per tile (full workspace); with the minimum workspace the same
 # call runs the 128 x 256-tile kernel. Both against the oracle: the down-proj
-# configuration (two splits) and ragged shapes (two and four splits, with and
-# without the scale/zero panel).
-@pytest.mark.parametrize("M,d,N", [(2048, 14336, 4096), (1000, 8192, 2064), (600, 14336, 4096)])
-def test_linear_split_k(paro, M, d, N):
-    log(f"linear split-k M={M} d={d} N={N}")
-    x, layer, b = synthetic.linear_case(seed=M + d + N + 7, M=M, d=d, N=N)
-    G = layer.group
+# configuration (two splits, 56 groups of 128 per split in the scale/zero
+# panel) and ragged shapes: two splits of 32 groups (panel); four splits of 28
+# groups (not a multiple of 8: no panel); eight splits of 24 groups (panel);
+# four splits of 56 groups of 64 (panel) and of 14 groups of 256 (no panel).
+@pytest.mark.parametrize("M,d,N,G", [(2048, 14336, 4096, 128), (1000, 8192, 2064, 128), (600, 14336, 4096, 128),
+                                     (512, 24576, 2048, 128), (700, 14336, 4096, 64), (600, 14336, 4096, 256)])
+def test_linear_split_k(paro, M, d, N, G):
+    log(f"linear split-k M={M} d={d} N={N} group={G}")
+    x, layer, b = synthetic.linear_case(seed=M + d + N + 7, M=M, d=d, N=N, group=G)
+    assert layer.group == G
     r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, G)
     qw, s, z = paro.paro_quantize_weights(r, dev(layer.w), G)
     rows = np.sort(synthetic.rng_for(3520, M).choice(M, 48, replace=False))
