@@ -70,6 +70,9 @@ constexpr int kWaitVmLgkm0 = 0x70;
 // on MI355X, 64-token tiles win at 128 tiles (1024 x 4096 -> 4096: 699
 // against 581 TFLOP/s) and lose at 256 (2048 x 4096 -> 4096: 760 against 918).
 constexpr int64_t kHalfTileBelow = 256;
+// 64-token tiles below which the tiles are also narrowed to 128 channels, so
+// that every CU gets a workgroup
+constexpr int64_t kNarrowTileBelow = 256;
 // 256 x 256 tiles (at 256 tokens) from which the wide kernel is used: measured
 // on MI355X, 4096 x 4096 -> 4096 (256 tiles): 128 against 135 us; 2048 x
 // 14336 -> 4096 (128 tiles) runs 372 against 288 us
@@ -87,14 +90,16 @@ constexpr int64_t kMinSplitKT = 48;
 constexpr int kWideWN = 2;
 
 // MT: 32-token m tiles per wavefront (4: 128-token workgroup tiles; 2: 64,
-// for layers with few output tiles).
-template <int KS, int MT>
+// for layers with few output tiles). NT: 32-channel n tiles per wavefront (2:
+// 256-channel workgroup tiles; 1: 128, for layers with fewer still).
+template <int KS, int MT, int NT>
 __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(2)))
 void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ qw,
                     const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zr,
                     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N,
                     int d, int gsh, int mblk, int nblk) {
   constexpr int GB_M = 32 * MT;           // tokens per workgroup tile
+  constexpr int GN = 128 * NT;            // output channels per workgroup tile
   constexpr int GB_XSTAGE = GB_M * GB_K;  // halfs per X' stage (16 KB at MT = 4)
   __shared__ __attribute__((aligned(1024))) _Float16 X0[KS][GB_XSTAGE], X1[KS][GB_XSTAGE];
   __shared__ __attribute__((aligned(1024))) u4 W0[KS][GB_WSTAGE], W1[KS][GB_WSTAGE];
@@ -116,8 +121,8 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
   const int mb = mg * 8 + (rem & 7);
   if (mb >= mblk) return;
   const int m0 = mb * GB_M;
-  const int nw0 = nb * GB_N;       // workgroup's first output channel
-  const int n0 = nw0 + 64 * w;     // this wavefront's first output channel
+  const int nw0 = nb * GN;         // workgroup's first output channel
+  const int n0 = nw0 + 32 * NT * w;  // this wavefront's first output channel
   const int groups = d >> (6 + gsh);  // quantization groups of 64 << gsh channels per row
   const int KT = (d / GB_K) / KS;  // k-tiles per group of wavefronts
   const int kt0 = kg * KT;
@@ -128,11 +133,11 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(x + (size_t)m0 * d), (short)0, min(M - m0, GB_M) * d * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(qw + (size_t)nw0 * (d >> 1)), (short)0, min(N - nw0, GB_N) * (d >> 1), kRsrcWord3);
+      (void*)(qw + (size_t)nw0 * (d >> 1)), (short)0, min(N - nw0, GN) * (d >> 1), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(sc + (size_t)nw0 * groups), (short)0, min(N - nw0, GB_N) * groups * 2, kRsrcWord3);
+      (void*)(sc + (size_t)nw0 * groups), (short)0, min(N - nw0, GN) * groups * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(zr + (size_t)nw0 * groups), (short)0, min(N - nw0, GB_N) * groups, kRsrcWord3);
+      (void*)(zr + (size_t)nw0 * groups), (short)0, min(N - nw0, GN) * groups, kRsrcWord3);
   // X' DMA c of wavefront w fills tile rows 8 (MT w + c) .. + 7; the lane at
   // position l % 8 of row l / 8 fetches the source chunk (l % 8) ^ swizzle
   // (arrays the lambdas below capture are sized for MT = 4: the host pass of
@@ -145,37 +150,41 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
     const int row = min(r, M - 1 - m0);
     xoff[c] = (uint32_t)(row * d + 8 * ((lane & 7) ^ ((r >> 1) & 7))) * 2u;
   }
-  // code DMA c of wavefront w fills tile rows 32 (2 w + c) .. + 31
+  // code DMA c of wavefront w fills tile rows 32 (NT w + c) .. + 31
   uint32_t woff[2];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int r = 32 * (2 * w + c) + (lane >> 1);
+  for (int c = 0; c < NT; ++c) {
+    const int r = 32 * (NT * w + c) + (lane >> 1);
     const int row = min(r, N - 1 - nw0);
     woff[c] = (uint32_t)(row * (d >> 1) + 16 * ((lane & 1) ^ ((r >> 3) & 1)));
   }
-  // group scale and zero: lane l of wavefront w fetches row 64 w + l
+  // group scale and zero: lane l of wavefront w fetches row 64 w + l (NT = 1:
+  // wavefronts 0 and 1 fetch the 128 rows)
+  const bool szw = NT == 2 || w < 2;
   const uint32_t szrow = (uint32_t)(min(64 * w + lane, N - 1 - nw0) * groups);
 
-  // the DMA of one k-tile: ten load-to-LDS instructions per lane
+  // the DMA of one k-tile: MT + NT + 2 load-to-LDS instructions per lane
   auto dma = [&](int kt, _Float16* xs, u4* ws, uint32_t* ss_l, uint32_t* zs_l) {
     const int kglob = kt0 + kt;
     const uint32_t gi = (uint32_t)(kglob >> gsh);  // the k-tile's group (64-channel k-tiles)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)&ss_l[64 * w], 2, (szrow + gi) * 2u, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_void*)&zs_l[64 * w], 1, szrow + gi, 0, 0, 0);
+    if (szw) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)&ss_l[64 * w], 2, (szrow + gi) * 2u, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_void*)&zs_l[64 * w], 1, szrow + gi, 0, 0, 0);
+    }
 #pragma unroll
     for (int c = 0; c < MT; ++c)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)&xs[(MT * w + c) * 64 * 8], 16, xoff[c],
                                                kglob * GB_K * 2, 0, 0);
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)&ws[(2 * w + c) * 64], 16, woff[c],
+    for (int c = 0; c < NT; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)&ws[(NT * w + c) * 64], 16, woff[c],
                                                kglob * (GB_K / 2), 0, 0);
   };
 
   const uint32_t one = fp16_1024_pair();
-  f16v acc[2][4];  // m tiles mm < MT used
+  f16v acc[2][4];  // n tiles j < NT and m tiles mm < MT used
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < NT; ++j)
 #pragma unroll
     for (int mm = 0; mm < MT; ++mm)
 #pragma unroll
@@ -191,8 +200,8 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
     u4 wf[2];
     h2 ss[2], zz[2], ss16[2], zz16[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = 64 * w + 32 * j + l32;
+    for (int j = 0; j < NT; ++j) {
+      const int r = 32 * NT * w + 32 * j + l32;
       wf[j] = wl[2 * r + (g ^ ((r >> 3) & 1))];
       // (rows past N read the last row's scale, clamped by the DMA; never stored)
       ss[j] = splat2(__builtin_bit_cast(_Float16, (uint16_t)(ss_l[r] & 0xffffu)));
@@ -205,14 +214,14 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
     for (int i = 0; i < 4; ++i) {
       h8 a[2], b[MT];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) a[j] = dequant8(wf[j][i], zz[j], ss[j], zz16[j], ss16[j], one);
+      for (int j = 0; j < NT; ++j) a[j] = dequant8(wf[j][i], zz[j], ss[j], zz16[j], ss16[j], one);
 #pragma unroll
       for (int mm = 0; mm < MT; ++mm) {
         const int r = 32 * mm + l32;
         b[mm] = *(const h8*)(xb + r * GB_K + 8 * ((4 * g + i) ^ ((r >> 1) & 7)));
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NT; ++j)
 #pragma unroll
         for (int mm = 0; mm < MT; ++mm)
           acc[j][mm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[j], b[mm], acc[j][mm], 0, 0, 0);
@@ -237,7 +246,7 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
     constexpr int PM = MT / 2;
     float* red = (float*)&X0[0][0];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NT; ++j) {
 #pragma unroll
       for (int h = 0; h < MT / PM; ++h) {
         if (kg == 1) {
@@ -260,19 +269,20 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
   }
 
   // epilogue: acc[j][mm][e] = C[n = n0 + 32 j + 8 (e/4) + 4 g + e%4][m = m0 + 32 mm + l32].
-  // Each wavefront stages its 64 (n) x 64 (m) output blocks through an 8 KB LDS
+  // Each wavefront stages its 32 NT (n) x 64 (m) output blocks through an LDS
   // region of its own (the operand stages are free after the last barrier) as
-  // fp16 rows of 64 outputs, 16-byte chunk c of row r at position c ^ (r & 7),
-  // and then stores whole 128-byte rows: lane l writes chunk l % 8 of row l / 8
-  // of each group of 8 rows.
+  // fp16 rows of 32 NT outputs (CR = 4 NT 16-byte chunks), chunk c of row r at
+  // position c ^ (r % CR), and then stores whole rows: lane l writes chunk
+  // l % CR of row l / CR of each group of 64 / CR rows.
   {
+    constexpr int CR = 4 * NT, RB = 16 * CR;
     uint8_t* stage = w == 0 ? (uint8_t*)&X0[0][0] : w == 1 ? (uint8_t*)&X1[0][0]
                    : w == 2 ? (uint8_t*)&W0[0][0] : (uint8_t*)&W1[0][0];
     constexpr int PASSES = MT / 2;  // 64 tokens per pass
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < NT; ++j) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int nl = 32 * j + 8 * q + 4 * g;  // local output channel of e = 4 q
@@ -292,15 +302,15 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
             pk.x = half_bits(acc[j][mm][4 * q + 0] + b4[0]) | (half_bits(acc[j][mm][4 * q + 1] + b4[1]) << 16);
             pk.y = half_bits(acc[j][mm][4 * q + 2] + b4[2]) | (half_bits(acc[j][mm][4 * q + 3] + b4[3]) << 16);
             const int c = nl >> 3;  // 16-byte chunk, 8-byte half (nl >> 2) & 1
-            *(uint2*)(stage + rl * 128 + ((c ^ (rl & 7)) << 4) + (((nl >> 2) & 1) << 3)) = pk;
+            *(uint2*)(stage + rl * RB + ((c ^ (rl % CR)) << 4) + (((nl >> 2) & 1) << 3)) = pk;
           }
         }
       }
       // (the region is this wavefront's own: its LDS accesses complete in order)
 #pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const int rl = 8 * rr + (lane >> 3), c = lane & 7;
-        const u4 v = *(const u4*)(stage + rl * 128 + ((c ^ (rl & 7)) << 4));
+      for (int rr = 0; rr < CR; ++rr) {
+        const int rl = (64 / CR) * rr + lane / CR, c = lane % CR;
+        const u4 v = *(const u4*)(stage + rl * RB + ((c ^ (rl % CR)) << 4));
         const int m = m0 + 64 * ps + rl, n = n0 + 8 * c;
         if (m < M && n < N) *(u4*)(y + (size_t)m * N + n) = v;
       }
@@ -767,11 +777,11 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
   }
 }
 
-template <int KS, int MT>
+template <int KS, int MT, int NT>
 void launch_gemm(unsigned blocks, hipStream_t stream, const uint16_t* x, const uint8_t* qweight,
                  const uint16_t* scales, const uint8_t* zeros, const uint16_t* bias, uint16_t* y,
                  int64_t M, int64_t N, int64_t d, int gsh, int mblk, int nblk) {
-  hipLaunchKernelGGL((w4_gemm_kernel<KS, MT>), dim3(blocks), dim3(256 * KS), 0, stream, x, qweight,
+  hipLaunchKernelGGL((w4_gemm_kernel<KS, MT, NT>), dim3(blocks), dim3(256 * KS), 0, stream, x, qweight,
                      scales, zeros, bias, y, (int)M, (int)N, (int)d, gsh, mblk, nblk);
 }
 
@@ -803,11 +813,14 @@ hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint1
                           int64_t N, int64_t d, int group, uint32_t* cnt, float* part, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const int gsh = group == 64 ? 0 : group == 128 ? 1 : 2;
-  const int nblk = (int)((N + GB_N - 1) / GB_N);
-  // 64-token tiles when 128-token ones would leave most SIMDs without work
-  const bool half = (int64_t)nblk * ((M + 127) / 128) < kHalfTileBelow;
+  const int nblk256 = (int)((N + GB_N - 1) / GB_N);
+  // 64-token tiles when 128-token ones would leave most SIMDs without work,
+  // and 128-channel ones when even those leave CUs without a workgroup
+  const bool half = (int64_t)nblk256 * ((M + 127) / 128) < kHalfTileBelow;
   const int gbm = half ? 64 : 128;
   const int mblk = (int)((M + gbm - 1) / gbm);
+  const bool narrow = half && (int64_t)nblk256 * mblk < kNarrowTileBelow;
+  const int nblk = narrow ? (int)((N + GB_N / 2 - 1) / (GB_N / 2)) : nblk256;
   const int64_t tiles = (int64_t)nblk * mblk;
   // 8 XCDs, each owning every 8th n-block, walked in super-blocks of 8 m-blocks
   const int64_t nbp = (nblk + 7) / 8;
@@ -821,7 +834,7 @@ hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint1
   const GemmPlan plan = plan_w4_gemm(M, N, d);
   if (plan.wide && (plan.ksplit == 1 || (cnt && part))) {
     const int mblkw = (int)((M + GW_M - 1) / GW_M);
-    const int64_t bw = 8 * nbp * (((int64_t)mblkw + 7) / 8) * 8 * plan.ksplit;
+    const int64_t bw = 8 * ((nblk256 + 7) / 8) * (((int64_t)mblkw + 7) / 8) * 8 * plan.ksplit;
     const int64_t groups = d >> (6 + gsh);
     const int sys = plan.ksplit > 1 && !xcd_dispatch_is_round_robin();
     // the scale and zero panel: whole groups per workgroup, at most 64 of
@@ -831,7 +844,7 @@ hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint1
                        ((uintptr_t)scales & 15) == 0 && ((uintptr_t)zeros & 7) == 0;
     auto go = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, dim3((unsigned)bw), dim3(256), 0, stream, x, qweight, scales, zeros, bias, y,
-                         (int)M, (int)N, (int)d, gsh, mblkw, nblk, plan.ksplit, part, cnt, sys);
+                         (int)M, (int)N, (int)d, gsh, mblkw, nblk256, plan.ksplit, part, cnt, sys);
     };
     if (plan.ksplit > 1) {
       if (panel) go(w4_gemm_wide_kernel<kWideWN, true, true>);
@@ -842,10 +855,12 @@ hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint1
     }
     return hipGetLastError();
   }
-  if (half && ks2) launch_gemm<2, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
-  else if (half) launch_gemm<1, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
-  else if (ks2) launch_gemm<2, 4>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
-  else launch_gemm<1, 4>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
+  if (narrow && ks2) launch_gemm<2, 2, 1>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
+  else if (narrow) launch_gemm<1, 2, 1>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
+  else if (half && ks2) launch_gemm<2, 2, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
+  else if (half) launch_gemm<1, 2, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
+  else if (ks2) launch_gemm<2, 4, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
+  else launch_gemm<1, 4, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
   return hipGetLastError();
 }
 

@@ -294,11 +294,15 @@ def test_linear_decode(paro, M):
     check_linear(paro, synthetic.decode_x(M), layer, rotated=False)
 
 
-# (the first four and the last two prefill shapes give fewer than 256 output
-# tiles of 128 tokens and run 64-token tiles; (2100, 512, 4112) runs 128-token
-# tiles with k split in halves inside the workgroup, (4200, 256, 4208) without)
+# (prefill shapes with fewer than 256 output tiles of 128 tokens x 256 channels
+# run 64-token tiles, and with fewer than 256 of those, 64 x 128 tiles: the
+# first four and (70, 128, 208), which has too few k-tiles to split k inside
+# the workgroup; (1100, 512, 4112) runs 64 x 256 tiles; (2100, 512, 4112)
+# runs 128-token tiles with k split in halves inside the workgroup,
+# (4200, 256, 4208) without)
 @pytest.mark.parametrize("M,d,N", [(17, 256, 64), (130, 512, 272), (300, 384, 128), (256, 1024, 512),
-                                   (3, 512, 48), (9, 1152, 1040), (2100, 512, 4112), (4200, 256, 4208)])
+                                   (70, 128, 208), (1100, 512, 4112), (3, 512, 48), (9, 1152, 1040),
+                                   (2100, 512, 4112), (4200, 256, 4208)])
 def test_linear_shapes_with_bias(paro, M, d, N):
     log(f"linear M={M} d={d} N={N}")
     x, layer, b = synthetic.linear_case(seed=M + d + N, M=M, d=d, N=N)
