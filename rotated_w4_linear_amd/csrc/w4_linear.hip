@@ -107,7 +107,7 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
   __shared__ __attribute__((aligned(16))) uint32_t Z0[KS][GB_N], Z1[KS][GB_N];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int kg = __builtin_amdgcn_readfirstlane(tid >> 8);     // k half (KS = 2)
+  const int kg = __builtin_amdgcn_readfirstlane(tid >> 8);     // k group (KS > 1)
   const int w = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // wavefront inside the group
   // XCD-aware tile order: workgroup b runs on XCD b % 8. XCD x owns the
   // n-blocks x, x + 8, ... and walks them in super-blocks of 8 m-blocks x all
@@ -239,33 +239,39 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
     if (kt + 1 < KT) step(kt + 1, &X1[kg][0], &W1[kg][0], &S1[kg][0], &Z1[kg][0], &X0[kg][0], &W0[kg][0], &S0[kg][0], &Z0[kg][0]);
   }
 
-  if constexpr (KS == 2) {
-    // the second k half hands its partial sums to the first through LDS (the
-    // X' stages 0 of both halves: 32 KB at MT = 4, 16 KB at MT = 2), PM m
-    // tiles of one n tile (16 KB per m tile) at a time
+  if constexpr (KS > 1) {
+    // the k groups add their partial sums pairwise through LDS, (0 + 1) +
+    // (2 + 3): in the round of span s, group kg = r + s hands its sums to
+    // group r (r a multiple of 2 s) through the X' stages 0 of groups r and
+    // r + 1 (32 KB at MT = 4, 16 KB at MT = 2), PM m tiles of one n tile
+    // (16 KB per m tile) at a time
     constexpr int PM = MT / 2;
-    float* red = (float*)&X0[0][0];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
+    for (int span = 1; span < KS; span *= 2) {
+      const int pos = kg & (2 * span - 1);
+      float* red = (float*)&X0[kg - pos][0];
 #pragma unroll
-      for (int h = 0; h < MT / PM; ++h) {
-        if (kg == 1) {
+      for (int j = 0; j < NT; ++j) {
 #pragma unroll
-          for (int mm = 0; mm < PM; ++mm)
+        for (int h = 0; h < MT / PM; ++h) {
+          if (pos == span) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) red[((w * PM + mm) * 16 + e) * 64 + lane] = acc[j][PM * h + mm][e];
+            for (int mm = 0; mm < PM; ++mm)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) red[((w * PM + mm) * 16 + e) * 64 + lane] = acc[j][PM * h + mm][e];
+          }
+          __syncthreads();
+          if (pos == 0) {
+#pragma unroll
+            for (int mm = 0; mm < PM; ++mm)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) acc[j][PM * h + mm][e] += red[((w * PM + mm) * 16 + e) * 64 + lane];
+          }
+          __syncthreads();
         }
-        __syncthreads();
-        if (kg == 0) {
-#pragma unroll
-          for (int mm = 0; mm < PM; ++mm)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[j][PM * h + mm][e] += red[((w * PM + mm) * 16 + e) * 64 + lane];
-        }
-        __syncthreads();
       }
     }
-    if (kg == 1) return;
+    if (kg != 0) return;
   }
 
   // epilogue: acc[j][mm][e] = C[n = n0 + 32 j + 8 (e/4) + 4 g + e%4][m = m0 + 32 mm + l32].
@@ -827,6 +833,9 @@ hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint1
   const int64_t blocks = 8 * nbp * (((int64_t)mblk + 7) / 8) * 8;
   // too few tiles to give every SIMD two wavefronts: split k inside the workgroup
   const bool ks2 = tiles < 512 && (d / GB_K) % 2 == 0 && d / GB_K >= 4;
+  // 64 x 128 tiles: four k groups (sixteen wavefronts), so that each CU has
+  // four k-tiles' loads in flight
+  const bool ks4 = narrow && (d / GB_K) % 4 == 0 && d / GB_K >= 16;
   const unsigned g = (unsigned)blocks;
   // layers with many 256 x 256 tiles take the one-wavefront-per-SIMD kernel,
   // layers with fewer the same kernel with k split across workgroups when the
@@ -855,7 +864,8 @@ hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint1
     }
     return hipGetLastError();
   }
-  if (narrow && ks2) launch_gemm<2, 2, 1>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
+  if (ks4) launch_gemm<4, 2, 1>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
+  else if (narrow && ks2) launch_gemm<2, 2, 1>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
   else if (narrow) launch_gemm<1, 2, 1>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
   else if (half && ks2) launch_gemm<2, 2, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
   else if (half) launch_gemm<1, 2, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
