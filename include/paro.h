@@ -186,7 +186,7 @@ int paro_quantize_weights(const paro_rotation* r, const uint16_t* w, int64_t N, 
  * uses no workspace. For M > 16 on layers with fewer than 256 output tiles of
  * 256 x 256 (at least 16) this includes fp32 partial tiles (256 KB per tile
  * and k-split) for splitting k across workgroups; paro_w4_linear also runs,
- * with the 128 x 256-tile kernel, on the minimum: 16 KiB + M d 2 bytes
+ * with the smaller-tile kernel, on the minimum: 16 KiB + M d 2 bytes
  * (rounded up to 256) with a plan, none without. */
 size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t N, int64_t d);
 
@@ -225,8 +225,9 @@ size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t 
  * a matrix-core kernel: 256 x 256 tiles from 256 such tiles; with fewer (at
  * least 16) the same kernel with k split across 2 to 8 workgroups per tile,
  * which meet through fp32 partial tiles in the workspace (the last to arrive
- * adds them in split order), when the workspace holds them; else 128 x 256
- * tiles.
+ * adds them in split order), when the workspace holds them; else a kernel
+ * with 128 x 256 tiles, or 64 x 256 or 64 x 128 (k split two or four ways
+ * inside the workgroup) for layers with few tiles.
  *
  * Arithmetic: X' exactly as paro_rotate computes it (fp16); fp32 accumulation
  * of exact fp16 products against the fp16 rounding of each dequantized weight
