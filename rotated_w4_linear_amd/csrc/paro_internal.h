@@ -138,13 +138,14 @@ hipError_t launch_nt_gemm_loss(const uint16_t* x, const uint16_t* w, int64_t M, 
 hipError_t launch_transpose_pad(const uint16_t* in, int64_t R, int64_t C, uint16_t* out, int64_t ldo,
                                 hipStream_t stream);
 // Large-batch linear (M > 16) on already transformed activations. The plan
-// says whether the 256 x 256-tile kernel runs and with how many k-splits
-// across workgroups; a split run needs the arrival counters (zero between
-// calls) and partial_bytes of fp32 partial tiles, and without them (NULL) the
-// layer takes the 128 x 256-tile kernel.
+// says whether the 256 x 256-tile kernel runs, and whether stream-K (the
+// tiles' k-tiles shared out among the workgroups); a stream-K run needs the
+// arrival counters (zero between calls) and partial_bytes of fp32 partial
+// tiles, and without them (NULL) the layer takes the smaller-tile kernel.
 struct GemmPlan {
   bool wide = false;
-  int ksplit = 1;
+  bool sk = false;
+  int sk_slots = 0;  // stream-K workgroups per XCD
   size_t partial_bytes = 0;
 };
 GemmPlan plan_w4_gemm(int64_t M, int64_t N, int64_t d);

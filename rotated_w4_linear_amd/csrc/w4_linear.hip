@@ -8,6 +8,8 @@
 // masked into the mantissas of a pair of fp16 1024.0 values with one
 // v_and_or_b32, (1024 + q) - (1024 + z) = q - z is exact in packed fp16, and
 // one packed multiply by the fp16 scale rounds once.
+#include <algorithm>
+
 #include "paro_internal.h"
 #include "w4_common.h"
 
@@ -66,6 +68,8 @@ constexpr int kAuxL2R = 1;
 constexpr int kAuxSysW = 17;
 // s_waitcnt immediate (gfx9 encoding): vmcnt(0) lgkmcnt(0), expcnt untouched
 constexpr int kWaitVmLgkm0 = 0x70;
+// lgkmcnt(0) alone (vmcnt and expcnt at their maxima)
+constexpr int kWaitLgkm0 = 0xC07F;
 // Output tiles (at 128 tokens) below which 64-token tiles are used: measured
 // on MI355X, 64-token tiles win at 128 tiles (1024 x 4096 -> 4096: 699
 // against 581 TFLOP/s) and lose at 256 (2048 x 4096 -> 4096: 760 against 918).
@@ -77,15 +81,17 @@ constexpr int64_t kNarrowTileBelow = 256;
 // on MI355X, 4096 x 4096 -> 4096 (256 tiles): 128 against 135 us; 2048 x
 // 14336 -> 4096 (128 tiles) runs 372 against 288 us
 constexpr int64_t kWideMinTiles = 256;
-// with fewer (but at least kSplitMinTiles) the wide kernel splits k across up to
-// kMaxSplit workgroups per tile, each taking at least kMinSplitKT k-tiles: the
-// partial tiles (256 KB per workgroup, written and read back) pay off only on
-// long k. Measured on MI355X: 2048 x 14336 -> 4096 (two splits of 112 k-tiles)
-// 242 against 292 us for the 128 x 256-tile kernel; 2048 x 4096 -> 4096 (two
-// of 32) 88 against 73 us, 2048 x 4096 -> 1024 (eight of 8) 102 against 48 us
-constexpr int64_t kSplitMinTiles = 16;
-constexpr int kMaxSplit = 8;
+// Stream-K (the wide kernel with the tiles' k-tiles shared out evenly among
+// the workgroups of each XCD) when each workgroup's range holds at least
+// kMinSplitKT k-tiles: the partial tiles (256 KB per piece, written and read
+// back) pay off only on long ranges. Measured on MI355X with uniform splits:
+// 2048 x 14336 -> 4096 (two splits of 112 k-tiles) 242 against 292 us for the
+// 128 x 256-tile kernel; 2048 x 4096 -> 4096 (two of 32) 88 against 73 us,
+// 2048 x 4096 -> 1024 (eight of 8) 102 against 48 us
 constexpr int64_t kMinSplitKT = 48;
+// k-tiles a stream-K range is charged for cutting tiles at unequal k (see
+// plan_w4_gemm)
+constexpr int64_t kSkMisaligned = 20;
 // n tiles of 32 channels per wavefront in the wide kernel
 constexpr int kWideWN = 2;
 
@@ -341,6 +347,11 @@ constexpr int GW_XSTAGE = GW_M * GB_K;  // halfs per X' stage (32 KB)
 // tile in LDS (48 KB at 64; a multiple of 16 groups, scales and zeros 16-byte
 // aligned)
 constexpr int kPanelGroups = 64;
+// stream-K workgroups per XCD at most (one workgroup per CU: 256 CUs in 8
+// XCDs)
+constexpr int kSkSlots = 32;
+// wide-kernel modes
+constexpr int kModeTile = 0, kModeSkOne = 1, kModeSkMany = 2;
 
 // Instruction order inside a scheduling region of 16 MFMAs: the region's ND
 // LDS reads first, the first NW MFMAs alone (while those reads return), then
@@ -381,47 +392,69 @@ __device__ __forceinline__ void sched_order() {
 
 // WN: 32-channel n tiles per wavefront (4: 128 (n) x 128 (m) wavefront tiles,
 // 2: 64 (n) x 256 (m)); MTW = 16 / WN m tiles of 32 tokens.
-// SPLIT: k split across ksplit > 1 workgroups per tile (a separate
-// instantiation, so that the reduction's registers do not weigh on the other).
-template <int WN, bool PANEL, bool SPLIT>
+// MODE: kModeTile, one tile per workgroup; kModeSkOne and kModeSkMany,
+// stream-K (separate instantiations, so that the reduction's and the segment
+// loop's registers do not weigh on the others). Stream-K: the grid is `slots` (<= kSkSlots) workgroups
+// per XCD. The tiles of XCD x (its n-blocks x, x + 8, ... in the
+// data-parallel order) are laid end to end as one sequence of k-tiles, and
+// workgroup j of the XCD takes the j-th of `slots` equal ranges of it (even
+// lengths): whole tiles,
+// plus at most one partial tile at each end. The pieces of a partial tile
+// meet through fp32 partial tiles in the workspace; the last to arrive adds
+// them in k order and runs the epilogue.
+template <int WN, bool PANEL, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ qw,
                          const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zr,
                          const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N,
-                         int d, int gsh, int mblk, int nblk, int ksplit, float* __restrict__ part,
+                         int d, int gsh, int mblk, int nblk, int slots, float* __restrict__ part,
                          uint32_t* __restrict__ cnt, int sys) {
   __shared__ __attribute__((aligned(1024))) _Float16 X0[GW_XSTAGE], X1[GW_XSTAGE];
   __shared__ __attribute__((aligned(1024))) u4 W0[GB_WSTAGE], W1[GB_WSTAGE];
   __shared__ __attribute__((aligned(16))) uint32_t S0[GB_N], S1[GB_N], Z0[GB_N], Z1[GB_N];
-  // PANEL: the tile's scales and zeros of the groups this workgroup's k-tiles
-  // span, loaded once and stored group-major ([group][256 rows]), so that the
-  // 32 rows one read spans are consecutive in LDS
+  // PANEL: the tile's scales and zeros of the groups a segment's k-tiles span
+  // (from the 8-aligned group below its first), loaded once per segment and
+  // stored group-major ([group][256 rows]), so that the 32 rows one read
+  // spans are consecutive in LDS
   __shared__ __attribute__((aligned(1024))) uint16_t SPT[PANEL ? GB_N * kPanelGroups : 8];
   __shared__ __attribute__((aligned(1024))) uint8_t ZPT[PANEL ? GB_N * kPanelGroups : 16];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront 0..3
+  __shared__ uint32_t s_last;
+  constexpr bool SK = MODE != kModeTile;
+  const int tid_k = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid_k >> 6);  // wavefront 0..3
   constexpr int MTW = 16 / WN, NWAV = 8 / WN;               // m tiles; wavefronts along n
   const int wn = w % NWAV, wm = w / NWAV;                   // the wavefront's n and m blocks
-  // XCD-aware tile order, as in w4_gemm_kernel; with ksplit > 1 the ksplit
-  // workgroups of a tile (consecutive slots of one XCD, so that they meet in
-  // its L2) each take 1 / ksplit of the k-tiles
-  const int xcd = blockIdx.x & 7, idx0 = blockIdx.x >> 3;
-  if (!SPLIT) ksplit = 1;
-  const int ks = idx0 % ksplit, idx = idx0 / ksplit;
+  // XCD-aware tile order, as in w4_gemm_kernel
+  const int xcd = blockIdx.x & 7;
   const int nbx = (nblk - xcd + 7) >> 3;
   if (nbx <= 0) return;
-  const int mg = idx / (8 * nbx), rem = idx - mg * 8 * nbx;
-  const int nb = xcd + 8 * (rem / 8);
-  const int mb = mg * 8 + (rem & 7);
-  if (mb >= mblk) return;
+  const int groups = d >> (6 + gsh);
+  const int L = d / GB_K;  // k-tiles per tile
+  const uint32_t one = fp16_1024_pair();
+  // SK: range j of this XCD's sequence of k-tiles starts at rstart(j)
+  // (`slots` ranges of H / slots k-tile pairs, rounded down); owner(u) is
+  // the range holding k-tile u (the host keeps every range non-empty)
+  const int jw = blockIdx.x >> 3;
+  const int64_t H = SK ? (int64_t)nbx * mblk * L / 2 : 1;
+  auto rstart = [&](int j) -> int64_t { return 2 * (((int64_t)j * H) / slots); };
+  auto owner = [&](int64_t u) -> int {
+    int j = (int)min((int64_t)slots - 1, (u / 2) * slots / H);
+    while (j + 1 < slots && rstart(j + 1) <= u) ++j;
+    while (j > 0 && rstart(j) > u) --j;
+    return j;
+  };
+
+  // One segment: k-tiles kt0 .. kt0 + KT - 1 (KT even) of tile (mb, nb), the
+  // XCD's tile tl; first: the workgroup's first segment
+  auto segment = [&](const int mb, const int nb, const int kt0, const int KT, const int tl, const bool first) {
+  // the lane index through an opaque copy, so that nothing derived from it is
+  // hoisted out of the segment loop and held (spilled) across the k-loop
+  int tid_o = tid_k;
+  asm volatile("" : "+v"(tid_o));
+  const int tid = tid_o, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int m0 = mb * GW_M;
   const int nw0 = nb * GB_N;
-  const int groups = d >> (6 + gsh);
-  const int KT = d / GB_K / ksplit;  // k-tiles of this workgroup: kt0 .. kt0 + KT - 1
-  const int kt0 = ks * KT;
-  const int pg0 = kt0 >> gsh;  // first group of the panel
-  const int l32 = lane & 31, g = lane >> 5;
+  const int pg0 = PANEL ? ((kt0 >> gsh) & ~7) : 0;  // first group of the panel
 
   // buffer resources at the tile's first row (byte offsets < 2^31: d <= 2^21,
   // checked on the host); rows past M or N are clamped to the last row
@@ -478,7 +511,6 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
     for (int q = 0; q < 4; ++q) dma3(q, kt, xs, ws, ss_l, zs_l);
   };
 
-  const uint32_t one = fp16_1024_pair();
   // (arrays are sized for the largest WN and MTW and used up to WN, MTW: the
   // host pass of hipcc cannot instantiate lambdas capturing arrays of
   // template-dependent size)
@@ -631,7 +663,7 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
     const __amdgpu_buffer_rsrc_t rzp = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(zr + (size_t)nw0 * groups), (short)0, min(N - nw0, GB_N) * groups, kRsrcWord3);
     const int rr = 64 * w + lane;
-    const int pg = KT >> gsh;  // KT a multiple of the group's k-tiles (checked on the host)
+    const int pg = ((kt0 + KT - 1) >> gsh) - pg0 + 1;  // at most kPanelGroups (checked on the host)
     u4 sv[kPanelGroups / 8], zv[kPanelGroups / 16];
 #pragma unroll
     for (int c = 0; c < kPanelGroups / 8; ++c)
@@ -669,69 +701,78 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
   __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
   __builtin_amdgcn_s_barrier();
 
-  if constexpr (SPLIT) {
-    // Split k: every workgroup of the tile stores its fp32 partial tile
-    // (wavefront w's 256 accumulators per lane as [w][64 groups of 4][lane],
-    // 256 KB per workgroup) and counts itself in; the last to arrive adds the
-    // partial tiles in split order (so the sum does not depend on the order
-    // of arrival), resets the counter and runs the epilogue. As in the
-    // small-batch kernel, the workgroups of a tile share an XCD, so plain
-    // stores, an L2 atomic and loads that skip the per-CU cache suffice; where
-    // the dispatch rule is not established (sys) they go through memory.
-    __shared__ uint32_t s_last;
-    const int tile = mb * nblk + nb;
-    const size_t tile_floats = (size_t)GW_M * GB_N;
-    auto rsrc = [&](int k2) {
-      return __builtin_amdgcn_make_buffer_rsrc((void*)(part + ((size_t)tile * ksplit + k2) * tile_floats), (short)0,
-                                               (int)(tile_floats * 4), kRsrcWord3);
-    };
-    const __amdgpu_buffer_rsrc_t rmine = rsrc(ks);
+  if constexpr (SK) {
+    if (KT != L) {
+      // A partial tile: the workgroup stores its fp32 partial tile (wavefront
+      // w's 256 accumulators per lane as [w][64 groups of 4][lane], 256 KB) in
+      // its slot (0: its first segment, 1: its last; only those two can be
+      // partial) and counts itself in on the counter of the tile's first
+      // range; the last piece to arrive adds the pieces in range order (so
+      // the sum does not depend on the order of arrival), resets the counter
+      // and runs the epilogue. The ranges of a tile are those of one XCD, so
+      // plain stores, an L2 atomic and loads that skip the per-CU cache
+      // suffice; where the dispatch rule is not established (sys) they go
+      // through memory.
+      const size_t tile_floats = (size_t)GW_M * GB_N;
+      auto rsrc = [&](int j, int slot) {
+        return __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(part + ((size_t)(xcd * kSkSlots + j) * 2 + slot) * tile_floats), (short)0,
+            (int)(tile_floats * 4), kRsrcWord3);
+      };
+      const __amdgpu_buffer_rsrc_t rmine = rsrc(jw, first ? 0 : 1);
 #pragma unroll
-    for (int f = 0; f < 64; ++f) {
-      const int j = f >> 5, mm = (f >> 2) & 7, q = f & 3;
-      const u4 v = __builtin_bit_cast(u4, f4{acc[j][mm][4 * q], acc[j][mm][4 * q + 1], acc[j][mm][4 * q + 2],
-                                             acc[j][mm][4 * q + 3]});
-      const int off = ((w * 64 + f) * 64 + lane) * 16;
-      if (sys) __builtin_amdgcn_raw_buffer_store_b128(v, rmine, off, 0, kAuxSysW);
-      else __builtin_amdgcn_raw_buffer_store_b128(v, rmine, off, 0, 0);
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // this wavefront's stores have reached L2 / memory
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t old;
-      if (sys) old = __hip_atomic_fetch_add(&cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      else old = __hip_atomic_fetch_add(&cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = old == (uint32_t)(ksplit - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    // 16 groups of 4 accumulators at a time, summed in split order from the
-    // stored partial tiles (this workgroup's own included)
+      for (int f = 0; f < 64; ++f) {
+        const int j = f >> 5, mm = (f >> 2) & 7, q = f & 3;
+        const u4 v = __builtin_bit_cast(u4, f4{acc[j][mm][4 * q], acc[j][mm][4 * q + 1], acc[j][mm][4 * q + 2],
+                                               acc[j][mm][4 * q + 3]});
+        const int off = ((w * 64 + f) * 64 + lane) * 16;
+        if (sys) __builtin_amdgcn_raw_buffer_store_b128(v, rmine, off, 0, kAuxSysW);
+        else __builtin_amdgcn_raw_buffer_store_b128(v, rmine, off, 0, 0);
+      }
+      const int ja = owner((int64_t)tl * L);
+      const int pieces = owner((int64_t)tl * L + L - 1) - ja + 1;
+      const int ctr = xcd * slots + ja;
+      __builtin_amdgcn_s_waitcnt(0);  // this wavefront's stores have reached L2 / memory
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t old;
+        if (sys) old = __hip_atomic_fetch_add(&cnt[ctr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        else old = __hip_atomic_fetch_add(&cnt[ctr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = old == (uint32_t)(pieces - 1);
+      }
+      __syncthreads();
+      if (!s_last) return;
+      // the first piece is range ja's first segment if the tile is the first
+      // of that range, else its last
+      const int slot0 = rstart(ja) / L == tl ? 0 : 1;
+      // 16 groups of 4 accumulators at a time, summed in range order from the
+      // stored partial tiles (this workgroup's own included)
 #pragma unroll
-    for (int f0 = 0; f0 < 64; f0 += 16) {
-      f4 r[16];
-      for (int k2 = 0; k2 < ksplit; ++k2) {
-        const __amdgpu_buffer_rsrc_t rk = rsrc(k2);
-        f4 v[16];
+      for (int f0 = 0; f0 < 64; f0 += 16) {
+        f4 r[16];
+        for (int p = 0; p < pieces; ++p) {
+          const __amdgpu_buffer_rsrc_t rk = rsrc(ja + p, p == 0 ? slot0 : 0);
+          f4 v[16];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const int off = ((w * 64 + f0 + t) * 64 + lane) * 16;
-          v[t] = __builtin_bit_cast(f4, sys ? __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, kAuxSysW)
-                                            : __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, kAuxL2R));
+          for (int e = 0; e < 16; ++e) {
+            const int off = ((w * 64 + f0 + e) * 64 + lane) * 16;
+            v[e] = __builtin_bit_cast(f4, sys ? __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, kAuxSysW)
+                                              : __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, kAuxL2R));
+          }
+#pragma unroll
+          for (int e = 0; e < 16; ++e) r[e] = p == 0 ? v[e] : r[e] + v[e];
         }
 #pragma unroll
-        for (int t = 0; t < 16; ++t) r[t] = k2 == 0 ? v[t] : r[t] + v[t];
-      }
+        for (int e = 0; e < 16; ++e) {
+          const int f = f0 + e, j = f >> 5, mm = (f >> 2) & 7, q = f & 3;
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const int f = f0 + t, j = f >> 5, mm = (f >> 2) & 7, q = f & 3;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[j][mm][4 * q + e] = r[t][e];
+          for (int c = 0; c < 4; ++c) acc[j][mm][4 * q + c] = r[e][c];
+        }
       }
-    }
-    if (tid == 0) {
-      if (sys) __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      else __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) {
+        if (sys) __hip_atomic_store(&cnt[ctr], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        else __hip_atomic_store(&cnt[ctr], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
 
@@ -781,6 +822,50 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
       }
     }
   }
+  };
+
+  if constexpr (!SK) {
+    // one tile per workgroup: XCD x walks its n-blocks in super-blocks of 8
+    // m-blocks
+    const int idx = blockIdx.x >> 3;
+    const int mg = idx / (8 * nbx), rem = idx - mg * 8 * nbx;
+    const int nb = xcd + 8 * (rem / 8);
+    const int mb = mg * 8 + (rem & 7);
+    if (mb >= mblk) return;
+    segment(mb, nb, 0, L, 0, true);
+  } else {
+    // the XCD's tile t in the same order (the last super-block may hold
+    // fewer than 8 m-blocks)
+    int64_t u = rstart(jw);
+    const int64_t ue = rstart(jw + 1);
+    const int tfirst = (int)(u / L);
+    if constexpr (MODE == kModeSkOne) {
+      // every range lies in one tile (checked on the host)
+      const int t = tfirst;
+      const int sb = t / (8 * nbx);
+      const int rows = min(8, mblk - 8 * sb);
+      const int rem = t - sb * 8 * nbx;
+      segment(8 * sb + rem % rows, xcd + 8 * (rem / rows), (int)(u - (int64_t)t * L), (int)(ue - u), t, true);
+    } else {
+      while (u < ue) {
+        const int t = (int)(u / L);
+        const int k0 = (int)(u - (int64_t)t * L);
+        const int k1 = (int)min((int64_t)L, k0 + (ue - u));
+        const int sb = t / (8 * nbx);
+        const int rows = min(8, mblk - 8 * sb);
+        const int rem = t - sb * 8 * nbx;
+        segment(8 * sb + rem % rows, xcd + 8 * (rem / rows), k0, k1 - k0, t, t == tfirst);
+        u += k1 - k0;
+        if (u < ue) {
+          // the epilogue's LDS reads before the next segment's DMA and panel
+          // (an LDS wait and a barrier: __syncthreads would also wait for the
+          // epilogue's global stores)
+          __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+          __builtin_amdgcn_s_barrier();
+        }
+      }
+    }
+  }
 }
 
 template <int KS, int MT, int NT>
@@ -798,21 +883,75 @@ GemmPlan plan_w4_gemm(int64_t M, int64_t N, int64_t d) {
   const int64_t nblk = (N + GB_N - 1) / GB_N, mblkw = (M + GW_M - 1) / GW_M;
   const int64_t tiles = nblk * mblkw, kt = d / GB_K;
   if (M <= 16 || d > (int64_t(1) << 21) || kt % 2 || d < 4 * GB_K) return p;
+  // one tile per workgroup from kWideMinTiles tiles (stream-K measured slower
+  // there: 2048 x 4096 -> 14336, 448 tiles, 252 against 223 us, the
+  // workgroups of an XCD no longer reading the same k-tiles at the same
+  // time); below, stream-K when every XCD holds n-blocks
   if (tiles >= kWideMinTiles) {
     p.wide = true;
     return p;
   }
-  if (tiles < kSplitMinTiles) return p;
-  // split k across workgroups until the tiles fill one workgroup per CU
-  int ks = 1;
-  while (2 * ks <= kMaxSplit && tiles * 2 * ks <= kWideMinTiles && kt % (4 * ks) == 0 && kt / (2 * ks) >= kMinSplitKT)
-    ks *= 2;
-  if (ks < 2) return p;
-  p.wide = true;
-  p.ksplit = ks;
-  p.partial_bytes = (size_t)tiles * ks * GW_M * GB_N * 4;
+  const int64_t nbmin = nblk / 8, nbmax = (nblk + 7) / 8;
+  if (nbmin < 1) return p;
+  // Workgroups per XCD: the fewest k-tiles per range on the busiest XCD,
+  // counting kSkMisaligned more for ranges that do not cut the tiles into
+  // equal pieces (nor hold whole tiles): their pieces start at different k,
+  // so the workgroups of an XCD stop sharing k-tiles in L2 (measured: 1300 x
+  // 8192 -> 4096, 96 tiles of 128 k-tiles, 123 us with ranges of 48 against
+  // 113 with 24 workgroups per XCD taking half tiles). Every range keeps at
+  // least two k-tiles on the least busy XCD and kMinSplitKT on the busiest;
+  // ranges of whole tiles (one tile per workgroup on fewer workgroups than
+  // CUs) are not taken, nor misaligned ones on fewer than 3/4 of the CUs.
+  int best = 0;
+  int64_t best_cost = 0;
+  for (int sl = kSkSlots; sl >= kSkSlots / 2; sl -= 4) {
+    const int64_t units = nbmax * mblkw * kt;
+    if (nbmin * mblkw * kt < 2 * sl) continue;
+    const int64_t U = (units + sl - 1) / sl;
+    if (U < kMinSplitKT || U % kt == 0) continue;  // (whole tiles: fewer workgroups than CUs)
+    const bool aligned = units % (2 * sl) == 0 && kt % U == 0;
+    if (!aligned && sl < kSkSlots * 3 / 4) continue;
+    const int64_t cost = U + (aligned ? 0 : kSkMisaligned);
+    if (!best || cost < best_cost) {
+      best = sl;
+      best_cost = cost;
+    }
+  }
+  if (best) {
+    p.wide = p.sk = true;
+    p.sk_slots = best;
+    p.partial_bytes = (size_t)8 * kSkSlots * 2 * GW_M * GB_N * 4;
+  }
   return p;
 }
+
+namespace {
+// A stream-K split's most groups per segment panel (from the 8-aligned group
+// below a segment's first k-tile's: whole tiles span all of a row's groups,
+// partial ones lie at the ends of the ranges), and whether every range lies
+// in one tile.
+void sk_shape(int64_t nblk, int64_t mblkw, int64_t L, int gsh, int slots, int64_t* panel_groups, bool* one_tile) {
+  auto span = [&](int64_t kt0, int64_t KT) { return ((kt0 + KT - 1) >> gsh) - ((kt0 >> gsh) & ~int64_t(7)) + 1; };
+  int64_t most = 0;
+  bool one = true;
+  for (int64_t x = 0; x < 8; ++x) {
+    const int64_t nbx = (nblk - x + 7) / 8;
+    if (nbx <= 0) continue;
+    const int64_t H = nbx * mblkw * L / 2;
+    for (int64_t j = 0; j < slots; ++j) {
+      const int64_t s = 2 * (j * H / slots), e = 2 * ((j + 1) * H / slots);
+      if (e <= s) continue;
+      const int64_t t = s / L, k0 = s - t * L, te = (e - 1) / L;
+      one = one && te == t;
+      most = std::max(most, span(k0, std::min(L - k0, e - s)));
+      if (te > t) most = std::max(most, span(0, e - te * L));
+      if (te > t + 1 || (te > t && k0 == 0)) most = std::max(most, span(0, L));
+    }
+  }
+  *panel_groups = most;
+  *one_tile = one;
+}
+}  // namespace
 
 hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
                           const uint8_t* zeros, const uint16_t* bias, uint16_t* y, int64_t M,
@@ -838,29 +977,35 @@ hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint1
   const bool ks4 = narrow && (d / GB_K) % 4 == 0 && d / GB_K >= 16;
   const unsigned g = (unsigned)blocks;
   // layers with many 256 x 256 tiles take the one-wavefront-per-SIMD kernel,
-  // layers with fewer the same kernel with k split across workgroups when the
-  // workspace holds the partial tiles
+  // one tile per workgroup when the tiles fill whole rounds of one workgroup
+  // per CU, else stream-K when the workspace holds the partial tiles
   const GemmPlan plan = plan_w4_gemm(M, N, d);
-  if (plan.wide && (plan.ksplit == 1 || (cnt && part))) {
+  if (plan.wide && (!plan.sk || (cnt && part))) {
     const int mblkw = (int)((M + GW_M - 1) / GW_M);
-    const int64_t bw = 8 * ((nblk256 + 7) / 8) * (((int64_t)mblkw + 7) / 8) * 8 * plan.ksplit;
+    const int64_t L = d / GB_K;
     const int64_t groups = d >> (6 + gsh);
-    const int sys = plan.ksplit > 1 && !xcd_dispatch_is_round_robin();
-    // the scale and zero panel: whole groups per workgroup, at most 64 of
-    // them, a multiple of 8; scales 16-byte and zeros 8-byte aligned
-    const int64_t ktw = d / GB_K / plan.ksplit, pg = ktw >> gsh;
-    const bool panel = ktw % (int64_t(1) << gsh) == 0 && pg <= kPanelGroups && pg % 8 == 0 &&
-                       ((uintptr_t)scales & 15) == 0 && ((uintptr_t)zeros & 7) == 0;
+    const int sys = plan.sk && !xcd_dispatch_is_round_robin();
+    // the scale and zero panel: at most kPanelGroups groups per segment;
+    // rows of a multiple of 8 groups, scales 16-byte and zeros 8-byte aligned
+    int64_t pgs = groups;
+    bool one_tile = false;
+    if (plan.sk) sk_shape(nblk256, mblkw, L, gsh, plan.sk_slots, &pgs, &one_tile);
+    const bool panel = pgs <= kPanelGroups && groups % 8 == 0 && ((uintptr_t)scales & 15) == 0 &&
+                       ((uintptr_t)zeros & 7) == 0;
+    const int64_t bw = plan.sk ? 8 * plan.sk_slots : 8 * ((nblk256 + 7) / 8) * (((int64_t)mblkw + 7) / 8) * 8;
     auto go = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, dim3((unsigned)bw), dim3(256), 0, stream, x, qweight, scales, zeros, bias, y,
-                         (int)M, (int)N, (int)d, gsh, mblkw, nblk256, plan.ksplit, part, cnt, sys);
+                         (int)M, (int)N, (int)d, gsh, mblkw, nblk256, plan.sk_slots, part, cnt, sys);
     };
-    if (plan.ksplit > 1) {
-      if (panel) go(w4_gemm_wide_kernel<kWideWN, true, true>);
-      else go(w4_gemm_wide_kernel<kWideWN, false, true>);
+    if (plan.sk && one_tile) {
+      if (panel) go(w4_gemm_wide_kernel<kWideWN, true, kModeSkOne>);
+      else go(w4_gemm_wide_kernel<kWideWN, false, kModeSkOne>);
+    } else if (plan.sk) {
+      if (panel) go(w4_gemm_wide_kernel<kWideWN, true, kModeSkMany>);
+      else go(w4_gemm_wide_kernel<kWideWN, false, kModeSkMany>);
     } else {
-      if (panel) go(w4_gemm_wide_kernel<kWideWN, true, false>);
-      else go(w4_gemm_wide_kernel<kWideWN, false, false>);
+      if (panel) go(w4_gemm_wide_kernel<kWideWN, true, kModeTile>);
+      else go(w4_gemm_wide_kernel<kWideWN, false, kModeTile>);
     }
     return hipGetLastError();
   }

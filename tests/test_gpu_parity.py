@@ -323,17 +323,25 @@ def test_linear_wide_tiles(paro, M, d, N):
     check_linear(paro, x, layer, rotated=False, rows=rows)
 
 
-# layers with 16 to 255 output tiles of 256 x 256 and long k split k across 2 to
-# 8 workgroups per tile (full workspace); with the minimum workspace the same
-# call runs the 128 x 256-tile kernel. Both against the oracle: the down-proj
-# configuration (two splits, 56 groups of 128 per split in the scale/zero
-# panel) and ragged shapes: two splits of 32 groups (panel); four splits of 28
-# groups (not a multiple of 8: no panel); eight splits of 24 groups (panel);
-# four splits of 56 groups of 64 (panel) and of 14 groups of 256 (no panel).
-@pytest.mark.parametrize("M,d,N,G", [(2048, 14336, 4096, 128), (1000, 8192, 2064, 128), (600, 14336, 4096, 128),
-                                     (512, 24576, 2048, 128), (700, 14336, 4096, 64), (600, 14336, 4096, 256)])
-def test_linear_split_k(paro, M, d, N, G):
-    log(f"linear split-k M={M} d={d} N={N} group={G}")
+# layers with fewer than 256 output tiles of 256 x 256 and long k run
+# stream-K when the workspace holds the partial tiles (full workspace): each
+# XCD's tiles are laid end to end as one sequence of k-tiles and shared out
+# among 16 to 32 workgroups of the XCD. With the minimum workspace the same
+# call runs the smaller-tile kernel. Both against the oracle: the down-proj
+# configuration (32 workgroups per XCD, each tile in two pieces, 56 groups of
+# 128 per piece in the scale/zero panel), 3072 tokens (ranges of 1.3 tiles:
+# pieces at both ends, too many groups for the panel), ragged M and N with
+# unequal XCDs (13 and 9 n-blocks), groups of 256 and of 64, 24 and 16
+# workgroups per XCD (tiles cut in 2 or 4 equal pieces), and layers that do
+# not take stream-K (q/o-proj at 2048 tokens: the smaller-tile kernel; 448
+# tiles of 256 x 256: one per workgroup).
+@pytest.mark.parametrize("M,d,N,G,sk", [(2048, 14336, 4096, 128, True), (3072, 14336, 4096, 128, True),
+                                        (2600, 8192, 3088, 128, True), (1500, 16384, 4096, 256, True),
+                                        (1300, 8192, 4096, 64, True), (1000, 8192, 2064, 128, True),
+                                        (600, 14336, 4096, 128, True), (2048, 4096, 4096, 128, False),
+                                        (2048, 4096, 14336, 128, False)])
+def test_linear_stream_k(paro, M, d, N, G, sk):
+    log(f"linear stream-k M={M} d={d} N={N} group={G}")
     x, layer, b = synthetic.linear_case(seed=M + d + N + 7, M=M, d=d, N=N, group=G)
     assert layer.group == G
     r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, G)
@@ -344,15 +352,15 @@ def test_linear_split_k(paro, M, d, N, G):
                                    layer.alpha, b)
     full = paro.paro_w4_linear_workspace_size(r, M, N, d)
     minimum = 16384 + (M * d * 2 + 255) // 256 * 256
-    assert full > minimum
-    for nbytes in (full, minimum, full):
+    assert full == minimum + (128 << 20 if sk else 0)
+    for nbytes in ((full, minimum, full) if sk else (full,)):
         ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
         y = host(paro.paro_w4_linear(r, dev(x), qw, s, z, dev(b), group=G, workspace=ws))
         assert np.all(np.isfinite(y[rows].astype(np.float32)))
         metrics.assert_linear_close(y[rows], ref)
         assert int(ws[:16384].count_nonzero()) == 0  # every call leaves the counters zero
-    # plain layer: the split run (default workspace) and, with no workspace at
-    # all, the 128 x 256-tile kernel
+    # plain layer: the default workspace (stream-K where planned) and, with no
+    # workspace at all, one tile per workgroup or the smaller-tile kernel
     refp = oracle.rotated_w4_linear(x[rows], host(qw), host(s), host(z), G, bias=b)
     yp = host(paro.paro_w4_linear(None, dev(x), qw, s, z, dev(b), group=G))
     metrics.assert_linear_close(yp[rows], refp)
