@@ -184,10 +184,10 @@ int paro_quantize_weights(const paro_rotation* r, const uint16_t* w, int64_t N, 
 /* Bytes of device workspace with which paro_w4_linear runs its fastest
  * kernels for this plan (NULL: plain W4) and these sizes; 0 means the call
  * uses no workspace. For M > 16 on layers with fewer than 256 output tiles of
- * 256 x 256 (at least 16) this includes fp32 partial tiles (256 KB per tile
- * and k-split) for splitting k across workgroups; paro_w4_linear also runs,
- * with the smaller-tile kernel, on the minimum: 16 KiB + M d 2 bytes
- * (rounded up to 256) with a plan, none without. */
+ * 256 x 256 whose k-tiles can be shared out among the workgroups (stream-K)
+ * this includes 128 MiB of fp32 partial tiles (two of 256 KB per workgroup);
+ * paro_w4_linear also runs, with the smaller-tile kernel, on the minimum:
+ * 16 KiB + M d 2 bytes (rounded up to 256) with a plan, none without. */
 size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t N, int64_t d);
 
 /*
@@ -209,7 +209,7 @@ size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t 
  *   d <= 2^22, M < 2^30, else PARO_ERR_UNSUPPORTED.
  *   workspace, workspace_bytes: device memory of
  *            paro_w4_linear_workspace_size(r, M, N, d) bytes, or of at least
- *            the minimum given there (M > 16: then without the k-split),
+ *            the minimum given there (M > 16: then without stream-K),
  *            256-byte aligned (may be NULL when the size in use is 0;
  *            smaller than the minimum: PARO_ERR_WORKSPACE). Its first 16 KiB hold
  *            arrival counters that must be zero before the first call that
@@ -222,17 +222,19 @@ size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t 
  * plans of group 64 or 128 that execute at most 8 stages, applies the
  * transform to the activations inside the same kernel; other plans rotate
  * into the workspace first. M > 16 rotates into the workspace and then runs
- * a matrix-core kernel: 256 x 256 tiles from 256 such tiles; with fewer (at
- * least 16) the same kernel with k split across 2 to 8 workgroups per tile,
- * which meet through fp32 partial tiles in the workspace (the last to arrive
- * adds them in split order), when the workspace holds them; else a kernel
- * with 128 x 256 tiles, or 64 x 256 or 64 x 128 (k split two or four ways
- * inside the workgroup) for layers with few tiles.
+ * a matrix-core kernel: 256 x 256 tiles from 256 such tiles, one per
+ * workgroup; with fewer, when every XCD holds n-blocks and k is long enough,
+ * the same kernel with each XCD's k-tiles shared out in equal ranges among 16
+ * to 32 of its workgroups (stream-K): partial tiles meet through fp32 partial
+ * tiles in the workspace (the last piece to arrive adds them in k order),
+ * when the workspace holds them; else a kernel with 128 x 256 tiles, or
+ * 64 x 256 or 64 x 128 (k split two or four ways inside the workgroup) for
+ * layers with few tiles.
  *
  * Arithmetic: X' exactly as paro_rotate computes it (fp16); fp32 accumulation
  * of exact fp16 products against the fp16 rounding of each dequantized weight
  * (q - z) * s, in an order that depends on the sizes (and for M > 16 on
- * whether the workspace holds the k-split's partial tiles) but not on timing;
+ * whether the workspace holds the stream-K partial tiles) but not on timing;
  * fp16 output.
  * Errors: PARO_ERR_NULL, PARO_ERR_SHAPE, PARO_ERR_ALIGN, PARO_ERR_UNSUPPORTED,
  * PARO_ERR_WORKSPACE, PARO_ERR_HIP.
@@ -257,7 +259,7 @@ int paro_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qwe
  *            paro_w4_linear_workspace_size) must not exceed that size (for
  *            example M x d <= 32 Mi elements for a rotated layer with
  *            M > 16), else PARO_ERR_WORKSPACE and nothing is enqueued; the
- *            k-split's partial tiles are used when they fit as well.
+ *            stream-K partial tiles are used when they fit as well.
  *   Sharing: every call on one device uses that device's single array, so
  *            calls that may run at the same time on one device (several
  *            streams or threads) race and give wrong results: serialise them,
