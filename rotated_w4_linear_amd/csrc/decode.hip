@@ -75,8 +75,12 @@ __device__ __forceinline__ int xl_offset(int m, int k) {
 // T: token rows staged and rotated (4 for M <= 4, else 16); MFMA columns past
 // T read tile rows that were never written and are ignored like those past M.
 // TJ: 16-row tiles per wavefront (the workgroup owns 64 TJ output channels).
+// At least four wavefronts per SIMD (registers within 128): with the
+// transform at T = 16 the kernel took 117 VGPRs and 16 AGPRs, three
+// wavefronts per SIMD, and layers with more than 768 workgroups (gate/up-proj
+// at M = 16: 896) then ran in two rounds.
 template <bool ROT, int KMAX, bool KEXACT, bool FAST, int T, int TJ, bool SZV>
-__global__ __launch_bounds__(256) void w4_decode_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void w4_decode_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zr,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N, int d,
@@ -444,10 +448,12 @@ hipError_t launch_w4_decode(const uint16_t* x, const uint8_t* qweight, const uin
   // but with the transform fused and more than 4 tokens, every workgroup's
   // transform of its k-slice (an LDS-bound chain of exchanges) sits on the
   // critical path, and 128-channel workgroups halve how often each segment is
-  // transformed (4096 -> 4096 at M = 16: 10.9 -> 10.0 us measured)
+  // transformed (4096 -> 4096 at M = 16: 10.9 -> 10.0 us measured), unless
+  // they would leave half the CUs idle (4096 -> 1024 at M = 16: 8.74 -> 7.76
+  // us with 64-channel workgroups)
   const int64_t wg128 = ((N + 127) / 128) * ((d / 128 + DK_SEGS - 1) / DK_SEGS);
   const bool small = M <= 4;
-  const bool tj1 = wg128 < 384 && (small || r == nullptr);
+  const bool tj1 = wg128 < 384 && (small || r == nullptr || wg128 < 128);
   // full slices and aligned bases: vector scale / zero loads
   if (group == 128 && (d / 128) % DK_SEGS == 0 && ((uintptr_t)scales & 7) == 0 &&
       ((uintptr_t)zeros & 3) == 0) {
