@@ -75,22 +75,30 @@ __device__ __forceinline__ int xl_offset(int m, int k) {
 // T: token rows staged and rotated (4 for M <= 4, else 16); MFMA columns past
 // T read tile rows that were never written and are ignored like those past M.
 // TJ: 16-row tiles per wavefront (the workgroup owns 64 TJ output channels).
-// At least four wavefronts per SIMD (registers within 128): with the
-// transform at T = 16 the kernel took 117 VGPRs and 16 AGPRs, three
+// TB: blocks of 16 token columns (T = 16; M up to 16 TB): the blocks'
+// activations are transformed one after the other, and every dequantized
+// weight fragment feeds TB MFMAs.
+// At least four wavefronts per SIMD with one block (registers within 128):
+// with the transform at T = 16 the kernel took 117 VGPRs and 16 AGPRs, three
 // wavefronts per SIMD, and layers with more than 768 workgroups (gate/up-proj
 // at M = 16: 896) then ran in two rounds.
-template <bool ROT, int KMAX, bool KEXACT, bool FAST, int T, int TJ, bool SZV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void w4_decode_kernel(
+template <bool ROT, int KMAX, bool KEXACT, bool FAST, int T, int TJ, bool SZV, int TB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB == 1 ? 4 : 2))) void w4_decode_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zr,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N, int d,
     const uint32_t* __restrict__ tab, int K, float* part, uint32_t* cnt, int ksl, int nbl,
     int nb_base, int sys, int gsh) {
-  // X' tile: [16 tokens][64 chunks of 16 bytes]; chunk c of token m is stored
-  // at position c ^ m, so the 16 tokens of one MFMA operand read land on 16
-  // distinct 16-byte positions.
-  __shared__ u4 xl[DK_TOK * 64];
-  __shared__ rot::f4 xch[ROT ? 4 * (T / 4) * 64 : 1];
+  // X' tile: [16 TB tokens][64 chunks of 16 bytes]; chunk c of token m is
+  // stored at position c ^ m, so the 16 tokens of one MFMA operand read land
+  // on 16 distinct 16-byte positions.
+  __shared__ u4 xl[DK_TOK * TB * 64];
+  // the transform's exchange slots; with four token blocks they share the
+  // LDS of the last block's rows (written only after every wavefront's last
+  // transform), so that two workgroups fit a CU
+  constexpr bool XCH_IN_XL = ROT && TB == 4;
+  __shared__ rot::f4 xch_own[ROT && !XCH_IN_XL ? 4 * (T / 4) * 64 : 1];
+  rot::f4* xch = XCH_IN_XL ? (rot::f4*)&xl[DK_TOK * (TB - 1) * 64] : xch_own;
   __shared__ int s_last;
 
   constexpr int NB = 64 * TJ;  // output channels per workgroup
@@ -113,13 +121,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void w
   // (in a slice cut short by the end of d, wavefronts without a segment
   // process a copy of the last one into their own, never read, part of the
   // tile: no branch lets the compiler sink these loads behind the weights)
+  // (every token block's activations before the weights: loads complete in
+  // order, so a block requested after the weights would wait for all of them)
   const int seg = min(g0 + w, groups - 1);
-  uint32_t raw[T];
+  uint32_t raw[TB][T];
   rot::Lane<1, KMAX, KEXACT, FAST> L;
   {
     const uint32_t* xs = (const uint32_t*)(x + seg * 128) + lane;
 #pragma unroll
-    for (int i = 0; i < T; ++i) raw[i] = xs[(size_t)min(i, M - 1) * (size_t)(d >> 1)];
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int i = 0; i < T; ++i) raw[tb][i] = xs[(size_t)min(16 * tb + i, M - 1) * (size_t)(d >> 1)];
     if constexpr (ROT) L.load(tab, seg, K, lane);
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -180,34 +192,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void w
   // in-order load counter would otherwise hold the weight loads back
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- 3. X' of the segment into the LDS tile --------------------------------
-  {
+  // ---- 3. X' of the segment into the LDS tile (block by block) --------------
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) {
     uint32_t pk[T];
     int k0;  // slice-local channel of the low half of this lane's pair
     if constexpr (ROT) {
       float X[1][T], B[1][T];
 #pragma unroll
-      for (int i = 0; i < T; ++i) L.unpack(raw[i], 0, X[0][i], B[0][i]);
+      for (int i = 0; i < T; ++i) L.unpack(raw[tb][i], 0, X[0][i], B[0][i]);
       L.template run<T>(X, B, (char*)&xch[w * (T / 4) * 64]);
 #pragma unroll
       for (int i = 0; i < T; ++i) pk[i] = L.pack(X[0][i], B[0][i], 0);
       k0 = 128 * w + (int)(L.stoff[0] >> 1);
+      if (XCH_IN_XL && tb == TB - 1) __syncthreads();  // every wavefront is done with the slots
     } else {
 #pragma unroll
-      for (int i = 0; i < T; ++i) pk[i] = raw[i];
+      for (int i = 0; i < T; ++i) pk[i] = raw[tb][i];
       k0 = 128 * w + 2 * lane;
     }
     // (k0 is even: the lane's two channels are adjacent halves of one chunk)
 #pragma unroll
-    for (int i = 0; i < T; ++i) *(uint32_t*)(xlb + xl_offset(i, k0)) = pk[i];
+    for (int i = 0; i < T; ++i) *(uint32_t*)(xlb + xl_offset(16 * tb + i, k0)) = pk[i];
   }
   __syncthreads();
 
   // ---- 4. dequantize and multiply, group by group as the weights land -------
   const uint32_t one = fp16_1024_pair();
-  f4 acc[TJ];
+  f4 acc[TB][TJ];
 #pragma unroll
-  for (int j = 0; j < TJ; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[tb][j] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int q = 0; q < DK_SEGS; ++q) {
     if (q < nq) {
@@ -221,16 +237,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void w
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const h8 b = *(const h8*)(xlb + (r * 64 + ((16 * q + 4 * kq + i) ^ r)) * 16);
+        h8 b[TB];
 #pragma unroll
-        for (int j = 0; j < TJ; ++j)
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              dequant8(wv[j][q][i], zz[j], ss[j], zz16[j], ss16[j], one), b, acc[j], 0, 0, 0);
+        for (int tb = 0; tb < TB; ++tb) {
+          const int m = 16 * tb + r;
+          b[tb] = *(const h8*)(xlb + (m * 64 + ((16 * q + 4 * kq + i) ^ m)) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const h8 a = dequant8(wv[j][q][i], zz[j], ss[j], zz16[j], ss16[j], one);
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb)
+            acc[tb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[tb], acc[tb][j], 0, 0, 0);
+        }
       }
     }
   }
 
-  // ---- 5. acc[j][e] = Y[n = rb + 16 j + 4 kq + e][m = r] ------------------------
+  // ---- 5. acc[tb][j][e] = Y[n = rb + 16 j + 4 kq + e][m = 16 tb + r] ------------
   auto store_y = [&](int m, int n, f4 v) {
     if (bias) {
       const uint2 braw = *(const uint2*)(bias + n);
@@ -246,10 +270,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void w
   };
   if (ksl == 1) {
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int n = rb + 16 * j + 4 * kq;
-      if (r < M && n < N) store_y(r, n, acc[j]);
-    }
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int n = rb + 16 * j + 4 * kq, m = 16 * tb + r;
+        if (m < M && n < N) store_y(m, n, acc[tb][j]);
+      }
     return;
   }
   // partial sums: [k-slice][M][N] fp32; offsets in bytes from part (< 2^31,
@@ -257,15 +283,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void w
   const __amdgpu_buffer_rsrc_t rp =
       __builtin_amdgcn_make_buffer_rsrc((void*)part, (short)0, 0x7fffffff, kRsrcWord3);
 #pragma unroll
-  for (int j = 0; j < TJ; ++j) {
-    const int n = rb + 16 * j + 4 * kq;
-    if (r < M && n < N) {
-      const int off = (int)((((size_t)ks * M + r) * N + n) * 4);
-      const u4 v = __builtin_bit_cast(u4, acc[j]);
-      if (sys) __builtin_amdgcn_raw_buffer_store_b128(v, rp, off, 0, kAuxSys);
-      else __builtin_amdgcn_raw_buffer_store_b128(v, rp, off, 0, 0);
+  for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int n = rb + 16 * j + 4 * kq, m = 16 * tb + r;
+      if (m < M && n < N) {
+        const int off = (int)((((size_t)ks * M + m) * N + n) * 4);
+        const u4 v = __builtin_bit_cast(u4, acc[tb][j]);
+        if (sys) __builtin_amdgcn_raw_buffer_store_b128(v, rp, off, 0, kAuxSys);
+        else __builtin_amdgcn_raw_buffer_store_b128(v, rp, off, 0, 0);
+      }
     }
-  }
   __builtin_amdgcn_s_waitcnt(0);  // this wavefront's stores have reached L2 / memory
   __syncthreads();
   if (tid == 0) {
@@ -394,7 +422,7 @@ bool xcd_dispatch_is_round_robin() {
 
 namespace {
 
-template <bool ROT, int KMAX, bool KEXACT, bool FAST, int T, int TJ, bool SZV>
+template <bool ROT, int KMAX, bool KEXACT, bool FAST, int T, int TJ, bool SZV, int TB>
 hipError_t launch_t(const uint16_t* x, const uint8_t* qw, const uint16_t* sc, const uint8_t* zr,
                     const uint16_t* bias, uint16_t* y, int M, int N, int d, int gsh,
                     const paro_rotation* r, void* ws, hipStream_t stream) {
@@ -409,7 +437,7 @@ hipError_t launch_t(const uint16_t* x, const uint8_t* qw, const uint16_t* sc, co
   for (int nb0 = 0; nb0 < nbl_all; nb0 += kMaxNb) {
     const int nbl = min(kMaxNb, nbl_all - nb0);
     const unsigned blocks = 8u * (unsigned)ksl * (unsigned)((nbl + 7) / 8);
-    hipLaunchKernelGGL((w4_decode_kernel<ROT, KMAX, KEXACT, FAST, T, TJ, SZV>), dim3(blocks), dim3(256), 0,
+    hipLaunchKernelGGL((w4_decode_kernel<ROT, KMAX, KEXACT, FAST, T, TJ, SZV, TB>), dim3(blocks), dim3(256), 0,
                        stream, x, qw, sc, zr, bias, y, M, N, d, tab, K, part, cnt, ksl, nbl, nb0,
                        sys, gsh);
     const hipError_t e = hipGetLastError();
@@ -418,17 +446,17 @@ hipError_t launch_t(const uint16_t* x, const uint8_t* qw, const uint16_t* sc, co
   return hipSuccess;
 }
 
-template <int T, int TJ, bool SZV>
+template <int T, int TJ, bool SZV, int TB>
 hipError_t launch_plan(const uint16_t* x, const uint8_t* qw, const uint16_t* sc, const uint8_t* zr,
                        const uint16_t* bias, uint16_t* y, int m, int n, int k, int gsh,
                        const paro_rotation* r, void* ws, hipStream_t stream) {
-  if (!r) return launch_t<false, 0, true, true, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, gsh, r, ws, stream);
-  if (r->lay.stages == 0) return launch_t<true, 0, true, true, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, gsh, r, ws, stream);
+  if (!r) return launch_t<false, 0, true, true, T, TJ, SZV, TB>(x, qw, sc, zr, bias, y, m, n, k, gsh, r, ws, stream);
+  if (r->lay.stages == 0) return launch_t<true, 0, true, true, T, TJ, SZV, TB>(x, qw, sc, zr, bias, y, m, n, k, gsh, r, ws, stream);
   if (r->lay.fast) {
-    if (r->lay.stages == 8) return launch_t<true, 8, true, true, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, gsh, r, ws, stream);
-    return launch_t<true, 8, false, true, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, gsh, r, ws, stream);
+    if (r->lay.stages == 8) return launch_t<true, 8, true, true, T, TJ, SZV, TB>(x, qw, sc, zr, bias, y, m, n, k, gsh, r, ws, stream);
+    return launch_t<true, 8, false, true, T, TJ, SZV, TB>(x, qw, sc, zr, bias, y, m, n, k, gsh, r, ws, stream);
   }
-  return launch_t<true, 8, false, false, T, TJ, SZV>(x, qw, sc, zr, bias, y, m, n, k, gsh, r, ws, stream);
+  return launch_t<true, 8, false, false, T, TJ, SZV, TB>(x, qw, sc, zr, bias, y, m, n, k, gsh, r, ws, stream);
 }
 
 }  // namespace
@@ -455,17 +483,27 @@ hipError_t launch_w4_decode(const uint16_t* x, const uint8_t* qweight, const uin
   const bool small = M <= 4;
   const bool tj1 = wg128 < 384 && (small || r == nullptr || wg128 < 128);
   // full slices and aligned bases: vector scale / zero loads
-  if (group == 128 && (d / 128) % DK_SEGS == 0 && ((uintptr_t)scales & 7) == 0 &&
-      ((uintptr_t)zeros & 3) == 0) {
-    if (tj1) return small ? launch_plan<4, 1, true>(x, qweight, scales, zeros, bias, y, m, n, k, gsh, r, ws, stream)
-                          : launch_plan<16, 1, true>(x, qweight, scales, zeros, bias, y, m, n, k, gsh, r, ws, stream);
-    return small ? launch_plan<4, 2, true>(x, qweight, scales, zeros, bias, y, m, n, k, gsh, r, ws, stream)
-                 : launch_plan<16, 2, true>(x, qweight, scales, zeros, bias, y, m, n, k, gsh, r, ws, stream);
+  const bool szv = group == 128 && (d / 128) % DK_SEGS == 0 && ((uintptr_t)scales & 7) == 0 &&
+                   ((uintptr_t)zeros & 3) == 0;
+  // token blocks of 16 beyond 16 tokens
+  const int tb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+#define PARO_DECODE_PLAN(T_, TJ_, SZV_, TB_) \
+  launch_plan<T_, TJ_, SZV_, TB_>(x, qweight, scales, zeros, bias, y, m, n, k, gsh, r, ws, stream)
+  if (tb == 1) {
+    if (szv) {
+      if (tj1) return small ? PARO_DECODE_PLAN(4, 1, true, 1) : PARO_DECODE_PLAN(16, 1, true, 1);
+      return small ? PARO_DECODE_PLAN(4, 2, true, 1) : PARO_DECODE_PLAN(16, 2, true, 1);
+    }
+    if (tj1) return small ? PARO_DECODE_PLAN(4, 1, false, 1) : PARO_DECODE_PLAN(16, 1, false, 1);
+    return small ? PARO_DECODE_PLAN(4, 2, false, 1) : PARO_DECODE_PLAN(16, 2, false, 1);
   }
-  if (tj1) return small ? launch_plan<4, 1, false>(x, qweight, scales, zeros, bias, y, m, n, k, gsh, r, ws, stream)
-                        : launch_plan<16, 1, false>(x, qweight, scales, zeros, bias, y, m, n, k, gsh, r, ws, stream);
-  return small ? launch_plan<4, 2, false>(x, qweight, scales, zeros, bias, y, m, n, k, gsh, r, ws, stream)
-               : launch_plan<16, 2, false>(x, qweight, scales, zeros, bias, y, m, n, k, gsh, r, ws, stream);
+  if (tb == 2) {
+    if (szv) return tj1 ? PARO_DECODE_PLAN(16, 1, true, 2) : PARO_DECODE_PLAN(16, 2, true, 2);
+    return tj1 ? PARO_DECODE_PLAN(16, 1, false, 2) : PARO_DECODE_PLAN(16, 2, false, 2);
+  }
+  if (szv) return tj1 ? PARO_DECODE_PLAN(16, 1, true, 4) : PARO_DECODE_PLAN(16, 2, true, 4);
+  return tj1 ? PARO_DECODE_PLAN(16, 1, false, 4) : PARO_DECODE_PLAN(16, 2, false, 4);
+#undef PARO_DECODE_PLAN
 }
 
 }  // namespace paro

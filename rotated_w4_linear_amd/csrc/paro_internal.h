@@ -160,7 +160,7 @@ bool xcd_dispatch_is_round_robin();
 // kDecodeCounterBytes of arrival counters (zero between calls), then the fp32
 // partial sums [ceil(d / 512)][M][N].
 constexpr size_t kDecodeCounterBytes = 16384;
-constexpr int64_t kDecodeMaxM = 16;
+constexpr int64_t kDecodeMaxM = 64;
 bool decode_fuses_rotation(const paro_rotation* r);
 // Devices the library keeps per-device state for (device ordinals below this).
 constexpr int kMaxDevices = 64;

@@ -294,13 +294,28 @@ def test_linear_decode(paro, M):
     check_linear(paro, synthetic.decode_x(M), layer, rotated=False)
 
 
+# 17 to 64 tokens take the small-batch kernel with two or four blocks of 16
+# token columns (the last block ragged): 4096 -> 4096 (128-channel
+# workgroups), 4096 -> 1024 (64-channel), 1152 -> 1040 (scales and zeros
+# loaded one group at a time), groups of 64 and 256 (the latter transformed
+# into the workspace first).
+@pytest.mark.parametrize("M", [17, 32, 33, 48, 64])
+@pytest.mark.parametrize("d,N,G", [(4096, 4096, 128), (4096, 1024, 128), (1152, 1040, 128), (1024, 272, 64),
+                                   (1024, 272, 256)])
+def test_linear_small_batch_blocks(paro, M, d, N, G):
+    log(f"linear small batch M={M} d={d} N={N} group={G}")
+    x, layer, b = synthetic.linear_case(seed=700 + M + d + N + G, M=M, d=d, N=N, group=G)
+    check_linear(paro, x, layer, bias=b)
+    check_linear(paro, x, layer, rotated=False)
+
+
 # (prefill shapes with fewer than 256 output tiles of 128 tokens x 256 channels
 # run 64-token tiles, and with fewer than 256 of those, 64 x 128 tiles: the
 # first four and (70, 128, 208), which has too few k-tiles to split k inside
 # the workgroup; (1100, 512, 4112) runs 64 x 256 tiles; (2100, 512, 4112)
 # runs 128-token tiles with k split in halves inside the workgroup,
 # (4200, 256, 4208) without)
-@pytest.mark.parametrize("M,d,N", [(17, 256, 64), (130, 512, 272), (300, 384, 128), (256, 1024, 512),
+@pytest.mark.parametrize("M,d,N", [(65, 256, 64), (130, 512, 272), (300, 384, 128), (256, 1024, 512),
                                    (70, 128, 208), (1100, 512, 4112), (3, 512, 48), (9, 1152, 1040),
                                    (2100, 512, 4112), (4200, 256, 4208)])
 def test_linear_shapes_with_bias(paro, M, d, N):
@@ -411,16 +426,17 @@ def test_linear_workspace_errors(paro):
         paro.paro_w4_linear(r, dev(x), qw, s, z, workspace=small)
     assert e.value.status == -7
     assert paro.paro_w4_linear_workspace_size(r, 8, 32, 256) >= 16384
-    assert paro.paro_w4_linear_workspace_size(r, 17, 32, 256) >= 16384 + 17 * 256 * 2
+    assert paro.paro_w4_linear_workspace_size(r, 65, 32, 256) >= 16384 + 65 * 256 * 2
 
 
 # ----------------------------------------------------------------------------
-# small batches (M <= 16): one kernel, transform fused in, split over k
+# small batches (M <= 64): one kernel, transform fused in, split over k
 # ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,d,N", [(1, 640, 400), (16, 640, 400), (5, 384, 48), (2, 4096, 4096),
                                    (16, 14336, 256), (11, 1152, 1040), (1, 128, 16),
-                                   (3, 4096, 14336), (16, 14336, 4096)])
+                                   (3, 4096, 14336), (16, 14336, 4096), (24, 4096, 1024), (40, 1152, 1040),
+                                   (64, 14336, 4096)])
 def test_decode_fused_equals_rotate_then_plain(paro, M, d, N):
     """The fused transform yields the X' bits paro_rotate yields and the k-split
     sum order does not depend on where X' came from: equal outputs bit for bit."""

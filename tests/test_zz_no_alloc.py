@@ -46,7 +46,7 @@ def run_pair(paro, r, x, qw, s, z, bias, G):
     N = qw.shape[0]
     # the workspace entry point with the workspace the scratch stands for: the
     # full size when it fits (the k-split's partial tiles included), else the
-    # minimum (for M > 16: X' only, or nothing for a plain layer)
+    # minimum (for M > 64: X' only, or nothing for a plain layer)
     full = paro.paro_w4_linear_workspace_size(r, M, N, d)
     if full <= SCRATCH_BYTES:
         nbytes = full
@@ -62,6 +62,7 @@ def run_pair(paro, r, x, qw, s, z, bias, G):
 
 @pytest.mark.parametrize("rotated,G,d,N,Ms", [
     (True, 128, 4096, 4096, (16, 4)),      # small batch, transform fused, k split over 8 slices
+    (True, 128, 4096, 4096, (48, 20)),     # small batch in blocks of 16 tokens (four, then two)
     (False, 128, 14336, 4096, (8, 1)),     # plain W4, 28 k-slices
     (True, 256, 1024, 512, (16, 5)),       # plan the small-batch kernel does not fuse: X' in the scratch
     (True, 128, 4096, 1024, (2048, 300)),  # matrix-core path, X' in the scratch
