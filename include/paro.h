@@ -183,7 +183,7 @@ int paro_quantize_weights(const paro_rotation* r, const uint16_t* w, int64_t N, 
 
 /* Bytes of device workspace with which paro_w4_linear runs its fastest
  * kernels for this plan (NULL: plain W4) and these sizes; 0 means the call
- * uses no workspace. For M > 16 on layers with fewer than 256 output tiles of
+ * uses no workspace. For M > 64 on layers with fewer than 256 output tiles of
  * 256 x 256 whose k-tiles can be shared out among the workgroups (stream-K)
  * this includes 128 MiB of fp32 partial tiles (two of 256 KB per workgroup);
  * paro_w4_linear also runs, with the smaller-tile kernel, on the minimum:
@@ -209,7 +209,7 @@ size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t 
  *   d <= 2^22, M < 2^30, else PARO_ERR_UNSUPPORTED.
  *   workspace, workspace_bytes: device memory of
  *            paro_w4_linear_workspace_size(r, M, N, d) bytes, or of at least
- *            the minimum given there (M > 16: then without stream-K),
+ *            the minimum given there (M > 64: then without stream-K),
  *            256-byte aligned (may be NULL when the size in use is 0;
  *            smaller than the minimum: PARO_ERR_WORKSPACE). Its first 16 KiB hold
  *            arrival counters that must be zero before the first call that
@@ -218,10 +218,11 @@ size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t 
  *            run at the same time (different streams) need different
  *            workspaces.
  *
- * Execution: M <= 16 runs one kernel that streams the packed weights and, for
- * plans of group 64 or 128 that execute at most 8 stages, applies the
- * transform to the activations inside the same kernel; other plans rotate
- * into the workspace first. M > 16 rotates into the workspace and then runs
+ * Execution: M <= 64 runs one kernel that streams the packed weights (token
+ * columns in blocks of 16) and, for plans of group 64 or 128 that execute at
+ * most 8 stages, applies the transform to the activations inside the same
+ * kernel; other plans rotate into the workspace first. M > 64 rotates into
+ * the workspace and then runs
  * a matrix-core kernel: 256 x 256 tiles from 256 such tiles, one per
  * workgroup; with fewer, when every XCD holds n-blocks and k is long enough,
  * the same kernel with each XCD's k-tiles shared out in equal ranges among 16
@@ -233,7 +234,7 @@ size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t 
  *
  * Arithmetic: X' exactly as paro_rotate computes it (fp16); fp32 accumulation
  * of exact fp16 products against the fp16 rounding of each dequantized weight
- * (q - z) * s, in an order that depends on the sizes (and for M > 16 on
+ * (q - z) * s, in an order that depends on the sizes (and for M > 64 on
  * whether the workspace holds the stream-K partial tiles) but not on timing;
  * fp16 output.
  * Errors: PARO_ERR_NULL, PARO_ERR_SHAPE, PARO_ERR_ALIGN, PARO_ERR_UNSUPPORTED,
@@ -258,7 +259,7 @@ int paro_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qwe
  *   Limit:   the minimum workspace of paro_w4_linear (see
  *            paro_w4_linear_workspace_size) must not exceed that size (for
  *            example M x d <= 32 Mi elements for a rotated layer with
- *            M > 16), else PARO_ERR_WORKSPACE and nothing is enqueued; the
+ *            M > 64), else PARO_ERR_WORKSPACE and nothing is enqueued; the
  *            stream-K partial tiles are used when they fit as well.
  *   Sharing: every call on one device uses that device's single array, so
  *            calls that may run at the same time on one device (several
@@ -362,7 +363,7 @@ size_t paro_layer_loss_workspace_size(const paro_rotation* r, int64_t M, int64_t
  *   workspace: at least paro_layer_loss_workspace_size(r, M, N, d, dtheta ||
  *            dalpha) bytes, 256-byte aligned, zero-filled once after
  *            allocation (its first 16 KiB hold paro_w4_linear's arrival
- *            counters for M <= 16, which every call leaves zero, whatever M
+ *            counters for M <= 64, which every call leaves zero, whatever M
  *            and N the workspace is reused with). Calls that may run at the
  *            same time need different workspaces.
  * Every step runs in this library's kernels (the dense products on the

@@ -290,15 +290,15 @@ int check_w4_linear(const char* fn, const paro_rotation* r, const uint16_t* x,
     return PARO_ERR_ALIGN;
   }
   if (M <= kDecodeMaxM && (uint64_t)((d / 128 + 3) / 4) * (uint64_t)M * (uint64_t)N * 4 >= (1ull << 31)) {
-    set_error(f + ": ceil(d / 512) * M * N * 4 must be below 2^31 for M <= 16");
+    set_error(f + ": ceil(d / 512) * M * N * 4 must be below 2^31 for M <= 64");
     return PARO_ERR_UNSUPPORTED;
   }
   return PARO_OK;
 }
 
-// The smallest workspace paro_w4_linear runs with: as reported for M <= 16,
-// the transformed activations (and the counters before them) for M > 16; the
-// partial tiles of the split large-batch kernel only speed the call up.
+// The smallest workspace paro_w4_linear runs with: as reported for M <= 64,
+// the transformed activations (and the counters before them) for M > 64; the
+// stream-K partial tiles of the large-batch kernel only speed the call up.
 size_t w4_linear_min_workspace(const paro_rotation* r, int64_t M, int64_t N, int64_t d) {
   if (M <= kDecodeMaxM || M <= 0) return paro_w4_linear_workspace_size(r, M, N, d);
   if (!r) return 0;

@@ -1,4 +1,4 @@
-// gfx950 kernel for the W4G128 linear layer with few tokens (decode, M <= 16),
+// gfx950 kernel for the W4G128 linear layer with few tokens (decode, M <= 64),
 // with the online activation transform fused in:
 //   Y[m][n] = sum_k X'[m][k] (q[n][k] - z[n][k/G]) s[n][k/G] + b[n],
 //   X' = X T^-1
@@ -37,7 +37,7 @@
 // counter go through memory-side (system scope) stores, loads and atomics
 // instead. The kernel launch itself only reads the recorded result.
 // The rotation is recomputed by each of the N / 128 n-blocks that read a
-// segment: with M <= 16 this is ALU work hidden under the weight loads.
+// segment: with few tokens this is ALU work hidden under the weight loads.
 //
 // Dequantization (w4_common.h): two codes at a time are masked into the
 // mantissas of a pair of fp16 1024.0 values, (v - (1024 + z)) = q - z is

@@ -155,7 +155,7 @@ hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint1
 // Whether paro_device_init found workgroup b running on XCD b % 8.
 bool xcd_dispatch_is_round_robin();
 
-// Small-batch linear (M <= 16). With r != NULL the activation transform runs
+// Small-batch linear (M <= kDecodeMaxM). With r != NULL the activation transform runs
 // inside the kernel (requires decode_fuses_rotation(r)); ws is the workspace:
 // kDecodeCounterBytes of arrival counters (zero between calls), then the fp32
 // partial sums [ceil(d / 512)][M][N].

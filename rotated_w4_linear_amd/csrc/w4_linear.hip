@@ -882,7 +882,7 @@ GemmPlan plan_w4_gemm(int64_t M, int64_t N, int64_t d) {
   GemmPlan p;
   const int64_t nblk = (N + GB_N - 1) / GB_N, mblkw = (M + GW_M - 1) / GW_M;
   const int64_t tiles = nblk * mblkw, kt = d / GB_K;
-  if (M <= 16 || d > (int64_t(1) << 21) || kt % 2 || d < 4 * GB_K) return p;
+  if (M <= kDecodeMaxM || d > (int64_t(1) << 21) || kt % 2 || d < 4 * GB_K) return p;
   // one tile per workgroup from kWideMinTiles tiles (stream-K measured slower
   // there: 2048 x 4096 -> 14336, 448 tiles, 252 against 223 us, the
   // workgroups of an XCD no longer reading the same k-tiles at the same
