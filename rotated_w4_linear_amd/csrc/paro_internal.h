@@ -146,6 +146,7 @@ struct GemmPlan {
   bool wide = false;
   bool sk = false;
   int sk_slots = 0;  // stream-K workgroups per XCD
+  int nsplit = 1;    // smaller-tile kernel: workgroups per tile along k
   size_t partial_bytes = 0;
 };
 GemmPlan plan_w4_gemm(int64_t M, int64_t N, int64_t d);

@@ -77,6 +77,9 @@ constexpr int64_t kHalfTileBelow = 256;
 // 64-token tiles below which the tiles are also narrowed to 128 channels, so
 // that every CU gets a workgroup
 constexpr int64_t kNarrowTileBelow = 256;
+// k-tiles per group of wavefronts below which the 64 x 128-tile kernel does
+// not split k further across workgroups
+constexpr int64_t kMinNarrowSplitKT = 4;
 // 256 x 256 tiles (at 256 tokens) from which the wide kernel is used: measured
 // on MI355X, 4096 x 4096 -> 4096 (256 tiles): 128 against 135 us; 2048 x
 // 14336 -> 4096 (128 tiles) runs 372 against 288 us
@@ -97,13 +100,17 @@ constexpr int kWideWN = 2;
 
 // MT: 32-token m tiles per wavefront (4: 128-token workgroup tiles; 2: 64,
 // for layers with few output tiles). NT: 32-channel n tiles per wavefront (2:
-// 256-channel workgroup tiles; 1: 128, for layers with fewer still).
-template <int KS, int MT, int NT>
+// 256-channel workgroup tiles; 1: 128, for layers with fewer still). SPLIT: k
+// also split across ksplit workgroups per tile (consecutive slots of one
+// XCD), which meet through fp32 partial tiles; the last to arrive adds them
+// in split order.
+template <int KS, int MT, int NT, bool SPLIT>
 __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(2)))
 void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ qw,
                     const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zr,
                     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N,
-                    int d, int gsh, int mblk, int nblk) {
+                    int d, int gsh, int mblk, int nblk, int ksplit, float* __restrict__ part,
+                    uint32_t* __restrict__ cnt, int sys) {
   constexpr int GB_M = 32 * MT;           // tokens per workgroup tile
   constexpr int GN = 128 * NT;            // output channels per workgroup tile
   constexpr int GB_XSTAGE = GB_M * GB_K;  // halfs per X' stage (16 KB at MT = 4)
@@ -119,7 +126,9 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
   // n-blocks x, x + 8, ... and walks them in super-blocks of 8 m-blocks x all
   // its n-blocks, so the workgroups resident on one XCD share both their X'
   // and their weight k-tiles through its L2.
-  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  const int xcd = blockIdx.x & 7, idx0 = blockIdx.x >> 3;
+  if (!SPLIT) ksplit = 1;
+  const int ks = idx0 % ksplit, idx = idx0 / ksplit;
   const int nbx = (nblk - xcd + 7) >> 3;
   if (nbx <= 0) return;
   const int mg = idx / (8 * nbx), rem = idx - mg * 8 * nbx;
@@ -130,8 +139,8 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
   const int nw0 = nb * GN;         // workgroup's first output channel
   const int n0 = nw0 + 32 * NT * w;  // this wavefront's first output channel
   const int groups = d >> (6 + gsh);  // quantization groups of 64 << gsh channels per row
-  const int KT = (d / GB_K) / KS;  // k-tiles per group of wavefronts
-  const int kt0 = kg * KT;
+  const int KT = (d / GB_K) / (KS * ksplit);  // k-tiles per group of wavefronts
+  const int kt0 = (ks * KS + kg) * KT;
   const int l32 = lane & 31, g = lane >> 5;
 
   // Buffer resources based at this tile's first row (byte offsets < 2^31,
@@ -277,7 +286,66 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
         }
       }
     }
-    if (kg != 0) return;
+    if constexpr (!SPLIT) {
+      if (kg != 0) return;
+    }
+  }
+
+  if constexpr (SPLIT) {
+    // Split k across workgroups: group 0 of every workgroup of the tile stores
+    // its fp32 partial tile ([w][f][lane] 16-byte chunks, GB_M x GN floats)
+    // and the workgroup counts itself in; the last to arrive adds the partial
+    // tiles in split order (so the sum does not depend on the order of
+    // arrival), resets the counter and runs the epilogue. The workgroups of a
+    // tile share an XCD: plain stores, an L2 atomic and loads that skip the
+    // per-CU cache suffice; where the dispatch rule is not established (sys)
+    // they go through memory. Every wavefront takes part in the barriers.
+    __shared__ uint32_t s_last;
+    const int tile = mb * nblk + nb;
+    constexpr int NF = NT * MT * 4;  // 16-byte chunks per lane
+    auto rsrc = [&](int k2) {
+      return __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(part + ((size_t)tile * ksplit + k2) * (size_t)(GB_M * GN)), (short)0, GB_M * GN * 4, kRsrcWord3);
+    };
+    if (kg == 0) {
+      const __amdgpu_buffer_rsrc_t rmine = rsrc(ks);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int j = f / (MT * 4), mm = (f / 4) % MT, q = f % 4;
+        const u4 v = __builtin_bit_cast(u4, f4{acc[j][mm][4 * q], acc[j][mm][4 * q + 1], acc[j][mm][4 * q + 2],
+                                               acc[j][mm][4 * q + 3]});
+        const int off = ((w * NF + f) * 64 + lane) * 16;
+        if (sys) __builtin_amdgcn_raw_buffer_store_b128(v, rmine, off, 0, kAuxSysW);
+        else __builtin_amdgcn_raw_buffer_store_b128(v, rmine, off, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wavefront's stores have reached L2 / memory
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t old;
+      if (sys) old = __hip_atomic_fetch_add(&cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      else old = __hip_atomic_fetch_add(&cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = old == (uint32_t)(ksplit - 1);
+    }
+    __syncthreads();
+    if (!s_last || kg != 0) return;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int j = f / (MT * 4), mm = (f / 4) % MT, q = f % 4;
+      const int off = ((w * NF + f) * 64 + lane) * 16;
+      f4 t = {0.f, 0.f, 0.f, 0.f};
+      for (int k2 = 0; k2 < ksplit; ++k2) {
+        const f4 v = __builtin_bit_cast(f4, sys ? __builtin_amdgcn_raw_buffer_load_b128(rsrc(k2), off, 0, kAuxSysW)
+                                                : __builtin_amdgcn_raw_buffer_load_b128(rsrc(k2), off, 0, kAuxL2R));
+        t = k2 == 0 ? v : t + v;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[j][mm][4 * q + e] = t[e];
+    }
+    if (tid == 0) {
+      if (sys) __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      else __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 
   // epilogue: acc[j][mm][e] = C[n = n0 + 32 j + 8 (e/4) + 4 g + e%4][m = m0 + 32 mm + l32].
@@ -872,8 +940,42 @@ template <int KS, int MT, int NT>
 void launch_gemm(unsigned blocks, hipStream_t stream, const uint16_t* x, const uint8_t* qweight,
                  const uint16_t* scales, const uint8_t* zeros, const uint16_t* bias, uint16_t* y,
                  int64_t M, int64_t N, int64_t d, int gsh, int mblk, int nblk) {
-  hipLaunchKernelGGL((w4_gemm_kernel<KS, MT, NT>), dim3(blocks), dim3(256 * KS), 0, stream, x, qweight,
-                     scales, zeros, bias, y, (int)M, (int)N, (int)d, gsh, mblk, nblk);
+  hipLaunchKernelGGL((w4_gemm_kernel<KS, MT, NT, false>), dim3(blocks), dim3(256 * KS), 0, stream, x, qweight,
+                     scales, zeros, bias, y, (int)M, (int)N, (int)d, gsh, mblk, nblk, 1, nullptr, nullptr, 0);
+}
+
+// Smaller-tile kernel geometry, as launch_w4_gemm chooses it: 64-token tiles
+// when 128-token ones would leave most SIMDs without work, 128-channel ones
+// when even those leave CUs without a workgroup; k split two or four ways
+// inside the workgroup; and (nsplit > 1) across workgroups when the tiles do
+// not fill the CUs.
+struct SmallGemm {
+  int nblk256, mblk, nblk, ksin, nsplit;
+  bool half, narrow;
+  int64_t tiles;
+};
+SmallGemm small_gemm(int64_t M, int64_t N, int64_t d) {
+  SmallGemm g;
+  g.nblk256 = (int)((N + GB_N - 1) / GB_N);
+  g.half = (int64_t)g.nblk256 * ((M + 127) / 128) < kHalfTileBelow;
+  const int gbm = g.half ? 64 : 128;
+  g.mblk = (int)((M + gbm - 1) / gbm);
+  g.narrow = g.half && (int64_t)g.nblk256 * g.mblk < kNarrowTileBelow;
+  g.nblk = g.narrow ? (int)((N + GB_N / 2 - 1) / (GB_N / 2)) : g.nblk256;
+  g.tiles = (int64_t)g.nblk * g.mblk;
+  const int64_t kt = d / GB_K;
+  const bool ks2 = g.tiles < 512 && kt % 2 == 0 && kt >= 4;
+  const bool ks4 = g.narrow && kt % 4 == 0 && kt >= 16;
+  g.ksin = ks4 ? 4 : ks2 ? 2 : 1;
+  // with 64 x 128 tiles (and k split four ways inside) that leave CUs idle:
+  // up to 4 workgroups per tile, each group of wavefronts keeping at least
+  // kMinNarrowSplitKT k-tiles
+  g.nsplit = 1;
+  if (g.narrow && g.ksin == 4)
+    while (g.nsplit < 4 && g.tiles * 2 * g.nsplit <= 256 && kt % (g.ksin * 2 * g.nsplit) == 0 &&
+           kt / (g.ksin * 2 * g.nsplit) >= kMinNarrowSplitKT && g.tiles <= (int64_t)(kDecodeCounterBytes / 4))
+      g.nsplit *= 2;
+  return g;
 }
 
 }  // namespace
@@ -892,7 +994,6 @@ GemmPlan plan_w4_gemm(int64_t M, int64_t N, int64_t d) {
     return p;
   }
   const int64_t nbmin = nblk / 8, nbmax = (nblk + 7) / 8;
-  if (nbmin < 1) return p;
   // Workgroups per XCD: the fewest k-tiles per range on the busiest XCD,
   // counting kSkMisaligned more for ranges that do not cut the tiles into
   // equal pieces (nor hold whole tiles): their pieces start at different k,
@@ -904,7 +1005,7 @@ GemmPlan plan_w4_gemm(int64_t M, int64_t N, int64_t d) {
   // CUs) are not taken, nor misaligned ones on fewer than 3/4 of the CUs.
   int best = 0;
   int64_t best_cost = 0;
-  for (int sl = kSkSlots; sl >= kSkSlots / 2; sl -= 4) {
+  for (int sl = kSkSlots; nbmin >= 1 && sl >= kSkSlots / 2; sl -= 4) {
     const int64_t units = nbmax * mblkw * kt;
     if (nbmin * mblkw * kt < 2 * sl) continue;
     const int64_t U = (units + sl - 1) / sl;
@@ -921,6 +1022,12 @@ GemmPlan plan_w4_gemm(int64_t M, int64_t N, int64_t d) {
     p.wide = p.sk = true;
     p.sk_slots = best;
     p.partial_bytes = (size_t)8 * kSkSlots * 2 * GW_M * GB_N * 4;
+    return p;
+  }
+  const SmallGemm g = small_gemm(M, N, d);
+  if (g.nsplit > 1) {
+    p.nsplit = g.nsplit;
+    p.partial_bytes = (size_t)g.tiles * g.nsplit * 64 * 128 * 4;
   }
   return p;
 }
@@ -958,23 +1065,13 @@ hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint1
                           int64_t N, int64_t d, int group, uint32_t* cnt, float* part, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const int gsh = group == 64 ? 0 : group == 128 ? 1 : 2;
-  const int nblk256 = (int)((N + GB_N - 1) / GB_N);
-  // 64-token tiles when 128-token ones would leave most SIMDs without work,
-  // and 128-channel ones when even those leave CUs without a workgroup
-  const bool half = (int64_t)nblk256 * ((M + 127) / 128) < kHalfTileBelow;
-  const int gbm = half ? 64 : 128;
-  const int mblk = (int)((M + gbm - 1) / gbm);
-  const bool narrow = half && (int64_t)nblk256 * mblk < kNarrowTileBelow;
-  const int nblk = narrow ? (int)((N + GB_N / 2 - 1) / (GB_N / 2)) : nblk256;
-  const int64_t tiles = (int64_t)nblk * mblk;
+  const SmallGemm sg = small_gemm(M, N, d);
+  const int nblk256 = sg.nblk256, mblk = sg.mblk, nblk = sg.nblk;
+  const bool half = sg.half, narrow = sg.narrow;
   // 8 XCDs, each owning every 8th n-block, walked in super-blocks of 8 m-blocks
   const int64_t nbp = (nblk + 7) / 8;
   const int64_t blocks = 8 * nbp * (((int64_t)mblk + 7) / 8) * 8;
-  // too few tiles to give every SIMD two wavefronts: split k inside the workgroup
-  const bool ks2 = tiles < 512 && (d / GB_K) % 2 == 0 && d / GB_K >= 4;
-  // 64 x 128 tiles: four k groups (sixteen wavefronts), so that each CU has
-  // four k-tiles' loads in flight
-  const bool ks4 = narrow && (d / GB_K) % 4 == 0 && d / GB_K >= 16;
+  const bool ks2 = sg.ksin == 2, ks4 = sg.ksin == 4;
   const unsigned g = (unsigned)blocks;
   // layers with many 256 x 256 tiles take the one-wavefront-per-SIMD kernel,
   // one tile per workgroup when the tiles fill whole rounds of one workgroup
@@ -1009,7 +1106,12 @@ hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint1
     }
     return hipGetLastError();
   }
-  if (ks4) launch_gemm<4, 2, 1>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
+  if (ks4 && sg.nsplit > 1 && cnt && part) {
+    const int sys = !xcd_dispatch_is_round_robin();
+    hipLaunchKernelGGL((w4_gemm_kernel<4, 2, 1, true>), dim3(g * (unsigned)sg.nsplit), dim3(1024), 0, stream, x,
+                       qweight, scales, zeros, bias, y, (int)M, (int)N, (int)d, gsh, mblk, nblk, sg.nsplit, part,
+                       cnt, sys);
+  } else if (ks4) launch_gemm<4, 2, 1>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
   else if (narrow && ks2) launch_gemm<2, 2, 1>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
   else if (narrow) launch_gemm<1, 2, 1>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
   else if (half && ks2) launch_gemm<2, 2, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);

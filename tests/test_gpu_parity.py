@@ -390,6 +390,35 @@ def test_linear_stream_k(paro, M, d, N, G, sk):
     metrics.assert_linear_close(host(y0)[rows], refp)
 
 
+# 65 to a few hundred tokens on the 64 x 128-tile kernel: with the full
+# workspace k is also split across 2 or 4 workgroups per tile (fp32 partial
+# tiles, the last to arrive adds them in split order); with the minimum
+# workspace it is not. Both against the oracle, ragged M and N included.
+@pytest.mark.parametrize("M,d,N,G", [(65, 4096, 4096, 128), (128, 4096, 4112, 128), (200, 2048, 1040, 128),
+                                     (256, 4096, 4096, 64), (130, 14336, 4096, 128)])
+def test_linear_narrow_split(paro, M, d, N, G):
+    log(f"linear narrow split M={M} d={d} N={N} group={G}")
+    x, layer, b = synthetic.linear_case(seed=M + d + N + 11, M=M, d=d, N=N, group=G)
+    r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, G)
+    qw, s, z = paro.paro_quantize_weights(r, dev(layer.w), G)
+    rows = np.sort(synthetic.rng_for(3530, M).choice(M, min(M, 40), replace=False))
+    rows[-1] = M - 1
+    ref = oracle.rotated_w4_linear(x[rows], host(qw), host(s), host(z), G, layer.pairs, layer.theta,
+                                   layer.alpha, b)
+    full = paro.paro_w4_linear_workspace_size(r, M, N, d)
+    minimum = 16384 + (M * d * 2 + 255) // 256 * 256
+    assert full > minimum
+    for nbytes in (full, minimum, full):
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        y = host(paro.paro_w4_linear(r, dev(x), qw, s, z, dev(b), group=G, workspace=ws))
+        metrics.assert_linear_close(y[rows], ref)
+        assert int(ws[:16384].count_nonzero()) == 0
+    refp = oracle.rotated_w4_linear(x[rows], host(qw), host(s), host(z), G, bias=b)
+    yp = host(paro.paro_w4_linear(None, dev(x), qw, s, z, dev(b), group=G))
+    metrics.assert_linear_close(yp[rows], refp)
+    r.close()
+
+
 def test_linear_gemv_vs_gemm_same_rows(paro):
     """Rows 0..15 through the GEMV (M = 16) and the GEMM (M = 40) agree."""
     x, layer, b = synthetic.linear_case(seed=5, M=40, d=1024, N=256)

@@ -135,7 +135,10 @@ def test_hot_calls_validate_before_any_launch(paro):
     assert lib.paro_quantize_weights(None, None, 8, 256, 128, dummy, dummy, dummy, None) == -1
     # workspace: none for plain large-batch calls; counters + fp32 partial sums
     # [ceil(d / 512)][M][N] for small batches; + X' for rotated large batches
-    assert lib.paro_w4_linear_workspace_size(None, 65, 64, 4096) == 0
+    assert lib.paro_w4_linear_workspace_size(None, 65, 64, 256) == 0
+    # (65 tokens, 64 -> 4096 channels: two 64 x 128 tiles, k split across 4
+    # workgroups each: fp32 partial tiles of 32 KB)
+    assert lib.paro_w4_linear_workspace_size(None, 65, 64, 4096) == 16384 + 2 * 4 * 32768
     assert lib.paro_w4_linear_workspace_size(None, 64, 64, 4096) == 16384 + 8 * 64 * 64 * 4
     assert lib.paro_w4_linear_workspace_size(None, 16, 64, 4096) == 16384 + 8 * 16 * 64 * 4
     assert lib.paro_w4_linear_workspace_size(None, 1, 64, 512) == 16384
