@@ -185,9 +185,11 @@ int paro_quantize_weights(const paro_rotation* r, const uint16_t* w, int64_t N, 
  * kernels for this plan (NULL: plain W4) and these sizes; 0 means the call
  * uses no workspace. For M > 64 on layers with fewer than 256 output tiles of
  * 256 x 256 whose k-tiles can be shared out among the workgroups (stream-K)
- * this includes 128 MiB of fp32 partial tiles (two of 256 KB per workgroup);
- * paro_w4_linear also runs, with the smaller-tile kernel, on the minimum:
- * 16 KiB + M d 2 bytes (rounded up to 256) with a plan, none without. */
+ * this includes 128 MiB of fp32 partial tiles (two of 256 KB per workgroup),
+ * and on layers whose 64 x 128 tiles leave CUs idle 32 KB per tile and k
+ * split; paro_w4_linear also runs, with the smaller-tile kernel unsplit, on
+ * the minimum: 16 KiB + M d 2 bytes (rounded up to 256) with a plan, none
+ * without. */
 size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t N, int64_t d);
 
 /*
@@ -230,7 +232,9 @@ size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t 
  * tiles in the workspace (the last piece to arrive adds them in k order),
  * when the workspace holds them; else a kernel with 128 x 256 tiles, or
  * 64 x 256 or 64 x 128 (k split two or four ways inside the workgroup) for
- * layers with few tiles.
+ * layers with few tiles, the latter with k also split across 2 or 4
+ * workgroups per tile when the tiles leave CUs idle and the workspace holds
+ * their partial tiles.
  *
  * Arithmetic: X' exactly as paro_rotate computes it (fp16); fp32 accumulation
  * of exact fp16 products against the fp16 rounding of each dequantized weight
