@@ -234,7 +234,7 @@ size_t paro_w4_linear_workspace_size(const paro_rotation* r, int64_t M, int64_t 
     size_t bytes = kDecodeCounterBytes;
     const size_t ksl = (size_t)((d / 128 + 3) / 4);
     if (ksl > 1) bytes += round256(ksl * (size_t)M * (size_t)N * 4);
-    if (r && !decode_fuses_rotation(r)) bytes += round256((size_t)M * (size_t)d * 2);
+    if (r && !decode_fuses_rotation(r, M, N, d)) bytes += round256((size_t)M * (size_t)d * 2);
     return bytes;
   }
   const size_t split = plan_w4_gemm(M, N, d).partial_bytes;
@@ -315,7 +315,7 @@ int run_w4_linear(const paro_rotation* r, const uint16_t* x, const uint8_t* qwei
   if (M <= kDecodeMaxM) {
     const paro_rotation* fused = r;
     const uint16_t* xin = x;
-    if (r && !decode_fuses_rotation(r)) {
+    if (r && !decode_fuses_rotation(r, M, N, d)) {
       // stand-alone transform into the workspace tail, then the plain kernel
       uint16_t* xr = (uint16_t*)(ws + ws_bytes - (((size_t)M * (size_t)d * 2 + 255) & ~(size_t)255));
       e = launch_rotate(r, x, xr, M, stream);

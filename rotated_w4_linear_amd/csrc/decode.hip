@@ -465,6 +465,17 @@ bool decode_fuses_rotation(const paro_rotation* r) {
   return r == nullptr || (r->lay.ppl == 1 && r->lay.stages <= 8);
 }
 
+// Beyond 16 tokens the N / 128 workgroups that each transform the same
+// k-slice make the fused transform the larger cost, and one stand-alone
+// transform (4-5 us) before the plain kernel is cheaper: from 33 tokens on
+// every layer, from 17 on layers of at least 2^25 weights. Measured,
+// graph-replayed, fused against transform-then-plain: 64 tokens, 4096 ->
+// 14336 51.4 against 38.8 us, 14336 -> 4096 72.4 against 57.3, 4096 -> 4096
+// 21.6 against about 18.4; 32 tokens, 4096 -> 4096 13.7 against about 15.
+bool decode_fuses_rotation(const paro_rotation* r, int64_t M, int64_t N, int64_t d) {
+  return decode_fuses_rotation(r) && (M <= 16 || (M <= 32 && N * d < (int64_t(1) << 25)));
+}
+
 hipError_t launch_w4_decode(const uint16_t* x, const uint8_t* qweight, const uint16_t* scales,
                             const uint8_t* zeros, const uint16_t* bias, uint16_t* y, int64_t M,
                             int64_t N, int64_t d, int group, const paro_rotation* r, void* ws,

@@ -163,6 +163,9 @@ bool xcd_dispatch_is_round_robin();
 constexpr size_t kDecodeCounterBytes = 16384;
 constexpr int64_t kDecodeMaxM = 64;
 bool decode_fuses_rotation(const paro_rotation* r);
+// whether the small-batch call with these sizes fuses it (else the transform
+// runs first, into the workspace)
+bool decode_fuses_rotation(const paro_rotation* r, int64_t M, int64_t N, int64_t d);
 // Devices the library keeps per-device state for (device ordinals below this).
 constexpr int kMaxDevices = 64;
 // Runs the XCD dispatch probe on device dev (current) once and records the

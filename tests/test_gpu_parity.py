@@ -298,10 +298,11 @@ def test_linear_decode(paro, M):
 # token columns (the last block ragged): 4096 -> 4096 (128-channel
 # workgroups), 4096 -> 1024 (64-channel), 1152 -> 1040 (scales and zeros
 # loaded one group at a time), groups of 64 and 256 (the latter transformed
-# into the workspace first).
+# into the workspace first), and 4096 -> 8192 (2^25 weights: transformed
+# into the workspace first from 17 tokens; the others from 33).
 @pytest.mark.parametrize("M", [17, 32, 33, 48, 64])
 @pytest.mark.parametrize("d,N,G", [(4096, 4096, 128), (4096, 1024, 128), (1152, 1040, 128), (1024, 272, 64),
-                                   (1024, 272, 256)])
+                                   (1024, 272, 256), (4096, 8192, 128)])
 def test_linear_small_batch_blocks(paro, M, d, N, G):
     log(f"linear small batch M={M} d={d} N={N} group={G}")
     x, layer, b = synthetic.linear_case(seed=700 + M + d + N + G, M=M, d=d, N=N, group=G)
