@@ -893,17 +893,20 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
   };
 
   if constexpr (!SK) {
-    // one tile per workgroup: XCD x walks its n-blocks in super-blocks of 8
-    // m-blocks
+    // one tile per workgroup: XCD x walks all of its n-blocks for each
+    // m-block in turn, so that the tiles resident on it at once span few
+    // m-blocks. An X' block (256 rows) is four times the bytes of a weight
+    // block, so sharing X' blocks saves more L2 misses than sharing weight
+    // blocks (MLP 8192 x 4096 -> 14336: 0.792 -> 0.783 ms against super-blocks
+    // of 8 m-blocks, fewer misses at the same work)
     const int idx = blockIdx.x >> 3;
-    const int mg = idx / (8 * nbx), rem = idx - mg * 8 * nbx;
-    const int nb = xcd + 8 * (rem / 8);
-    const int mb = mg * 8 + (rem & 7);
+    const int mb = idx / nbx;
+    const int nb = xcd + 8 * (idx - mb * nbx);
     if (mb >= mblk) return;
     segment(mb, nb, 0, L, 0, true);
   } else {
-    // the XCD's tile t in the same order (the last super-block may hold
-    // fewer than 8 m-blocks)
+    // the XCD's tile t, its n-blocks walked in super-blocks of 8 m-blocks
+    // (the last super-block may hold fewer)
     int64_t u = rstart(jw);
     const int64_t ue = rstart(jw + 1);
     const int tfirst = (int)(u / L);
@@ -1089,7 +1092,7 @@ hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint1
     if (plan.sk) sk_shape(nblk256, mblkw, L, gsh, plan.sk_slots, &pgs, &one_tile);
     const bool panel = pgs <= kPanelGroups && groups % 8 == 0 && ((uintptr_t)scales & 15) == 0 &&
                        ((uintptr_t)zeros & 7) == 0;
-    const int64_t bw = plan.sk ? 8 * plan.sk_slots : 8 * ((nblk256 + 7) / 8) * (((int64_t)mblkw + 7) / 8) * 8;
+    const int64_t bw = plan.sk ? 8 * plan.sk_slots : 8 * ((nblk256 + 7) / 8) * (int64_t)mblkw;
     auto go = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, dim3((unsigned)bw), dim3(256), 0, stream, x, qweight, scales, zeros, bias, y,
                          (int)M, (int)N, (int)d, gsh, mblkw, nblk256, plan.sk_slots, part, cnt, sys);
