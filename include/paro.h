@@ -478,7 +478,12 @@ int paro_mfma_loop(const void* src, int64_t n, float* out, int32_t blocks, int32
  *   layout[2] = 32-bit words per virtual lane per segment (the schedule's
  *               fields padded to a multiple of 4; the image of a segment is
  *               [layout[2] / 4][virtual lane][4], four consecutive fields of
- *               a lane side by side),
+ *               a lane side by side; after the segments' images comes the
+ *               store permutation, [segment][virtual lane][2] words: the LDS
+ *               byte offsets at which a lane writes its packed output pair
+ *               and from which it reads the natural pair of its own index,
+ *               which the activation transform uses for 256-channel
+ *               segments),
  *   layout[3] = 1 if the factored two-FMA stage form is used, 0 for the
  *               general 2x2 form,
  *   layout[4] = stages the activation schedule executes: K for a plan

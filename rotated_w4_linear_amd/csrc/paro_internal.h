@@ -41,6 +41,11 @@ namespace paro {
 //                     4 for the general 2x2 form)
 //   then              final scale of X, final scale of the fetched value,
 //                     store byte offset of the natural pair, store selector.
+// After all segments' images: the store permutation, [segs][NV][2] words.
+// Virtual lane v ends the last exchange holding the natural pair q(v) (the
+// pair at the store byte offset above); word 0 of lane v is the LDS byte
+// offset it writes its packed output word to, word 1 the offset virtual lane
+// v reads natural pair v from (slots planned like an exchange's).
 // ---------------------------------------------------------------------------
 struct RotPlanLayout {
   int seg_ch = 128;      // channels per segment
@@ -56,9 +61,15 @@ inline int rot_field_count(int K, int coef) { return 1 + 2 * (K + 1) + coef * K 
 // words per virtual lane in the image: the field count rounded up to four
 inline int rot_words(int K, int coef) { return (rot_field_count(K, coef) + 3) & ~3; }
 
+// first word of the store permutation, and the whole image, in words
+inline size_t rot_perm_base(int64_t segs, const RotPlanLayout& lay) { return (size_t)segs * lay.words * lay.nv; }
+inline size_t rot_table_words(int64_t segs, const RotPlanLayout& lay) {
+  return rot_perm_base(segs, lay) + (size_t)segs * lay.nv * 2;
+}
+
 struct RotPlanHost {
   RotPlanLayout lay;
-  std::vector<uint32_t> table;  // [segs][words / 4][nv][4]
+  std::vector<uint32_t> table;  // [segs][words / 4][nv][4], then [segs][nv][2]
   // canonical fp32 tables for the weight transform, per group, stage, pair:
   // local (i | j << 16), c bits, s bits
   std::vector<uint32_t> wt_pairs;  // [groups][K][G/2]

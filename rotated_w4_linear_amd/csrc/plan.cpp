@@ -539,7 +539,7 @@ int build_rotation_plan(int64_t d, int32_t group, int32_t K, const int32_t* pair
     lay.coef = fast ? 2 : 4;
     lay.words = rot_words(KA, lay.coef);
     lay.stages = KA;
-    std::vector<uint32_t> table((size_t)segs * lay.words * nv, 0);
+    std::vector<uint32_t> table(rot_table_words(segs, lay), 0);
     bool ok = true;
 
     for (int sg = 0; sg < segs && ok; ++sg) {
@@ -734,6 +734,20 @@ int build_rotation_plan(int64_t d, int32_t group, int32_t K, const int32_t* pair
         put(ff + 1, v, fbits((float)lam[kb]));
         put(ff + 2, v, (uint32_t)q * 4u);
         put(ff + 3, v, (kx & 1) == 0 ? kSelStoreX : kSelStoreB);
+      }
+      // store permutation: virtual lane v ends with the natural pair q(v) =
+      // kept / 2; one more exchange of the packed output words moves natural
+      // pair w to virtual lane w, so that each store instruction of the
+      // activation kernel writes one contiguous 256-byte piece of the row
+      // (the kernel takes it for 256-channel segments)
+      std::vector<int> src_perm(nv);
+      for (int v = 0; v < nv; ++v) src_perm[L.kept[KA][v] / 2] = v;
+      std::vector<int> pslot = plan_lds_slots(src_perm);
+      if (pslot.empty()) { ok = false; break; }
+      uint32_t* Pm = &table[rot_perm_base(segs, lay) + (size_t)sg * nv * 2];
+      for (int v = 0; v < nv; ++v) {
+        Pm[2 * v] = (uint32_t)pslot[v] * 16u;
+        Pm[2 * v + 1] = (uint32_t)pslot[src_perm[v]] * 16u;
       }
     }
     if (ok) {

@@ -164,12 +164,22 @@ def fma32(a, b, c):
 
 
 def field_major(img, lay, segs):
-    """The image as [segment][field][virtual lane]: the library stores four
-    consecutive fields of a lane side by side, [segment][words / 4][lane][4]."""
+    """The schedules of the image as [segment][field][virtual lane]: the library
+    stores four consecutive fields of a lane side by side,
+    [segment][words / 4][lane][4], and after them the store permutation."""
     nv = lay["seg_ch"] // 2
     W = lay["words"]
-    assert W % 4 == 0 and img.size == segs * W * nv
-    return img.reshape(segs, W // 4, nv, 4).transpose(0, 1, 3, 2).reshape(segs, W, nv)
+    assert W % 4 == 0 and img.size == segs * W * nv + segs * nv * 2
+    return img[:segs * W * nv].reshape(segs, W // 4, nv, 4).transpose(0, 1, 3, 2).reshape(segs, W, nv)
+
+
+def store_permutation(img, lay, segs):
+    """The store permutation after the schedules: [segment][virtual lane] LDS
+    write and read slots of the packed output words."""
+    nv = lay["seg_ch"] // 2
+    perm = img[segs * lay["words"] * nv:].reshape(segs, nv, 2)
+    assert np.all(perm % 16 == 0)
+    return perm[:, :, 0] // 16, perm[:, :, 1] // 16
 
 
 def emulate_rotate(img, lay, x, K, d):
@@ -182,6 +192,7 @@ def emulate_rotate(img, lay, x, K, d):
     C = 2 if lay["fast"] else 4
     segs = d // lay["seg_ch"]
     tab = field_major(img, lay, segs)
+    pws, prs = store_permutation(img, lay, segs)
     M = x.shape[0]
     out = np.zeros((M, d), np.float16)
     for s in range(segs):
@@ -222,8 +233,27 @@ def emulate_rotate(img, lay, x, K, d):
         second = np.where(sel == SEL_STORE_X, ob, ox)
         assert np.all((sel == SEL_STORE_X) | (sel == SEL_STORE_B))
         assert sorted(q.tolist()) == list(range(nv))
-        o[:, 2 * q] = first
-        o[:, 2 * q + 1] = second
+        if K == 0:
+            # no exchange: every lane still holds the natural pair it loaded
+            assert np.array_equal(q, np.arange(nv))
+            o[:, 0::2] = first
+            o[:, 1::2] = second
+            continue
+        # the activation kernel with 256-channel segments: the packed words
+        # go through the store permutation and lane w stores natural pair w
+        pw, pr = pws[s], prs[s]
+        assert sorted(pw.tolist()) == list(range(nv)) and sorted(pr.tolist()) == list(range(nv))
+        lds = np.zeros((M, nv, 2), np.float16)
+        lds[:, pw, 0] = first
+        lds[:, pw, 1] = second
+        o[:, 0::2] = lds[:, pr, 0]
+        o[:, 1::2] = lds[:, pr, 1]
+        # with 128-channel segments, and in the small-batch kernel, each lane
+        # places its pair at its store offset instead: the same layout
+        placed = np.zeros((M, lay["seg_ch"]), np.float16)
+        placed[:, 2 * q] = first
+        placed[:, 2 * q + 1] = second
+        assert np.array_equal(placed, o)
     return out
 
 
@@ -235,10 +265,15 @@ def check_slots_conflict_free(img, lay, K, d):
     K = lay["stages"]
     nv = lay["seg_ch"] // 2
     tab = field_major(img, lay, d // lay["seg_ch"])
+    pws, prs = store_permutation(img, lay, d // lay["seg_ch"])
     for s in range(tab.shape[0]):
-        for tau in range(K + 1):
-            wr = tab[s, 1 + 2 * tau] // 16
-            rd = tab[s, 2 + 2 * tau] // 16
+        # the K + 1 exchanges, then (with stages) the store permutation
+        for tau in range(K + 2 if K > 0 else K + 1):
+            if tau <= K:
+                wr = tab[s, 1 + 2 * tau] // 16
+                rd = tab[s, 2 + 2 * tau] // 16
+            else:
+                wr, rd = pws[s], prs[s]
             assert sorted(wr.tolist()) == list(range(nv))
             assert sorted(rd.tolist()) == list(range(nv))
             for blk in range(nv // 8):
