@@ -81,7 +81,8 @@ def test_rotate_decode(paro, M):
 @pytest.mark.parametrize("G,K,d,M", [(64, 8, 512, 37), (256, 8, 512, 37), (128, 1, 384, 9),
                                      (128, 0, 256, 5), (256, 0, 512, 3), (64, 0, 256, 2),
                                      (128, 3, 1024, 100), (256, 5, 768, 19), (128, 16, 256, 7),
-                                     (64, 32, 256, 5), (256, 12, 512, 6), (128, 2, 128, 1)])
+                                     (64, 32, 256, 5), (256, 12, 512, 6), (128, 2, 128, 1),
+                                     (256, 3, 512, 2050), (256, 2, 768, 4101)])
 def test_rotate_shapes(paro, G, K, d, M):
     log(f"rotate G={G} K={K} d={d} M={M}")
     x, layer = synthetic.rotation_case(seed=G + K * 7 + d + M, M=M, d=d, group=G, K=K)
@@ -149,6 +150,22 @@ def test_rotate_inplace_and_empty(paro):
     st = lib.paro_rotate(r.handle, ctypes.c_void_p(buf.data_ptr()), ctypes.c_void_p(buf.data_ptr()),
                          ctypes.c_int64(2 ** 31), None)
     assert paro.STATUS[st] == "PARO_ERR_SHAPE"
+
+
+def test_rotate_256_general_form_and_in_place(paro):
+    """256-channel segments, whose packed outputs go through the store
+    permutation before the stores: the general 2x2 form, and in place (each
+    wavefront's next batch is loaded before it stores the current one)."""
+    log("rotate G=256 general form, in place")
+    x, layer = synthetic.rotation_case(seed=13, M=29, d=1024, group=256, K=8)
+    layer.theta[:, ::3] = 1e-7
+    _, lay = paro.paro_rotation_plan_host(layer.pairs, layer.theta, layer.alpha, 256)
+    assert not lay["fast"] and lay["seg_ch"] == 256
+    check_rotation(paro, x, layer)
+    check_rotation(paro, x, layer, inplace=True)
+    log("rotate G=256 factored form in place, 8200 rows")
+    x, layer = synthetic.rotation_case(seed=14, M=8200, d=512, group=256, K=8)
+    check_rotation(paro, x, layer, rows=np.r_[0:40, 4090:4110, 8160:8200], inplace=True)
 
 
 def test_rotate_deterministic(paro):
