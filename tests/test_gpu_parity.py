@@ -483,10 +483,13 @@ def test_linear_workspace_errors(paro):
 @pytest.mark.parametrize("M,d,N", [(1, 640, 400), (16, 640, 400), (5, 384, 48), (2, 4096, 4096),
                                    (16, 14336, 256), (11, 1152, 1040), (1, 128, 16),
                                    (3, 4096, 14336), (16, 14336, 4096), (24, 4096, 1024), (40, 1152, 1040),
-                                   (64, 14336, 4096)])
+                                   (64, 14336, 4096), (16, 4096, 4096), (12, 4096, 1024), (8, 14336, 256),
+                                   (5, 14336, 144)])
 def test_decode_fused_equals_rotate_then_plain(paro, M, d, N):
     """The fused transform yields the X' bits paro_rotate yields and the k-split
-    sum order does not depend on where X' came from: equal outputs bit for bit."""
+    sum order does not depend on where X' came from: equal outputs bit for bit.
+    (8, 14336, 256) and (5, 14336, 144) take the grouped reduction of 28
+    k-slices (few outputs per n-block), the latter with a ragged n-block."""
     log(f"decode fused vs separate M={M} d={d} N={N}")
     x, layer, b = synthetic.linear_case(seed=40 + M + d, M=M, d=d, N=N)
     r = paro.Rotation(layer.pairs, layer.theta, layer.alpha, 128)
