@@ -110,7 +110,7 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
                     const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zr,
                     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N,
                     int d, int gsh, int mblk, int nblk, int ksplit, float* __restrict__ part,
-                    uint32_t* __restrict__ cnt, int sys) {
+                    uint32_t* __restrict__ cnt, int sys, int mmaj) {
   constexpr int GB_M = 32 * MT;           // tokens per workgroup tile
   constexpr int GN = 128 * NT;            // output channels per workgroup tile
   constexpr int GB_XSTAGE = GB_M * GB_K;  // halfs per X' stage (16 KB at MT = 4)
@@ -125,16 +125,27 @@ void w4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
   // XCD-aware tile order: workgroup b runs on XCD b % 8. XCD x owns the
   // n-blocks x, x + 8, ... and walks them in super-blocks of 8 m-blocks x all
   // its n-blocks, so the workgroups resident on one XCD share both their X'
-  // and their weight k-tiles through its L2.
+  // and their weight k-tiles through its L2; or (mmaj, layers with a large X'
+  // and N < 4 M) XCD x owns the m-blocks x, x + 8, ... and all n-blocks, so
+  // that it reads only its eighth of X'.
   const int xcd = blockIdx.x & 7, idx0 = blockIdx.x >> 3;
   if (!SPLIT) ksplit = 1;
   const int ks = idx0 % ksplit, idx = idx0 / ksplit;
-  const int nbx = (nblk - xcd + 7) >> 3;
-  if (nbx <= 0) return;
-  const int mg = idx / (8 * nbx), rem = idx - mg * 8 * nbx;
-  const int nb = xcd + 8 * (rem / 8);
-  const int mb = mg * 8 + (rem & 7);
-  if (mb >= mblk) return;
+  int mb, nb;
+  if (mmaj) {
+    // XCD x owns the m-blocks x, x + 8, ... and all n-blocks of each
+    const int mi = idx / nblk;
+    mb = xcd + 8 * mi;
+    nb = idx - mi * nblk;
+    if (mb >= mblk) return;
+  } else {
+    const int nbx = (nblk - xcd + 7) >> 3;
+    if (nbx <= 0) return;
+    const int mg = idx / (8 * nbx), rem = idx - mg * 8 * nbx;
+    nb = xcd + 8 * (rem / 8);
+    mb = mg * 8 + (rem & 7);
+    if (mb >= mblk) return;
+  }
   const int m0 = mb * GB_M;
   const int nw0 = nb * GN;         // workgroup's first output channel
   const int n0 = nw0 + 32 * NT * w;  // this wavefront's first output channel
@@ -942,9 +953,10 @@ void w4_gemm_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
 template <int KS, int MT, int NT>
 void launch_gemm(unsigned blocks, hipStream_t stream, const uint16_t* x, const uint8_t* qweight,
                  const uint16_t* scales, const uint8_t* zeros, const uint16_t* bias, uint16_t* y,
-                 int64_t M, int64_t N, int64_t d, int gsh, int mblk, int nblk) {
+                 int64_t M, int64_t N, int64_t d, int gsh, int mblk, int nblk, int mmaj) {
   hipLaunchKernelGGL((w4_gemm_kernel<KS, MT, NT, false>), dim3(blocks), dim3(256 * KS), 0, stream, x, qweight,
-                     scales, zeros, bias, y, (int)M, (int)N, (int)d, gsh, mblk, nblk, 1, nullptr, nullptr, 0);
+                     scales, zeros, bias, y, (int)M, (int)N, (int)d, gsh, mblk, nblk, 1, nullptr, nullptr, 0,
+                     mmaj);
 }
 
 // Smaller-tile kernel geometry, as launch_w4_gemm chooses it: 64-token tiles
@@ -1075,7 +1087,17 @@ hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint1
   const int64_t nbp = (nblk + 7) / 8;
   const int64_t blocks = 8 * nbp * (((int64_t)mblk + 7) / 8) * 8;
   const bool ks2 = sg.ksin == 2, ks4 = sg.ksin == 4;
-  const unsigned g = (unsigned)blocks;
+  // The smaller-tile kernel's XCD order. By n-blocks, every XCD reads all of
+  // X' (2 M d bytes) and an eighth of the weights; by m-blocks, an eighth of
+  // X' and all of the weights (N d / 2 bytes), which is less when N < 4 M.
+  // Where X' is at least 8 MiB (twice an XCD's L2) the saved re-reads show:
+  // plain GEMM, 2048 x 4096 -> 1024 35.5 -> 32.0 us, 1024 x 4096 -> 1024
+  // 26.3 -> 24.8, 4096 x 4096 -> 1024 102 -> 56; 2048 x 4096 -> 4096 the same
+  // (76.5 us); with X' in L2 (2048 x 1024 -> 1024, 4 MiB) by n-blocks stays
+  // faster (14.1 against 16.1 us). At least 8 m-blocks, so that every XCD
+  // gets one.
+  const int mmaj = mblk >= 8 && N < 4 * M && 2 * M * d >= (int64_t(8) << 20);
+  const unsigned g = mmaj ? 8u * (unsigned)((mblk + 7) / 8) * (unsigned)nblk : (unsigned)blocks;
   // layers with many 256 x 256 tiles take the one-wavefront-per-SIMD kernel,
   // one tile per workgroup when the tiles fill whole rounds of one workgroup
   // per CU, else stream-K when the workspace holds the partial tiles
@@ -1113,14 +1135,14 @@ hipError_t launch_w4_gemm(const uint16_t* x, const uint8_t* qweight, const uint1
     const int sys = !xcd_dispatch_is_round_robin();
     hipLaunchKernelGGL((w4_gemm_kernel<4, 2, 1, true>), dim3(g * (unsigned)sg.nsplit), dim3(1024), 0, stream, x,
                        qweight, scales, zeros, bias, y, (int)M, (int)N, (int)d, gsh, mblk, nblk, sg.nsplit, part,
-                       cnt, sys);
-  } else if (ks4) launch_gemm<4, 2, 1>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
-  else if (narrow && ks2) launch_gemm<2, 2, 1>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
-  else if (narrow) launch_gemm<1, 2, 1>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
-  else if (half && ks2) launch_gemm<2, 2, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
-  else if (half) launch_gemm<1, 2, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
-  else if (ks2) launch_gemm<2, 4, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
-  else launch_gemm<1, 4, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk);
+                       cnt, sys, mmaj);
+  } else if (ks4) launch_gemm<4, 2, 1>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk, mmaj);
+  else if (narrow && ks2) launch_gemm<2, 2, 1>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk, mmaj);
+  else if (narrow) launch_gemm<1, 2, 1>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk, mmaj);
+  else if (half && ks2) launch_gemm<2, 2, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk, mmaj);
+  else if (half) launch_gemm<1, 2, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk, mmaj);
+  else if (ks2) launch_gemm<2, 4, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk, mmaj);
+  else launch_gemm<1, 4, 2>(g, stream, x, qweight, scales, zeros, bias, y, M, N, d, gsh, mblk, nblk, mmaj);
   return hipGetLastError();
 }
 

@@ -342,6 +342,21 @@ def test_linear_shapes_with_bias(paro, M, d, N):
     check_linear(paro, x, layer, bias=b)
 
 
+# smaller-tile layers whose X' is at least 8 MiB and N < 4 M run with every XCD
+# owning whole m-blocks (it reads an eighth of X'): k/v-proj shapes at 1024,
+# 2048 and 4100 tokens (ragged M and N), and (1030, 4096, 272), whose few
+# tiles also split k across workgroups; rows sampled (the last included)
+@pytest.mark.parametrize("M,d,N", [(2048, 4096, 1024), (4100, 4096, 1040), (1024, 4096, 1024),
+                                   (1030, 4096, 272)])
+def test_linear_m_major_tiles(paro, M, d, N):
+    log(f"linear m-major tiles M={M} d={d} N={N}")
+    x, layer, b = synthetic.linear_case(seed=M + d + N + 5, M=M, d=d, N=N)
+    rows = np.sort(synthetic.rng_for(3511, M).choice(M, 96, replace=False))
+    rows[-1] = M - 1
+    check_linear(paro, x, layer, bias=b, rows=rows)
+    check_linear(paro, x, layer, rotated=False, rows=rows)
+
+
 # shapes with at least 256 output tiles of 256 x 256 run the one-wavefront-per-SIMD
 # kernel (d = 1024, 2048 and 4096 with the scale and zero panel in LDS): ragged in M
 # and N, rows sampled (the last included), every column checked
